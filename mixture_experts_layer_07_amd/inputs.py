@@ -1,0 +1,126 @@
+"""Seeded synthetic inputs for the layer workloads.
+
+This module draws random numbers and nothing else: it holds none of the layer's
+arithmetic (no routing, no scoring, no expert math). Both the HIP path and the
+CPU oracle receive what it returns.
+
+Recipe (weights drawn N(0, 1/fan_in), i.e. variance 1/fan_in):
+  x        N(0,1) [T,H], cast to the activation dtype (fp32 or bf16, round to nearest even)
+  W_r      N(0,1/H) [H,E]: with x ~ N(0,1) the logits then have variance H * 1/H = 1
+  bias     "normal": N(0, std 0.1) [E] fp32;  "zipf": read from the committed file
+           tests/golden/decode_zipf_bias.txt (written by make_decode_zipf_bias.py beside it)
+  W13      [E, 2I, H], N(0,1/H): gate rows [0,I) then up rows [I,2I)
+  W2       [E, H, I],  N(0,1/I)
+  shared   one more expert of intermediate size I_shared, drawn the same way
+  fp8      weights drawn in fp32 as above, then per 128x128 block scale = absmax/448
+           and codes = e4m3(w / scale) via torch's float8_e4m3fn cast.
+x, W_r and the bias are drawn on the CPU (so every machine sees the same
+values); the expert weights are drawn on `device` with one generator per
+(tensor, expert), so any single expert can be regenerated on its own.
+"""
+import os
+
+import torch
+
+from .configs import LayerConfig
+
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ZIPF_BIAS_FILE = os.path.join(_ROOT, "tests", "golden", "decode_zipf_bias.txt")
+
+_TID = {"x": 1, "w_r": 2, "bias": 3, "w13": 4, "w2": 5, "w13s": 6, "w2s": 7}
+
+
+def _gen(seed, tensor, expert, device):
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) << 32) | (_TID[tensor] << 20) | int(expert))
+    return g
+
+
+def _randn(shape, std, seed, tensor, expert=0, device="cpu"):
+    g = _gen(seed, tensor, expert, device)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+
+
+def act_dtype(cfg: LayerConfig):
+    return torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+
+
+def load_zipf_bias(E):
+    if not os.path.exists(ZIPF_BIAS_FILE):
+        raise FileNotFoundError(f"{ZIPF_BIAS_FILE} missing; run make_decode_zipf_bias.py beside it")
+    vals = []
+    with open(ZIPF_BIAS_FILE) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                vals.extend(float(v) for v in line.split())
+    if len(vals) != E:
+        raise ValueError(f"{ZIPF_BIAS_FILE}: expected {E} values, found {len(vals)}")
+    return torch.tensor(vals, dtype=torch.float32)
+
+
+def make_router_inputs(cfg: LayerConfig):
+    """x [T,H], W_r [H,E] (activation dtype) and bias [E] fp32 or None, on the CPU."""
+    adt = act_dtype(cfg)
+    x = _randn((cfg.T, cfg.H), 1.0, cfg.seed, "x").to(adt)
+    w_r = _randn((cfg.H, cfg.E), cfg.H ** -0.5, cfg.seed, "w_r").to(adt)
+    if cfg.bias is None:
+        bias = None
+    elif cfg.bias == "normal":
+        bias = _randn((cfg.E,), 0.1, cfg.seed, "bias")
+    elif cfg.bias == "zipf":
+        bias = load_zipf_bias(cfg.E)
+    else:
+        raise ValueError(cfg.bias)
+    return x, w_r, bias
+
+
+def fp8_block_quantise(w):
+    """fp32 [N,K] -> (e4m3 codes as uint8 [N,K], fp32 scales [N/128, K/128]); input preparation."""
+    N, K = w.shape
+    blk = w.reshape(N // 128, 128, K // 128, 128)
+    s = blk.abs().amax(dim=(1, 3)) / 448.0
+    safe = torch.where(s == 0, torch.ones_like(s), s)
+    q = (blk / safe[:, None, :, None]).clamp(-448.0, 448.0)
+    q = torch.where((s == 0)[:, None, :, None], torch.zeros_like(q), q)
+    codes = q.reshape(N, K).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, s.contiguous()
+
+
+def expert_weights(cfg: LayerConfig, e, device="cpu", shared=False):
+    """(w13 [2I,H], w2 [H,I]) of routed expert e (or the shared expert) in the layer dtype.
+
+    For fp8 returns (w13_codes, w13_scale, w2_codes, w2_scale).
+    """
+    I = cfg.I_shared if shared else cfg.I
+    t13, t2 = ("w13s", "w2s") if shared else ("w13", "w2")
+    w13 = _randn((2 * I, cfg.H), cfg.H ** -0.5, cfg.seed, t13, e, device)
+    w2 = _randn((cfg.H, I), I ** -0.5, cfg.seed, t2, e, device)
+    if cfg.dtype == "f32":
+        return w13, w2
+    if cfg.dtype == "bf16":
+        return w13.to(torch.bfloat16), w2.to(torch.bfloat16)
+    c13, s13 = fp8_block_quantise(w13)
+    c2, s2 = fp8_block_quantise(w2)
+    return c13, s13, c2, s2
+
+
+def make_expert_weights(cfg: LayerConfig, device="cpu", shared=False):
+    """Stacked expert weights on `device`: dict with w13 [n,2I,H], w2 [n,H,I] (+ scales for fp8)."""
+    n = 1 if shared else cfg.E
+    I = cfg.I_shared if shared else cfg.I
+    if cfg.dtype == "fp8":
+        w13 = torch.empty((n, 2 * I, cfg.H), dtype=torch.uint8, device=device)
+        w2 = torch.empty((n, cfg.H, I), dtype=torch.uint8, device=device)
+        s13 = torch.empty((n, 2 * I // 128, cfg.H // 128), dtype=torch.float32, device=device)
+        s2 = torch.empty((n, cfg.H // 128, I // 128), dtype=torch.float32, device=device)
+        for e in range(n):
+            c13, a13, c2, a2 = expert_weights(cfg, e, device, shared)
+            w13[e], s13[e], w2[e], s2[e] = c13, a13, c2, a2
+        return {"w13": w13, "w2": w2, "w13_scale": s13, "w2_scale": s2}
+    dt = act_dtype(cfg)
+    w13 = torch.empty((n, 2 * I, cfg.H), dtype=dt, device=device)
+    w2 = torch.empty((n, cfg.H, I), dtype=dt, device=device)
+    for e in range(n):
+        w13[e], w2[e] = expert_weights(cfg, e, device, shared)
+    return {"w13": w13, "w2": w2, "w13_scale": None, "w2_scale": None}

@@ -1,0 +1,356 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (CPU only).
+
+Each test checks the oracle against a value printed on a page (golden files,
+cited there), a closed form, a brute-force search, an independent library
+routine, or an invariant, so that a dropped term, a flipped sign or index or a
+transposed operand in the oracle fails at least one of them.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    """Sections of a golden file: {header: [rows of floats]}."""
+    out, cur = {}, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line[0].isalpha() and ":" not in line:
+                cur = line
+                out[cur] = []
+            else:
+                out.setdefault(cur, []).append(line)
+    return out
+
+
+def rows(sec):
+    return np.array([[float(v) for v in r.split()] for r in sec])
+
+
+# ------------------------------------------------------------------ worked examples
+
+def test_top2_worked_example_select_and_renorm():
+    g = read_golden("primer_top2_example.txt")
+    s = rows(g["scores"])
+    ids = orc.select_topk(s, 2)
+    assert ids.tolist() == rows(g["topk_ids"]).astype(int).tolist()
+    w = np.take_along_axis(s, ids, 1)
+    np.testing.assert_allclose(w, rows(g["topk_weights"]), rtol=0, atol=1e-15)
+    # route() from logits: softmax(log s) == s because every row of s sums to one
+    z = np.log(s)
+    ids_r, w_raw = orc.route(z, "softmax", 2, renorm=False)
+    assert ids_r.tolist() == ids.tolist()
+    np.testing.assert_allclose(w_raw, rows(g["topk_weights"]), rtol=1e-12)
+    _, w_n = orc.route(z, "softmax", 2, renorm=True)
+    np.testing.assert_allclose(w_n[0], rows(g["renorm_token0"])[0], rtol=1e-12)
+    np.testing.assert_allclose(w_n.sum(1), 1.0, rtol=1e-12)
+    _, w_s = orc.route(z, "softmax", 2, renorm=True, route_scale=2.5)
+    np.testing.assert_allclose(w_s[0], 2.5 * rows(g["renorm_token0"])[0], rtol=1e-12)
+
+
+def test_grouped_worked_example():
+    g = read_golden("primer_grouped_example.txt")
+    s = rows(g["scores"])
+    np.testing.assert_allclose(orc.group_scores(s, 4, "max"), rows(g["group_scores_max"]))
+    for rule in ("max", "top2_sum"):   # with 2 experts per group both rules keep the same groups
+        ids3, kept = orc.grouped_select(s, 3, 4, 2, rule)
+        assert kept[0].tolist() == rows(g["kept_groups"]).astype(int)[0].tolist()
+        assert ids3[0].tolist() == rows(g["grouped_top3"]).astype(int)[0].tolist()
+        ids4, _ = orc.grouped_select(s, 4, 4, 2, rule)
+        assert ids4[0].tolist() == rows(g["grouped_top4"]).astype(int)[0].tolist()
+    assert orc.select_topk(s, 3)[0].tolist() == rows(g["plain_top3"]).astype(int)[0].tolist()
+    assert orc.select_topk(s, 4)[0].tolist() == rows(g["plain_top4"]).astype(int)[0].tolist()
+    np.testing.assert_allclose(orc.group_scores(s, 4, "top2_sum")[0], [0.9, 0.7, 1.6, 0.8])
+
+
+def test_dispatch_worked_example():
+    g = read_golden("primer_top2_example.txt")
+    ids = rows(g["topk_ids"]).astype(int)
+    counts, offsets, sp, pp = orc.permute(ids, 4)
+    want = {}
+    with open(os.path.join(GOLDEN, "primer_dispatch_example.txt")) as f:
+        for line in f:
+            if line.startswith("expert"):
+                e, toks = line.split(":")
+                want[int(e.split()[1])] = [int(t) for t in toks.split()]
+    for e in range(4):
+        assert (sp[offsets[e]:offsets[e + 1]] // 2).tolist() == want[e]
+    assert counts.tolist() == [1, 1, 3, 1]
+    assert offsets.tolist() == [0, 1, 2, 5, 6]
+    assert sp.tolist() == [2, 0, 1, 3, 5, 4]
+    assert pp.tolist() == [1, 2, 0, 3, 5, 4]
+
+
+# ------------------------------------------------------------------ brute force / closed forms
+
+def test_select_topk_brute_force():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        E, K = rng.integers(2, 7), None
+        K = int(rng.integers(1, E + 1))
+        keys = rng.normal(size=(1, E))
+        best = max(itertools.combinations(range(E), K), key=lambda c: keys[0, list(c)].sum())
+        ids = orc.select_topk(keys, K)[0]
+        assert set(ids.tolist()) == set(best)
+        assert np.all(np.diff(keys[0, ids]) < 0)      # descending order
+
+
+def test_grouped_select_brute_force():
+    rng = np.random.default_rng(1)
+    for _ in range(100):
+        n_group, size = int(rng.integers(2, 5)), int(rng.integers(2, 4))
+        E = n_group * size
+        kg = int(rng.integers(1, n_group + 1))
+        K = int(rng.integers(1, kg * size + 1))
+        keys = rng.normal(size=(1, E))
+        for rule in ("max", "top2_sum"):
+            gsc = [max(keys[0, g * size:(g + 1) * size]) if rule == "max"
+                   else sum(sorted(keys[0, g * size:(g + 1) * size])[-2:]) for g in range(n_group)]
+            groups = max(itertools.combinations(range(n_group), kg), key=lambda c: sum(gsc[i] for i in c))
+            elig = [e for g in groups for e in range(g * size, (g + 1) * size)]
+            best = max(itertools.combinations(elig, K), key=lambda c: keys[0, list(c)].sum())
+            ids, kept = orc.grouped_select(keys, K, n_group, kg, rule)
+            assert set(kept[0].tolist()) == set(groups)
+            assert set(ids[0].tolist()) == set(best)
+
+
+def test_tie_rule_lower_id_first():
+    keys = np.array([[0.5, 0.5, 0.5, 0.5], [0.1, 0.3, 0.3, 0.2], [1.0, 0.2, 1.0, 1.0]])
+    assert orc.select_topk(keys, 2).tolist() == [[0, 1], [1, 2], [0, 2]]
+    # group ties go to the lower group id too
+    keys = np.array([[0.2, 0.9, 0.9, 0.2, 0.1, 0.1]])
+    ids, kept = orc.grouped_select(keys, 2, 3, 1, "max")
+    assert kept[0].tolist() == [0] and ids[0].tolist() == [1, 0]
+
+
+def test_score_closed_forms():
+    z = np.array([[0.0, math.log(3.0)]])
+    np.testing.assert_allclose(orc.score(z, "softmax"), [[0.25, 0.75]], rtol=1e-15)
+    np.testing.assert_allclose(orc.score(z, "sigmoid"), [[0.5, 0.75]], rtol=1e-15)
+    rng = np.random.default_rng(2)
+    z = rng.normal(size=(5, 9)) * 3
+    s = orc.score(z, "softmax")
+    np.testing.assert_allclose(s.sum(1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(orc.score(z + 7.0, "softmax"), s, rtol=1e-12)   # shift invariance
+    assert (np.argsort(s, 1) == np.argsort(z, 1)).all()                         # order preserving
+    # softmax of a large logit gap does not overflow
+    assert np.isfinite(orc.score(np.array([[1000.0, 0.0]]), "softmax")).all()
+
+
+def test_router_logits_orientation():
+    x = np.array([[1.0, 0.0, 0.0], [0.0, 2.0, 0.0]])          # [T=2, H=3]
+    w_r = np.arange(12.0).reshape(3, 4)                       # [H=3, E=4]
+    np.testing.assert_array_equal(orc.router_logits(x, w_r), [[0, 1, 2, 3], [8, 10, 12, 14]])
+
+
+def test_selection_bias_changes_ids_not_weights():
+    z = np.log(np.array([[0.1, 0.6, 0.2, 0.1]]))
+    bias = np.array([0.0, 0.0, 0.0, 0.6])
+    ids, w = orc.route(z, "softmax", 2, bias=bias, renorm=False)
+    assert ids[0].tolist() == [3, 1]                          # 0.1 + 0.6 = 0.7 > 0.6
+    np.testing.assert_allclose(w[0], [0.1, 0.6], rtol=1e-12)  # unbiased scores
+
+
+# ------------------------------------------------------------------ dispatch invariants
+
+def test_permute_invariants():
+    rng = np.random.default_rng(3)
+    for T, E, K in [(1, 4, 1), (37, 8, 2), (200, 64, 8), (5, 16, 4)]:
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        counts, offsets, sp, pp = orc.permute(ids, E)
+        P = T * K
+        assert counts.sum() == P and offsets[-1] == P and (np.diff(offsets) == counts).all()
+        assert sorted(sp.tolist()) == list(range(P))             # bijection
+        assert (pp[sp] == np.arange(P)).all()
+        flat = ids.reshape(-1)
+        for e in range(E):
+            seg = sp[offsets[e]:offsets[e + 1]]
+            assert (flat[seg] == e).all() and (np.diff(seg) > 0).all()   # grouped and stable
+    with pytest.raises(ValueError):
+        orc.permute(np.array([[0, 4]]), 4)
+
+
+# ------------------------------------------------------------------ experts and combine
+
+def test_swiglu_expert_hand_worked():
+    # H=2, I=1: gate row picks x0, up row picks x1; W_down [H=2, I=1]
+    x = np.array([[1.0, 2.0]])
+    w13 = np.array([[1.0, 0.0], [0.0, 1.0]])
+    w2 = np.array([[1.0], [3.0]])
+    sig1 = 0.7310585786300049                               # 1 / (1 + e^-1)
+    np.testing.assert_allclose(orc.swiglu_expert(x, w13, w2), [[2 * sig1, 6 * sig1]], rtol=1e-15)
+    # swapping gate and up must change the result: SiLU(2) * 1 = 2 * 0.8807970779778823
+    w13s = np.array([[0.0, 1.0], [1.0, 0.0]])
+    np.testing.assert_allclose(orc.swiglu_expert(x, w13s, w2), [[2 * 0.8807970779778823,
+                                                                  6 * 0.8807970779778823]], rtol=1e-15)
+    # H=3, I=2 with non-square pieces (catches transposed operands)
+    x = np.array([[1.0, 0.0, -1.0]])
+    w13 = np.array([[0.0, 0.0, 0.0],      # g0 = 0  -> SiLU = 0
+                    [1.0, 5.0, 0.0],      # g1 = 1
+                    [7.0, 0.0, 0.0],      # u0 = 7
+                    [0.0, 0.0, -2.0]])    # u1 = 2
+    w2 = np.array([[1.0, 1.0], [0.0, 2.0], [5.0, 0.0]])
+    a1 = sig1 * 2.0
+    np.testing.assert_allclose(orc.swiglu_expert(x, w13, w2), [[a1, 2 * a1, 0.0]], rtol=1e-15)
+
+
+def test_silu_limits():
+    np.testing.assert_allclose(orc.silu([0.0, 50.0, -50.0]), [0.0, 50.0, 0.0], atol=1e-20)
+
+
+def _tiny_layer(seed, T, H, I, E):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(T, H))
+    w_r = rng.normal(size=(H, E)) / math.sqrt(H)
+    ex = [(rng.normal(size=(2 * I, H)) / math.sqrt(H), rng.normal(size=(H, I)) / math.sqrt(I))
+          for _ in range(E)]
+    return x, w_r, ex
+
+
+@pytest.mark.parametrize("fn,E,K,n_group,kg,rule,bias", [
+    ("softmax", 8, 2, 1, 1, "top2_sum", False),
+    ("sigmoid", 16, 4, 4, 2, "top2_sum", True),
+    ("sigmoid", 16, 3, 4, 2, "max", True),
+])
+def test_sparse_combine_equals_dense_mixing(fn, E, K, n_group, kg, rule, bias):
+    T, H, I = 16, 64, 32
+    x, w_r, ex = _tiny_layer(4, T, H, I, E)
+    b = np.random.default_rng(5).normal(size=E) * 0.1 if bias else None
+    z = orc.router_logits(x, w_r)
+    ids, w = orc.route(z, fn, K, b, n_group, kg, rule, True, 2.5 if bias else 1.0)
+    counts, offsets, sp, pp = orc.permute(ids, E)
+    y_perm = orc.expert_ffn(orc.gather_rows(x, sp, K), offsets, lambda e: ex[e])
+    sparse = orc.combine(pp, w, y_perm)
+    full = np.zeros((T, E))
+    np.put_along_axis(full, ids, w, 1)
+    dense = orc.dense_mix(x, lambda e: ex[e], E, full)
+    np.testing.assert_allclose(sparse, dense, rtol=0, atol=1e-12 * np.abs(dense).max())
+    out, ids2, w2 = orc.moe_layer(x, w_r, lambda e: ex[e], fn, K, E, b, n_group, kg, rule,
+                                  True, 2.5 if bias else 1.0)
+    assert (ids2 == ids).all()
+    np.testing.assert_allclose(out, sparse, rtol=0, atol=1e-12 * np.abs(dense).max())
+
+
+def test_single_expert_layer_is_a_dense_ffn():
+    # E=1, K=1, softmax: every weight is exactly one and the layer is one dense FFN.
+    T, H, I = 8, 16, 8
+    x, w_r, ex = _tiny_layer(6, T, H, I, 1)
+    out, ids, w = orc.moe_layer(x, w_r, lambda e: ex[e], "softmax", 1, 1)
+    assert (ids == 0).all() and (w == 1.0).all()
+    np.testing.assert_allclose(out, orc.swiglu_expert(x, *ex[0]), rtol=1e-14)
+    # shared expert alone adds its own FFN
+    out2, _, _ = orc.moe_layer(x, w_r, lambda e: ex[e], "softmax", 1, 1, get_shared=lambda: ex[0])
+    np.testing.assert_allclose(out2, 2 * out, rtol=1e-14)
+
+
+def test_expert_ffn_row_subset_matches_full():
+    T, H, I, E = 12, 32, 16, 4
+    x, w_r, ex = _tiny_layer(7, T, H, I, E)
+    offsets = np.array([0, 3, 3, 10, 12])
+    full = orc.expert_ffn(x, offsets, lambda e: ex[e])
+    rows_ = [11, 0, 5, 3]
+    np.testing.assert_allclose(orc.expert_ffn(x, offsets, lambda e: ex[e], rows=rows_), full[rows_])
+    np.testing.assert_allclose(full[3:10], orc.swiglu_expert(x[3:10], *ex[2]))
+
+
+# ------------------------------------------------------------------ fp8 e4m3
+
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.e4m3_decode_array(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.tolist() == np.isnan(mine).tolist()
+    assert set(np.nonzero(nan)[0].tolist()) == {0x7F, 0xFF}
+    np.testing.assert_array_equal(mine[~nan], ref[~nan])
+    assert mine[0x7E] == 448.0 and mine[0x38] == 1.0 and mine[0x08] == 2.0 ** -6
+    assert mine[0x01] == 2.0 ** -9 and mine[0x80] == 0.0 and math.copysign(1, mine[0x80]) < 0
+
+
+def test_e4m3_encode_vs_nearest_search_and_torch():
+    rng = np.random.default_rng(8)
+    table = orc.e4m3_decode_array(np.arange(127, dtype=np.uint8))
+    mids = (table[1:] + table[:-1]) / 2                      # exact ties go to the even code
+    vals = np.concatenate([rng.uniform(-460, 460, 20000), rng.normal(size=5000) * 1e-2,
+                           table, -table, mids, -mids, [0.0, 449.0, -1e6, 1e-12, -1e-12]])
+    vals32 = vals.astype(np.float32)
+    codes = orc.e4m3_encode(vals32)
+    a = np.minimum(np.abs(vals32.astype(np.float64)), 448.0)
+    d = np.abs(table[None, :] - a[:, None])
+    best = d.min(1, keepdims=True)
+    cand = np.where(d == best, np.arange(127)[None, :], 1000)
+    even = np.where((cand % 2 == 0) & (cand < 1000), cand, 1000).min(1)
+    brute = np.where(even < 1000, even, cand.min(1))
+    assert ((codes & 0x7F) == brute).all()
+    assert ((codes >> 7) == np.signbit(vals32)).all()
+    inr = np.abs(vals32) <= 448
+    t = torch.from_numpy(vals32[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    same = (t == codes[inr]) | ((t & 0x7F) == 0) & ((codes[inr] & 0x7F) == 0)
+    assert same.all()
+
+
+def test_quantize_rows_fp8_pins():
+    # exactly representable rows: codes * scale with absmax 448 * scale round-trip exactly
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 0x7E, size=(3, 256)).astype(np.uint8) | (rng.integers(0, 2, (3, 256)) << 7).astype(np.uint8)
+    codes[:, 0] = 0x7E
+    codes[:, 128] = 0xFE
+    scale = np.float32(2.0 ** -5)
+    vals = orc.e4m3_decode_array(codes) * scale
+    q, s = orc.quantize_rows_fp8(vals)
+    assert (s == scale).all()
+    np.testing.assert_array_equal(orc.dequantize_rows_fp8(q, s), vals)
+    # zero block -> scale 0, codes 0; nonzero block scale = absmax / 448
+    a = np.zeros((2, 256), np.float32)
+    a[1, 130] = -3.0
+    q, s = orc.quantize_rows_fp8(a)
+    assert s[0].tolist() == [0.0, 0.0] and s[1, 0] == 0.0
+    assert s[1, 1] == np.float32(3.0) / np.float32(448.0)
+    assert q[1, 130] == 0xFE and (q[0] == 0).all()
+    # relative error of a random row stays within half an e4m3 ulp (2^-4) of the block absmax scale
+    a = rng.normal(size=(4, 512)).astype(np.float32)
+    q, s = orc.quantize_rows_fp8(a)
+    err = np.abs(orc.dequantize_rows_fp8(q, s) - a)
+    assert (err <= np.repeat(s, 128, 1) * 448 * 2.0 ** -4 + 1e-30).all()
+
+
+def test_weight_block_dequant_orientation():
+    codes = np.full((256, 128), 0x38, np.uint8)       # every value 1.0
+    scales = np.array([[2.0], [3.0]], np.float32)      # [N/128=2, K/128=1]
+    w = orc.dequantize_weight_blocks(codes, scales)
+    assert (w[:128] == 2.0).all() and (w[128:] == 3.0).all()
+
+
+def test_fp8_layer_path_matches_exactly_representable_fp32():
+    # x and weights exactly representable in e4m3 at power-of-two scales: the fp8
+    # quantisation of x is lossless, so only the hidden re-quantisation differs.
+    T, H, I = 4, 128, 128
+    rng = np.random.default_rng(10)
+    x = orc.e4m3_decode_array(rng.integers(0, 0x70, size=(T, H)).astype(np.uint8))
+    x[:, 0] = 448.0
+    q, s = orc.quantize_rows_fp8(x)
+    np.testing.assert_array_equal(orc.dequantize_rows_fp8(q, s), x)
+
+
+# ------------------------------------------------------------------ near-tie accounting
+
+def test_near_tie_flags():
+    z = np.log(np.array([[0.4, 0.3, 0.3 - 1e-7, 0.0 + 1e-9],     # K=2 boundary tie
+                         [0.5, 0.3, 0.1, 0.1]]))                  # clear
+    flags = orc.near_tie_tokens(z, "softmax", 2)
+    assert flags.tolist() == [True, False]
+    keys = np.array([[0.9, 0.1, 0.5, 0.3, 0.5 - 1e-8, 0.0]])      # groups (max): 0.9, 0.5, 0.5-1e-8
+    zz = np.log(keys / (1 - keys + 1e-300) + 1e-300)              # sigmoid^-1
+    assert orc.near_tie_tokens(zz, "sigmoid", 1, None, 3, 1, "max").tolist() == [False]
+    assert orc.near_tie_tokens(zz, "sigmoid", 1, None, 3, 2, "max").tolist() == [True]
