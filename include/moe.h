@@ -1,0 +1,179 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) forward pass of a token-choice MoE FFN layer.
+ *
+ * The layer ("MoE 路由入门：从 Dense FFN 到 GroupedTopK", blog.freezetheflame.cc,
+ * sections 3-5; "MoE" chapter README, llm-infra-atlas.github.io/moe, section 0):
+ *
+ *   hidden_states x [T,H]
+ *     -> moe_route      router logits z = x W_r, softmax or sigmoid scores, plain or
+ *                       grouped top-K -> topk_ids [T,K], topk_weights [T,K]
+ *     -> moe_permute    pairs p = t*K + k bucketed by expert: counts, offsets, a stable
+ *                       order of the pairs, its inverse, and the expert-grouped rows x_perm
+ *     -> moe_expert_ffn per expert e, on its rows: y = W_down(SiLU(W_gate x) * W_up x)
+ *                       as two grouped GEMMs over ragged per-expert row counts
+ *     -> moe_combine    out[t] = sum_k w[t,k] * y_perm[pair_pos[t*K+k]] (+ shared expert row)
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device buffers are device pointers (hipMalloc'd or torch CUDA
+ *     tensors), contiguous, 16-byte aligned. Host pointers are only the config structs
+ *     and the out-parameters of the query functions.
+ *   - The caller owns and allocates every buffer, including the workspace (size from
+ *     moe_workspace_size). The library never allocates or frees device memory and keeps
+ *     no per-call state. A workspace must not be used by two calls in flight at once.
+ *   - All calls enqueue work on `stream` (a hipStream_t passed as void*, NULL = the
+ *     default stream) and return without waiting. Only moe_get_device_error waits.
+ *   - Arguments are checked on the host before anything is enqueued; on failure the call
+ *     returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE and has no
+ *     side effect. MOE_ERR_HIP reports a failed launch; moe_last_error() has the text.
+ *     No C++ exception crosses this boundary.
+ *   - The library only runs on gfx950 devices (MOE_ERR_UNSUPPORTED elsewhere).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, bad size or inconsistent config */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but not implemented (shape constraint, device) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_DEVICE = 5       /* a kernel flagged bad data (see moe_get_device_error) */
+} moe_status;
+
+/* Arithmetic type of a layer.
+ *  MOE_F32      x, W_r, expert weights, y and out are fp32; fp32 accumulation.
+ *  MOE_BF16     x, W_r, expert weights, intermediates and out are bf16; fp32 accumulation.
+ *  MOE_FP8_E4M3 x and W_r are bf16; the library quantises x per token per 128 channels to
+ *               e4m3 for the experts; expert weights are e4m3 codes with one fp32 scale per
+ *               128x128 block; the SwiGLU output is re-quantised per row per 128 channels;
+ *               fp32 accumulation; y_perm, y_shared and out are bf16. */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
+/* Score function ("MoE 路由入门", section 3). */
+enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
+/* Group score for grouped top-K ("MoE 路由入门", section 7 uses the group maximum). */
+enum { MOE_GROUP_MAX = 0, MOE_GROUP_TOP2_SUM = 1 };
+
+typedef struct moe_config {
+  int32_t T, H, I, E, K;   /* tokens, hidden, routed intermediate, routed experts, top-k */
+  int32_t score_fn;        /* MOE_SOFTMAX | MOE_SIGMOID */
+  int32_t renorm;          /* 1: divide the K selected scores by their sum */
+  float route_scale;       /* multiplies the weights after renormalisation (1.0 = none) */
+  int32_t n_group;         /* expert groups; 1 = plain top-K. Group g = experts [g*E/n, (g+1)*E/n) */
+  int32_t topk_group;      /* groups kept per token (ignored when n_group == 1) */
+  int32_t group_score;     /* MOE_GROUP_MAX | MOE_GROUP_TOP2_SUM */
+  int32_t dtype;           /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 */
+  int32_t I_shared;        /* intermediate size of the one shared expert; 0 = none */
+} moe_config;
+
+/* Validates a config (no device access). Limits: T >= 1, 1 <= K <= E <= 256, H and I
+ * multiples of 128 for bf16/fp8 and of 4 for fp32, E % n_group == 0, K <= topk_group*E/n_group,
+ * T*K < 2^31. */
+moe_status moe_check_config(const moe_config* cfg);
+
+/* Bytes of device workspace that moe_route, moe_permute and moe_expert_ffn (routed and
+ * shared) need for this config; 0 if the config is invalid. */
+size_t moe_workspace_size(const moe_config* cfg);
+
+/* moe_route -- router projection, scores and (grouped) top-K.
+ * "MoE 路由入门", sections 3 (z = x W_r, softmax or sigmoid), 4 (top-K output, renormalised
+ * weights), 7 (GroupedTopK), 8.3 (tie rule), 8.4 (router in fp32); selection-only bias from
+ * the "MoE" chapter README, sections 0 and 2.2.
+ *   x            device [T,H]  fp32 (MOE_F32) or bf16 (otherwise), row-major
+ *   w_router     device [H,E]  same dtype as x, row-major
+ *   bias         device [E] fp32 added to the scores for selection only, or NULL
+ *   topk_ids     device [T,K] int32 out: selected experts, descending key, ties -> lower id
+ *   topk_weights device [T,K] fp32 out: unbiased scores of topk_ids, renormalised if
+ *                cfg->renorm, times cfg->route_scale
+ * Logits and scores are computed in fp32. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
+                     int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_permute -- bucket the P = T*K (token, expert) pairs by expert ("MoE 路由入门", 5.1).
+ * Pair p = t*K + k has expert topk_ids[p].
+ *   topk_ids     device [T,K] int32 in; ids outside [0,E) set the device error word
+ *                (MOE_ERR_DEVICE from moe_get_device_error) and are dropped
+ *   counts       device [E] int32 out: pairs per expert
+ *   offsets      device [E+1] int32 out: exclusive prefix sum of counts, offsets[E] = P
+ *   sorted_pair  device [P] int32 out: pairs ordered by expert, ascending p within an expert
+ *   pair_pos     device [P] int32 out: inverse, pair_pos[sorted_pair[i]] = i
+ *   x            device [T,H] activations (fp32 / bf16 as in moe_route), or NULL to skip the gather
+ *   x_perm       device [P,H] out: row i = x[sorted_pair[i] / K]; same dtype as x, except
+ *                MOE_FP8_E4M3 where it holds e4m3 codes (uint8)
+ *   x_perm_scale device [P,H/128] fp32 out (MOE_FP8_E4M3 only, else NULL): row scale
+ *                absmax/448 of each 128-channel block; code = e4m3_rne_sat(x / scale) */
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
+                       void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_expert_ffn -- SwiGLU experts over expert-grouped rows, as two grouped GEMMs
+ * ("MoE 路由入门", sections 1 and 5.2; Linear-1 = gate and up together, "SwiGLU / FP8 Cast",
+ * Linear-2, from "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", section 5.1).
+ *   n_experts  number of experts in w13/w2 (cfg->E for the routed experts, 1 for the shared)
+ *   n_rows     rows of x_rows and y_rows (P for routed, T for shared); offsets[n_experts] = n_rows
+ *   inter      intermediate size of these experts (cfg->I or cfg->I_shared)
+ *   offsets    device [n_experts+1] int32: rows [offsets[e], offsets[e+1]) belong to expert e
+ *   x_rows     device [n_rows,H]: fp32 / bf16, or e4m3 codes (MOE_FP8_E4M3)
+ *   x_scale    device [n_rows,H/128] fp32 row-block scales (MOE_FP8_E4M3), else NULL
+ *   w13        device [n_experts, 2*inter, H]: gate rows [0,inter), up rows [inter,2*inter)
+ *   w13_scale  device [n_experts, 2*inter/128, H/128] fp32 (MOE_FP8_E4M3), else NULL
+ *   w2         device [n_experts, H, inter]
+ *   w2_scale   device [n_experts, H/128, inter/128] fp32 (MOE_FP8_E4M3), else NULL
+ *   y_rows     device [n_rows,H] out: fp32 (MOE_F32 and MOE_BF16: the fp32 accumulators, so
+ *              the combine rounds only once) or bf16 (MOE_FP8_E4M3)
+ * The SwiGLU output is kept in the workspace (bf16, fp32 for MOE_F32, e4m3 + scales for fp8). */
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_rows, int32_t inter,
+                          const int32_t* offsets, const void* x_rows, const float* x_scale,
+                          const void* w13, const float* w13_scale, const void* w2,
+                          const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* moe_combine -- weighted combine back to [T,H] ("MoE 路由入门", section 5.3; shared expert
+ * added before the residual, "MoE" chapter README, section 0).
+ *   pair_pos     device [P] int32 from moe_permute
+ *   topk_weights device [T,K] fp32 from moe_route
+ *   y_perm       device [P,H] from moe_expert_ffn (fp32 for MOE_F32 / MOE_BF16, bf16 for fp8)
+ *   y_shared     device [T,H] shared expert output (same dtype as y_perm), or NULL
+ *   out          device [T,H] out (fp32 for MOE_F32, else bf16)
+ * out[t] = sum_k topk_weights[t,k] * y_perm[pair_pos[t*K+k]] (+ y_shared[t]), accumulated in
+ * fp32 in k order, rounded once. Needs no workspace. */
+moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const float* topk_weights,
+                       const void* y_perm, const void* y_shared, void* out, void* stream);
+
+/* moe_quantize_fp8 -- e4m3 row quantisation of bf16 rows (the shared expert's input in the
+ * fp8 layer): per row per 128 columns, scale = absmax/448 (fp32), code = e4m3(v / scale),
+ * round to nearest even, saturating; an all-zero block gets scale 0 and codes 0.
+ *   in device [rows,cols] bf16; codes device [rows,cols] uint8 out; scales device [rows,cols/128]
+ *   fp32 out. cols must be a multiple of 128. */
+moe_status moe_quantize_fp8(int32_t rows, int32_t cols, const void* in, uint8_t* codes,
+                            float* scales, void* stream);
+
+/* Reads (and clears) the device error word kept at the start of `ws`, waiting for `stream`.
+ * *code = 0 when no kernel flagged bad data since the last read; otherwise the returned
+ * status is MOE_ERR_DEVICE and *code says what: 1 = expert id out of range in moe_permute. */
+moe_status moe_get_device_error(void* ws, int32_t* code, void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+/* Text of the last error on this host thread (empty if none). */
+const char* moe_last_error(void);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around every kernel this
+ * library enqueues (off by default; enabling adds two event records per launch).
+ * moe_profile_read waits for the recorded work, then writes up to `cap` entries:
+ * names[i] (static strings), total milliseconds and launch counts per kernel name, and
+ * returns the number of distinct kernels; moe_profile_reset drops all records. */
+void moe_profile_enable(int32_t on);
+void moe_profile_reset(void);
+int32_t moe_profile_read(const char** names, double* total_ms, int32_t* launches, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,323 @@
+// C-ABI entry points: host validation, workspace carving, kernel launches. Every check runs
+// before the first HIP call, so a rejected call has no side effect.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace moe {
+
+static thread_local std::string g_last_error;
+
+static moe_status fail(moe_status s, const std::string& why) {
+  g_last_error = why;
+  return s;
+}
+static moe_status fail_hip(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return MOE_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- device info (gfx950 only)
+static std::mutex g_dev_mu;
+static std::map<int, DevInfo> g_dev;
+static std::map<int, bool> g_dev_ok;
+static thread_local DevInfo g_cur;
+
+static moe_status ensure_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_dev_ok.find(dev);
+  if (it == g_dev_ok.end()) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
+    bool ok = strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    DevInfo d;
+    d.cus = p.multiProcessorCount > 0 ? p.multiProcessorCount : 256;
+    g_dev[dev] = d;
+    g_dev_ok[dev] = ok;
+    if (!ok) g_last_error = std::string("device is ") + p.gcnArchName + ", this library needs gfx950";
+    it = g_dev_ok.find(dev);
+  }
+  if (!it->second) return fail(MOE_ERR_UNSUPPORTED, "device is not gfx950");
+  g_cur = g_dev[dev];
+  return MOE_OK;
+}
+
+const DevInfo& dev_info() { return g_cur; }
+
+// ---------------------------------------------------------------- profiling
+struct Rec {
+  const char* name;
+  hipEvent_t a, b;
+};
+static std::mutex g_prof_mu;
+static bool g_prof = false;
+static std::vector<Rec> g_recs;
+struct Tot {
+  double ms = 0;
+  int n = 0;
+};
+static std::vector<std::pair<const char*, Tot>> g_tot;
+
+bool profiling_enabled() { return g_prof; }
+void profile_record(const char* name, hipEvent_t a, hipEvent_t b) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_recs.push_back({name, a, b});
+}
+
+static moe_status check_ws(const moe_config& c, void* ws, size_t ws_bytes, WsLayout* L) {
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  *L = layout(c);
+  if (ws_bytes < L->total)
+    return fail(MOE_ERR_WORKSPACE, "workspace smaller than moe_workspace_size()");
+  return MOE_OK;
+}
+
+template <class T>
+static T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    moe_status _s = (expr);           \
+    if (_s != MOE_OK) return _s;      \
+  } while (0)
+#define MOE_HIP(expr, where)                      \
+  do {                                            \
+    hipError_t _e = (expr);                       \
+    if (_e != hipSuccess) return fail_hip(_e, where); \
+  } while (0)
+
+static moe_status checked_config(const moe_config* cfg) {
+  std::string why;
+  moe_status s = check_config(cfg, &why);
+  if (s != MOE_OK) return fail(s, why);
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_check_config(const moe_config* cfg) { return checked_config(cfg); }
+
+size_t moe_workspace_size(const moe_config* cfg) {
+  if (check_config(cfg, nullptr) != MOE_OK) return 0;
+  return layout(*cfg).total;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
+                     int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes,
+                     void* stream) {
+  MOE_TRY(checked_config(cfg));
+  const moe_config& c = *cfg;
+  if (!x || !w_router || !topk_ids || !topk_weights)
+    return fail(MOE_ERR_INVALID_ARG, "moe_route: NULL buffer");
+  WsLayout L;
+  MOE_TRY(check_ws(c, ws, ws_bytes, &L));
+  MOE_TRY(ensure_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = at<float>(ws, L.logits);
+  if (c.dtype == MOE_F32) {
+    MOE_HIP(launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(w_router),
+                              logits, c.T, c.H, c.E, s),
+            "router_f32");
+  } else {
+    void* wrt = at<void>(ws, L.wrt);
+    MOE_HIP(launch_transpose_bf16(w_router, wrt, c.H, c.E, s), "transpose_router");
+    MOE_HIP(launch_router_bf16(x, wrt, logits, c.T, c.H, c.E, L.route_splits, s), "router_bf16");
+  }
+  MOE_HIP(launch_topk(c, logits, L.route_splits, bias, topk_ids, topk_weights, s), "topk");
+  return MOE_OK;
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
+                       void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
+                       void* stream) {
+  MOE_TRY(checked_config(cfg));
+  const moe_config& c = *cfg;
+  if (!topk_ids || !counts || !offsets || !sorted_pair || !pair_pos)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: NULL buffer");
+  if ((x == nullptr) != (x_perm == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: x and x_perm must both be given or both NULL");
+  if (x && c.dtype == MOE_FP8_E4M3 && !x_perm_scale)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: fp8 layers need x_perm_scale");
+  if (c.dtype != MOE_FP8_E4M3 && x_perm_scale)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: x_perm_scale is only for fp8 layers");
+  WsLayout L;
+  MOE_TRY(check_ws(c, ws, ws_bytes, &L));
+  MOE_TRY(ensure_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int P = c.T * c.K;
+  int32_t* hist = at<int32_t>(ws, L.hist);
+  int32_t* base = at<int32_t>(ws, L.base);
+  int32_t* err = at<int32_t>(ws, L.err);
+  MOE_HIP(launch_perm_hist(topk_ids, P, c.E, hist, err, s), "perm_hist");
+  MOE_HIP(launch_perm_scan(hist, L.perm_blocks, c.E, base, counts, s), "perm_scan");
+  MOE_HIP(launch_perm_scatter(topk_ids, P, c.E, base, counts, offsets, sorted_pair, pair_pos, s),
+          "perm_scatter");
+  if (x) MOE_HIP(launch_gather(c, sorted_pair, x, x_perm, x_perm_scale, s), "gather");
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_rows, int32_t inter,
+                          const int32_t* offsets, const void* x_rows, const float* x_scale,
+                          const void* w13, const float* w13_scale, const void* w2,
+                          const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                          void* stream) {
+  MOE_TRY(checked_config(cfg));
+  const moe_config& c = *cfg;
+  if (n_experts < 1 || n_experts > kMaxExperts)
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_experts must be in [1, 256]");
+  const int64_t P = (int64_t)c.T * c.K;
+  if (n_rows < 0 || n_rows > P)
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_rows must be in [0, T*K]");
+  const int maxI = c.I > c.I_shared ? c.I : c.I_shared;
+  const int q = c.dtype == MOE_F32 ? 4 : 128;
+  if (inter < 1 || inter > maxI || inter % q)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_expert_ffn: inter must be in [1, max(I, I_shared)] and a multiple of 128 "
+                "(4 for fp32)");
+  if (!offsets || !x_rows || !w13 || !w2 || !y_rows)
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: NULL buffer");
+  const bool fp8 = c.dtype == MOE_FP8_E4M3;
+  if (fp8 && (!x_scale || !w13_scale || !w2_scale))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: fp8 layers need x_scale, w13_scale, w2_scale");
+  if (!fp8 && (x_scale || w13_scale || w2_scale))
+    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: scales are only for fp8 layers");
+  WsLayout L;
+  MOE_TRY(check_ws(c, ws, ws_bytes, &L));
+  if (n_rows == 0) return MOE_OK;
+  MOE_TRY(ensure_device());
+  FfnArgs a;
+  a.dtype = c.dtype;
+  a.n_exp = n_experts;
+  a.n_rows = n_rows;
+  a.H = c.H;
+  a.I = inter;
+  a.offsets = offsets;
+  a.x = x_rows;
+  a.x_scale = x_scale;
+  a.w13 = w13;
+  a.w13_scale = w13_scale;
+  a.w2 = w2;
+  a.w2_scale = w2_scale;
+  a.y = y_rows;
+  a.h = at<void>(ws, L.h);
+  a.h_scale = fp8 ? at<float>(ws, L.hscale) : nullptr;
+  a.tiles = at<int32_t>(ws, L.tiles);
+  MOE_HIP(launch_expert_ffn(a, static_cast<hipStream_t>(stream)), "expert_ffn");
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const float* topk_weights,
+                       const void* y_perm, const void* y_shared, void* out, void* stream) {
+  MOE_TRY(checked_config(cfg));
+  if (!pair_pos || !topk_weights || !y_perm || !out)
+    return fail(MOE_ERR_INVALID_ARG, "moe_combine: NULL buffer");
+  MOE_TRY(ensure_device());
+  MOE_HIP(launch_combine(*cfg, pair_pos, topk_weights, y_perm, y_shared, out,
+                         static_cast<hipStream_t>(stream)),
+          "combine");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_fp8(int32_t rows, int32_t cols, const void* in, uint8_t* codes,
+                            float* scales, void* stream) {
+  if (rows < 0 || cols < 128 || cols % 128)
+    return fail(MOE_ERR_INVALID_ARG, "moe_quantize_fp8: rows >= 0, cols a positive multiple of 128");
+  if ((int64_t)rows * cols >= (int64_t(1) << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_quantize_fp8: too large");
+  if (!in || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "moe_quantize_fp8: NULL buffer");
+  if (rows == 0) return MOE_OK;
+  MOE_TRY(ensure_device());
+  MOE_HIP(launch_quantize_fp8(rows, cols, in, codes, scales, static_cast<hipStream_t>(stream)),
+          "quantize_fp8");
+  return MOE_OK;
+}
+
+moe_status moe_get_device_error(void* ws, int32_t* code, void* stream) {
+  if (!ws || !code) return fail(MOE_ERR_INVALID_ARG, "moe_get_device_error: NULL argument");
+  MOE_TRY(ensure_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  MOE_HIP(hipMemcpyAsync(&v, ws, sizeof(int32_t), hipMemcpyDeviceToHost, s), "read error word");
+  MOE_HIP(hipStreamSynchronize(s), "hipStreamSynchronize");
+  MOE_HIP(launch_clear_words(static_cast<int32_t*>(ws), 1, s), "clear error word");
+  *code = v;
+  if (v != 0) return fail(MOE_ERR_DEVICE, "a kernel flagged bad input data");
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    case MOE_ERR_DEVICE: return "device-side data error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+void moe_profile_enable(int32_t on) { g_prof = on != 0; }
+
+void moe_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_recs) {
+    (void)hipEventSynchronize(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_recs.clear();
+  g_tot.clear();
+}
+
+int32_t moe_profile_read(const char** names, double* total_ms, int32_t* launches, int32_t cap) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      bool found = false;
+      for (auto& t : g_tot)
+        if (strcmp(t.first, r.name) == 0) {
+          t.second.ms += ms;
+          t.second.n += 1;
+          found = true;
+          break;
+        }
+      if (!found) g_tot.push_back({r.name, Tot{ms, 1}});
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_recs.clear();
+  int32_t n = 0;
+  for (auto& t : g_tot) {
+    if (n < cap) {
+      if (names) names[n] = t.first;
+      if (total_ms) total_ms[n] = t.second.ms;
+      if (launches) launches[n] = t.second.n;
+    }
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

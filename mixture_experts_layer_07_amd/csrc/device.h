@@ -1,0 +1,88 @@
+// Device-side helpers for gfx950 (CDNA4): vector types, bf16 and e4m3 conversions,
+// wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even (inputs here are never NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// e4m3 ("fn" variant: bias 7, max 448, no infinities) from fp32: round to nearest even,
+// saturate to +-448, keep the sign (a negative value that rounds to zero gives 0x80).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  const uint32_t au = __float_as_uint(a);
+  const int ex = (int)(au >> 23) - 127;
+  if (ex < -6) {
+    // subnormal range: value = m * 2^-9, m in [0, 8]; m == 8 is the smallest normal (0x08)
+    const float m = rintf(a * 512.0f);
+    return sign | (uint32_t)m;
+  }
+  uint32_t keep = (au >> 20) & 7u;
+  const uint32_t rest = au & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep += 1;
+  uint32_t e = (uint32_t)(ex + 7);
+  if (keep == 8) {
+    keep = 0;
+    e += 1;
+  }
+  return sign | (e << 3) | keep;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Exclusive scan of one int per thread over a 256-thread workgroup (all threads must call);
+// returns this thread's exclusive prefix and the workgroup total in *tot.
+__device__ __forceinline__ int block_exscan_256(int v, int* sbuf4, int* tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sbuf4[wave] = incl;
+  __syncthreads();
+  int wbase = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int sw = sbuf4[w];
+    if (w < wave) wbase += sw;
+    all += sw;
+  }
+  __syncthreads();
+  *tot = all;
+  return wbase + incl - v;
+}
+
+// Workgroup id remapped so that consecutive logical ids run on the same XCD. Workgroups are
+// dispatched round-robin over the 8 XCDs; with a grid that is a multiple of 8, logical id
+// (x * G/8 + j) is placed on physical id (j * 8 + x), i.e. on XCD x.
+__device__ __forceinline__ int xcd_local_id(int b, int G) { return (b & 7) * (G >> 3) + (b >> 3); }
+
+}  // namespace moe

@@ -1,0 +1,112 @@
+// Internal declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <utility>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- workspace layout
+// One caller-owned arena, carved in a fixed order (every region 256-byte aligned):
+//   err      int32 device error word (+ padding)
+//   logits   [splits][T][E] fp32 router partial logits (summed in split order by top-K)
+//   wrt      [E][H] bf16 router weights transposed to K-major (bf16 / fp8 layers)
+//   hist     [perm_blocks][E] int32 per-block expert histogram
+//   base     [perm_blocks][E] int32 per-block starting rank inside each expert
+//   tiles    [2][257] int32 m-tile prefix sums of the grouped GEMMs
+//   h        [max_rows][max_I] SwiGLU output (fp32 / bf16 / e4m3 codes)
+//   hscale   [max_rows][max_I/128] fp32 (fp8 layer)
+struct WsLayout {
+  size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, h = 0, hscale = 0, total = 0;
+  int route_splits = 1;
+  int perm_blocks = 0;
+};
+
+constexpr int kPermBlock = 256;   // pairs per block in the permutation kernels
+constexpr int kMaxExperts = 256;
+
+// Validation; returns MOE_OK or the failure status with a reason in *why.
+moe_status check_config(const moe_config* c, std::string* why);
+// Workspace layout of a valid config.
+WsLayout layout(const moe_config& c);
+// Router split-K factor chosen from the shape (deterministic, host-side).
+int route_splits(const moe_config& c);
+
+// ---------------------------------------------------------------- profiling
+bool profiling_enabled();
+void profile_record(const char* name, hipEvent_t a, hipEvent_t b);
+
+// Launch `f` (which enqueues exactly one kernel on `s`), bracketed by HIP events on `s`
+// when profiling is on. Returns the launch error, if any.
+template <class F>
+hipError_t timed_launch(const char* name, hipStream_t s, F&& f) {
+  hipEvent_t a = nullptr, b = nullptr;
+  const bool prof = profiling_enabled();
+  if (prof) {
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return hipErrorOutOfMemory;
+    (void)hipEventRecord(a, s);
+  }
+  std::forward<F>(f)();
+  hipError_t e = hipGetLastError();
+  if (prof) {
+    (void)hipEventRecord(b, s);
+    profile_record(name, a, b);
+  }
+  return e;
+}
+
+// ---------------------------------------------------------------- launchers (kernels_*.hip)
+struct DevInfo {
+  int cus = 256;
+};
+const DevInfo& dev_info();
+
+// route
+hipError_t launch_router_f32(const float* x, const float* wr, float* logits, int T, int H, int E,
+                             hipStream_t s);
+hipError_t launch_transpose_bf16(const void* in, void* out, int rows, int cols, hipStream_t s);
+hipError_t launch_router_bf16(const void* x, const void* wrt, float* logits, int T, int H, int E,
+                              int splits, hipStream_t s);
+hipError_t launch_topk(const moe_config& c, const float* logits, int splits, const float* bias,
+                       int32_t* ids, float* weights, hipStream_t s);
+// permute
+hipError_t launch_clear_words(int32_t* p, int n, hipStream_t s);
+hipError_t launch_perm_hist(const int32_t* ids, int P, int E, int32_t* hist, int32_t* err,
+                            hipStream_t s);
+hipError_t launch_perm_scan(const int32_t* hist, int nblk, int E, int32_t* base, int32_t* counts,
+                            hipStream_t s);
+hipError_t launch_perm_scatter(const int32_t* ids, int P, int E, const int32_t* base,
+                               const int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                               int32_t* pair_pos, hipStream_t s);
+hipError_t launch_gather(const moe_config& c, const int32_t* sorted_pair, const void* x,
+                         void* x_perm, float* x_scale, hipStream_t s);
+hipError_t launch_quantize_fp8(int rows, int cols, const void* in, uint8_t* codes, float* scales,
+                               hipStream_t s);
+// expert FFN
+struct FfnArgs {
+  int dtype = MOE_BF16;
+  int n_exp = 0, n_rows = 0, H = 0, I = 0;
+  const int32_t* offsets = nullptr;
+  const void* x = nullptr;
+  const float* x_scale = nullptr;
+  const void* w13 = nullptr;
+  const float* w13_scale = nullptr;
+  const void* w2 = nullptr;
+  const float* w2_scale = nullptr;
+  void* y = nullptr;
+  void* h = nullptr;          // workspace
+  float* h_scale = nullptr;   // workspace (fp8)
+  int32_t* tiles = nullptr;   // workspace, [2][257]
+};
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s);
+// combine
+hipError_t launch_combine(const moe_config& c, const int32_t* pair_pos, const float* w,
+                          const void* y_perm, const void* y_shared, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,111 @@
+// Weighted combine back to [T,H].
+//
+// "MoE 路由入门：从 Dense FFN 到 GroupedTopK" (blog.freezetheflame.cc), section 5.3: each token's
+// K expert outputs are summed with its top-K weights, giving [T,H] again. The always-on shared
+// expert joins the sum before the residual ("MoE" chapter README, llm-infra-atlas.github.io/moe,
+// section 0). The combine is a gather: token t reads its K rows of y_perm through pair_pos, so no
+// atomics are needed and the result does not depend on scheduling. Accumulation is fp32 in k
+// order, the shared row last, then one rounding to the output type.
+//
+// Expert rows arrive as fp32 (fp32 and bf16 layers) or bf16 (fp8 layer); the output is fp32
+// (fp32 layer) or bf16. Each thread handles EPC consecutive channels per step.
+#include "device.h"
+#include "internal.h"
+
+namespace moe {
+
+template <int EPC, bool YF32>
+__device__ __forceinline__ void load_row_chunk(const uint8_t* row, int ch, float (&v)[EPC]) {
+  if constexpr (YF32) {
+    const float* p = reinterpret_cast<const float*>(row) + (size_t)ch * EPC;
+#pragma unroll
+    for (int q = 0; q < EPC / 4; ++q) {
+      const float4 f = reinterpret_cast<const float4*>(p)[q];
+      v[4 * q + 0] = f.x;
+      v[4 * q + 1] = f.y;
+      v[4 * q + 2] = f.z;
+      v[4 * q + 3] = f.w;
+    }
+  } else {
+    static_assert(EPC == 8, "bf16 rows are read 8 channels at a time");
+    const uint4 u = reinterpret_cast<const uint4*>(row)[ch];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_to_f32(w[j] & 0xFFFF);
+      v[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+  }
+}
+
+template <int EPC, bool YF32, bool OF32>
+__global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ pair_pos,
+                                                 const float* __restrict__ w,
+                                                 const uint8_t* __restrict__ y,
+                                                 const uint8_t* __restrict__ ysh,
+                                                 uint8_t* __restrict__ out, int H, int K) {
+  __shared__ int spp[kMaxExperts];
+  __shared__ float sw[kMaxExperts];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  for (int k = tid; k < K; k += 256) {
+    spp[k] = pair_pos[(size_t)t * K + k];
+    sw[k] = w[(size_t)t * K + k];
+  }
+  __syncthreads();
+  const size_t yrow = (size_t)H * (YF32 ? 4 : 2);
+  const size_t orow = (size_t)H * (OF32 ? 4 : 2);
+  const int nch = H / EPC;
+  for (int ch = tid; ch < nch; ch += 256) {
+    float acc[EPC], v[EPC];
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int r = spp[k];
+      if (r < 0) continue;
+      load_row_chunk<EPC, YF32>(y + (size_t)r * yrow, ch, v);
+      const float wk = sw[k];
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] = fmaf(wk, v[j], acc[j]);
+    }
+    if (ysh) {
+      load_row_chunk<EPC, YF32>(ysh + (size_t)t * yrow, ch, v);
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] += v[j];
+    }
+    uint8_t* o = out + (size_t)t * orow;
+    if constexpr (OF32) {
+#pragma unroll
+      for (int q = 0; q < EPC / 4; ++q)
+        reinterpret_cast<float4*>(o)[(size_t)ch * (EPC / 4) + q] =
+            make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    } else {
+      static_assert(OF32 || EPC == 8, "bf16 output is written 8 channels at a time");
+      uint32_t u[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        u[j] = (uint32_t)f32_to_bf16(acc[2 * j]) | ((uint32_t)f32_to_bf16(acc[2 * j + 1]) << 16);
+      reinterpret_cast<uint4*>(o)[ch] = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+  }
+}
+
+hipError_t launch_combine(const moe_config& c, const int32_t* pair_pos, const float* w,
+                          const void* y_perm, const void* y_shared, void* out, hipStream_t s) {
+  const uint8_t* y = static_cast<const uint8_t*>(y_perm);
+  const uint8_t* ysh = static_cast<const uint8_t*>(y_shared);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  const dim3 grid(c.T), block(256);
+  if (c.dtype == MOE_F32)
+    return timed_launch("combine_f32", s, [&] {
+      hipLaunchKernelGGL((k_combine<4, true, true>), grid, block, 0, s, pair_pos, w, y, ysh, o, c.H, c.K);
+    });
+  if (c.dtype == MOE_BF16)
+    return timed_launch("combine_f32_to_bf16", s, [&] {
+      hipLaunchKernelGGL((k_combine<8, true, false>), grid, block, 0, s, pair_pos, w, y, ysh, o, c.H, c.K);
+    });
+  return timed_launch("combine_bf16", s, [&] {
+    hipLaunchKernelGGL((k_combine<8, false, false>), grid, block, 0, s, pair_pos, w, y, ysh, o, c.H, c.K);
+  });
+}
+
+}  // namespace moe

@@ -1,0 +1,96 @@
+// Host-side argument validation and workspace layout. No HIP runtime calls here, so
+// every check runs (and is tested) without a GPU.
+#include <stdint.h>
+
+#include <string>
+
+#include "internal.h"
+
+namespace moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+moe_status check_config(const moe_config* c, std::string* why) {
+  auto bad = [&](moe_status s, const char* msg) {
+    if (why) *why = msg;
+    return s;
+  };
+  if (!c) return bad(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (c->T < 1 || c->H < 1 || c->I < 1 || c->E < 1 || c->K < 1)
+    return bad(MOE_ERR_INVALID_ARG, "T, H, I, E and K must be positive");
+  if (c->K > c->E) return bad(MOE_ERR_INVALID_ARG, "K must not exceed E");
+  if (c->E > kMaxExperts) return bad(MOE_ERR_UNSUPPORTED, "E above 256 is not supported");
+  if (c->score_fn != MOE_SOFTMAX && c->score_fn != MOE_SIGMOID)
+    return bad(MOE_ERR_INVALID_ARG, "unknown score function");
+  if (c->renorm != 0 && c->renorm != 1) return bad(MOE_ERR_INVALID_ARG, "renorm must be 0 or 1");
+  if (!(c->route_scale == c->route_scale) || c->route_scale > 3.0e38f || c->route_scale < -3.0e38f)
+    return bad(MOE_ERR_INVALID_ARG, "route_scale must be finite");
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8_E4M3)
+    return bad(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (c->n_group < 1 || c->E % c->n_group != 0)
+    return bad(MOE_ERR_INVALID_ARG, "n_group must be >= 1 and divide E");
+  if (c->n_group > 1) {
+    if (c->topk_group < 1 || c->topk_group > c->n_group)
+      return bad(MOE_ERR_INVALID_ARG, "topk_group must be in [1, n_group]");
+    if ((int64_t)c->K > (int64_t)c->topk_group * (c->E / c->n_group))
+      return bad(MOE_ERR_INVALID_ARG, "K exceeds the experts of the kept groups");
+    if (c->group_score != MOE_GROUP_MAX && c->group_score != MOE_GROUP_TOP2_SUM)
+      return bad(MOE_ERR_INVALID_ARG, "unknown group score");
+    if (c->group_score == MOE_GROUP_TOP2_SUM && c->E / c->n_group < 2)
+      return bad(MOE_ERR_INVALID_ARG, "top-2-sum group score needs >= 2 experts per group");
+  }
+  if (c->I_shared < 0) return bad(MOE_ERR_INVALID_ARG, "I_shared must be >= 0");
+  const int q = (c->dtype == MOE_F32) ? 4 : 128;
+  if (c->H % q || c->I % q || c->I_shared % q)
+    return bad(MOE_ERR_UNSUPPORTED,
+               c->dtype == MOE_F32 ? "fp32 layers need H, I, I_shared multiples of 4"
+                                   : "bf16/fp8 layers need H, I, I_shared multiples of 128");
+  const int64_t P = (int64_t)c->T * c->K;
+  if (P >= (int64_t(1) << 31)) return bad(MOE_ERR_INVALID_ARG, "T*K must be below 2^31");
+  const int64_t maxI = c->I > c->I_shared ? c->I : c->I_shared;
+  if (P * c->H >= (int64_t(1) << 40) || P * 2 * maxI >= (int64_t(1) << 40))
+    return bad(MOE_ERR_UNSUPPORTED, "buffers above 2^40 elements are not supported");
+  if ((int64_t)c->H * 2 * maxI >= (int64_t(1) << 31))
+    return bad(MOE_ERR_UNSUPPORTED, "one expert above 2^31 elements is not supported");
+  return MOE_OK;
+}
+
+int route_splits(const moe_config& c) {
+  if (c.dtype == MOE_F32) return 1;
+  const int mtiles = (c.T + 31) / 32;
+  const int nk = c.H / 128;
+  int want = (256 + mtiles - 1) / mtiles;  // aim for >= 256 workgroups
+  if (want < 1) want = 1;
+  return want < nk ? want : nk;
+}
+
+WsLayout layout(const moe_config& c) {
+  WsLayout L;
+  const size_t T = (size_t)c.T, E = (size_t)c.E, H = (size_t)c.H;
+  const size_t P = T * (size_t)c.K;
+  const size_t maxI = (size_t)(c.I > c.I_shared ? c.I : c.I_shared);
+  L.route_splits = route_splits(c);
+  L.perm_blocks = (int)((P + kPermBlock - 1) / kPermBlock);
+  size_t off = 0;
+  L.err = off;
+  off += 256;
+  L.logits = off;
+  off = align256(off + (size_t)L.route_splits * T * E * 4);
+  L.wrt = off;
+  off = align256(off + (c.dtype == MOE_F32 ? 0 : E * H * 2));
+  L.hist = off;
+  off = align256(off + (size_t)L.perm_blocks * E * 4);
+  L.base = off;
+  off = align256(off + (size_t)L.perm_blocks * E * 4);
+  L.tiles = off;
+  off = align256(off + 2 * 257 * 4);
+  const size_t elem = c.dtype == MOE_F32 ? 4 : (c.dtype == MOE_BF16 ? 2 : 1);
+  L.h = off;
+  off = align256(off + P * maxI * elem);
+  L.hscale = off;
+  off = align256(off + (c.dtype == MOE_FP8_E4M3 ? P * (maxI / 128) * 4 : 0));
+  L.total = off;
+  return L;
+}
+
+}  // namespace moe

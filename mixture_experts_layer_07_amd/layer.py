@@ -1,0 +1,88 @@
+"""One MoE layer forward on torch device buffers: the four C-ABI calls in order.
+
+route -> permute -> expert FFN (routed experts, then the shared expert if any) -> combine.
+Buffers are allocated once at construction and reused by every forward; the calls are
+enqueued on the current stream and none of them waits.
+"""
+import torch
+
+from . import binding as B
+from .configs import LayerConfig
+
+
+class MoELayer:
+    def __init__(self, cfg: LayerConfig, w_router, bias, experts, shared=None, device="cuda"):
+        """experts / shared: dicts with w13, w2 (+ w13_scale, w2_scale for fp8) on `device`."""
+        self.cfg = cfg
+        self.c = B.make_config(cfg)
+        B.moe_check_config(self.c)
+        T, H, E, K, P = cfg.T, cfg.H, cfg.E, cfg.K, cfg.P
+        act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        self.fp8 = cfg.dtype == "fp8"
+        dev = torch.device(device)
+        self.w_router = w_router
+        self.bias = bias
+        self.experts = experts
+        self.shared = shared if cfg.I_shared > 0 else None
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.ws = torch.empty(B.moe_workspace_size(self.c), dtype=torch.uint8, device=dev)
+        self.ws[:256].zero_()
+        self.topk_ids = torch.empty((T, K), **i32)
+        self.topk_weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.sorted_pair = torch.empty(P, **i32)
+        self.pair_pos = torch.empty(P, **i32)
+        self.x_perm = torch.empty((P, H), dtype=torch.uint8 if self.fp8 else act, device=dev)
+        self.x_perm_scale = (torch.empty((P, H // 128), dtype=torch.float32, device=dev)
+                             if self.fp8 else None)
+        # expert outputs: fp32 accumulators for fp32 / bf16 layers, bf16 for the fp8 layer
+        ydt = torch.bfloat16 if self.fp8 else torch.float32
+        self.y_perm = torch.empty((P, H), dtype=ydt, device=dev)
+        self.out = torch.empty((T, H), dtype=act, device=dev)
+        if self.shared is not None:
+            self.y_shared = torch.empty((T, H), dtype=ydt, device=dev)
+            self.shared_offsets = torch.tensor([0, T], **i32)
+            if self.fp8:
+                self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+                self.xq_scale = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+        else:
+            self.y_shared = None
+
+    def route(self, x):
+        B.moe_route(self.c, x, self.w_router, self.bias, self.topk_ids, self.topk_weights, self.ws)
+
+    def permute(self, x):
+        B.moe_permute(self.c, self.topk_ids, self.counts, self.offsets, self.sorted_pair,
+                      self.pair_pos, x, self.x_perm, self.x_perm_scale, self.ws)
+
+    def expert_ffn(self):
+        ex = self.experts
+        B.moe_expert_ffn(self.c, self.cfg.E, self.cfg.P, self.cfg.I, self.offsets, self.x_perm,
+                         self.x_perm_scale, ex["w13"], ex.get("w13_scale"), ex["w2"],
+                         ex.get("w2_scale"), self.y_perm, self.ws)
+
+    def shared_ffn(self, x):
+        if self.shared is None:
+            return
+        sh = self.shared
+        xs, xs_scale = x, None
+        if self.fp8:
+            B.moe_quantize_fp8(self.cfg.T, self.cfg.H, x, self.xq, self.xq_scale)
+            xs, xs_scale = self.xq, self.xq_scale
+        B.moe_expert_ffn(self.c, 1, self.cfg.T, self.cfg.I_shared, self.shared_offsets, xs, xs_scale,
+                         sh["w13"], sh.get("w13_scale"), sh["w2"], sh.get("w2_scale"),
+                         self.y_shared, self.ws)
+
+    def combine(self):
+        B.moe_combine(self.c, self.pair_pos, self.topk_weights, self.y_perm, self.y_shared, self.out)
+
+    def forward(self, x):
+        self.route(x)
+        self.permute(x)
+        self.expert_ffn()
+        self.shared_ffn(x)
+        self.combine()
+        return self.out
+
+    __call__ = forward

@@ -56,7 +56,8 @@ __all__ = [
     "route", "near_tie_tokens", "permute", "gather_rows",
     "e4m3_decode", "e4m3_decode_array", "e4m3_encode",
     "quantize_rows_fp8", "dequantize_rows_fp8", "dequantize_weight_blocks",
-    "silu", "swiglu_expert", "expert_ffn", "combine", "moe_layer", "dense_mix",
+    "silu", "swiglu_hidden", "swiglu_expert", "expert_ffn", "combine",
+    "moe_layer", "dense_mix",
 ]
 
 NEAR_TIE_GAP = 1e-5   # key gap under which a selection is reported as a near tie
@@ -325,6 +326,14 @@ def silu(g):
         return g / (1.0 + np.exp(-g))
 
 
+def swiglu_hidden(x, w13):
+    """SiLU(W_gate x) * W_up x per row ([primer] §1): x [M,H], w13 [2I,H] -> [M,I] fp64."""
+    x = np.asarray(x, np.float64)
+    w13 = np.asarray(w13, np.float64)
+    I = w13.shape[0] // 2
+    return silu(x @ w13[:I].T) * (x @ w13[I:].T)
+
+
 def swiglu_expert(x, w13, w2, fp8_hidden=False):
     """One SwiGLU expert on rows of x ([primer] §1, [survey] §1 and §5.1).
 
@@ -334,12 +343,7 @@ def swiglu_expert(x, w13, w2, fp8_hidden=False):
     output is quantised per row per 128 channels and dequantised before
     Linear-2, as the fp8 layer does ("SwiGLU / FP8 Cast", [survey] §5.1).
     """
-    x = np.asarray(x, np.float64)
-    w13 = np.asarray(w13, np.float64)
-    I = w13.shape[0] // 2
-    g = x @ w13[:I].T
-    u = x @ w13[I:].T
-    a = silu(g) * u
+    a = swiglu_hidden(x, w13)
     if fp8_hidden:
         codes, s = quantize_rows_fp8(a)
         a = dequantize_rows_fp8(codes, s)

@@ -1,0 +1,143 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases: every stage on every row, at shapes that span several tiles and ragged tails.
+Full cases: the five workloads at their real sizes, in the same launch configuration as the
+benchmark: all ids and the permutation exactly, outputs on sampled rows and tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from mixture_experts_layer_07_amd import binding as B
+from mixture_experts_layer_07_amd.configs import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_parity import Case, check_ffn, full_check, row_err, sample_rows  # noqa: E402
+
+
+def zipf_bias(E, s=1.2, seed=0, scale=0.15):
+    """A skewed selection bias for small decode-shaped cases: b_e = scale * log(rank^-s)."""
+    rank = np.random.default_rng(seed).permutation(E) + 1
+    return torch.tensor(scale * np.log(rank.astype(np.float64) ** -s) + 0.3, dtype=torch.float32)
+
+
+SMALL = {
+    "tiny-fp32": (CONFIGS[1], None),
+    "mixtral-bf16": (CONFIGS[2].scaled(T=520, H=384, I=384), None),
+    "dsv3-bf16": (CONFIGS[3].scaled(T=520, H=256, I=256, E=32, K=8, I_shared=128), None),
+    "decode-bf16": (CONFIGS[4].scaled(T=40, H=512, I=256, E=64, K=8, bias="normal", I_shared=256), "zipf"),
+    # fp8: the real intermediate size, so one flipped hidden code weighs what it does at full size
+    "dsv3-fp8": (CONFIGS[5].scaled(T=260, H=256, I=2048, E=32, K=8, I_shared=2048), None),
+    "decode-fp8": (CONFIGS[5].scaled(T=24, H=256, I=2048, E=64, K=8, I_shared=2048), None),
+    "fp32-grouped": (CONFIGS[3].scaled(T=100, H=64, I=96, E=16, K=4, n_group=4, topk_group=2,
+                                       dtype="f32", I_shared=32), None),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_layer_parity(name):
+    cfg, bias = SMALL[name]
+    b = zipf_bias(cfg.E) if bias == "zipf" else None
+    case = Case(cfg, bias=b)
+    rep = full_check(case)
+    print(name, rep)
+
+
+def test_determinism_run_twice_bitwise():
+    cfg = SMALL["dsv3-bf16"][0]
+    case = Case(cfg)
+    a = case.run().clone()
+    ids = case.layer.topk_ids.clone()
+    b = case.run().clone()
+    assert torch.equal(ids, case.layer.topk_ids)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_single_token_and_all_experts():
+    # T = 1, and K = E (every expert selected)
+    for cfg in (CONFIGS[3].scaled(T=1, H=256, I=128, E=16, K=4, n_group=4, topk_group=2, I_shared=128),
+                CONFIGS[2].scaled(T=33, H=256, I=128, E=4, K=4)):
+        full_check(Case(cfg))
+
+
+def test_permute_skewed_ids_and_ragged_experts():
+    # caller-supplied ids: expert 3 gets every token (2 m-tiles of 256 plus a tail), most experts none
+    cfg = CONFIGS[2].scaled(T=300, H=256, I=256, E=16, K=2)
+    case = Case(cfg)
+    L = case.layer
+    t = torch.arange(cfg.T)
+    ids = torch.stack([torch.full_like(t, 3), torch.where(t % 3 == 0, 5, 15)], 1).to(torch.int32)
+    L.topk_ids.copy_(ids)
+    L.permute(case.xd)
+    L.expert_ffn()
+    torch.cuda.synchronize()
+    counts, offsets, sp, pp = orc.permute(ids.numpy(), cfg.E)
+    assert (L.offsets.cpu().numpy() == offsets).all()
+    assert (L.sorted_pair.cpu().numpy() == sp).all() and (L.pair_pos.cpu().numpy() == pp).all()
+    check_ffn(case, offsets, np.arange(cfg.P), {})
+    assert B.moe_get_device_error(L.ws) == 0
+
+
+def test_out_of_range_ids_set_the_device_error():
+    cfg = CONFIGS[2].scaled(T=64, H=256, I=128, E=8, K=2)
+    case = Case(cfg)
+    L = case.layer
+    ids = torch.randint(0, 8, (cfg.T, cfg.K), dtype=torch.int32)
+    ids[5, 1] = 8
+    ids[9, 0] = -1
+    L.topk_ids.copy_(ids)
+    L.permute(case.xd)
+    assert B.moe_get_device_error(L.ws) == 1
+    assert B.moe_get_device_error(L.ws) == 0       # read clears
+    pp = L.pair_pos.cpu().numpy()
+    assert pp[5 * 2 + 1] == -1 and pp[9 * 2] == -1
+    assert int(L.offsets[-1]) == cfg.P - 2
+
+
+def test_quantize_fp8_bit_exact():
+    rng = np.random.default_rng(0)
+    rows = rng.normal(size=(37, 512)).astype(np.float32)
+    rows[3] = 0.0                                       # all-zero blocks
+    rows[4, :128] = 1e-30                               # tiny values
+    rows[5, 128:256] = np.linspace(-448, 448, 128)      # exact grid points
+    rows[6] *= 1e4
+    x = torch.from_numpy(rows).to(torch.bfloat16)
+    codes = torch.empty((37, 512), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((37, 4), dtype=torch.float32, device="cuda")
+    B.moe_quantize_fp8(37, 512, x.cuda(), codes, scales)
+    torch.cuda.synchronize()
+    want_c, want_s = orc.quantize_rows_fp8(x.float().numpy())
+    assert (scales.cpu().numpy() == want_s).all()
+    assert (codes.cpu().numpy() == want_c).all()
+
+
+FULL = [1, 2, 3, 4, 5]
+
+
+@pytest.mark.parametrize("cid", FULL)
+def test_full_size_parity(cid):
+    """Real workload sizes: exact routing / permutation; sampled expert rows and tokens."""
+    cfg = CONFIGS[cid]
+    case = Case(cfg, wdev="cuda")
+    rng = np.random.default_rng(cid)
+    case.run()
+    from gpu_parity import (check_combine, check_end_to_end, check_permute, check_route,
+                            check_shared)
+    rep = {}
+    ids_g, w_g = check_route(case, rep)
+    perm_rows = None if cfg.P <= 16384 else rng.integers(0, cfg.P, 256)
+    counts, offsets, sp, pp = check_permute(case, ids_g, perm_rows)
+    if cfg.P <= 1024:
+        rows = np.arange(cfg.P) if cfg.T * cfg.H <= 2 ** 16 else sample_rows(offsets, 24, rng)
+    else:
+        rows = sample_rows(offsets, 12, rng)
+    check_ffn(case, offsets, rows, rep)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 6)]))
+    if cfg.I_shared:
+        check_shared(case, toks, rep)
+    check_combine(case, pp, w_g, toks, rep)
+    check_end_to_end(case, ids_g, w_g, toks, rep)
+    print(cfg.name, rep, "empty experts:", int((counts == 0).sum()), "max count:", int(counts.max()))
