@@ -1,0 +1,134 @@
+// Shared pieces of the grouped expert GEMMs: arguments, tile decode, weight-row mapping,
+// direct-to-LDS tile loads and the epilogue activation.
+//
+// A grouped GEMM is a set of per-expert GEMMs run by one kernel whose tiles carry an expert id
+// ("MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", wqh011128.github.io, 3.7.2);
+// per-expert row counts are dynamic ("MoE 路由入门：从 Dense FFN 到 GroupedTopK", 5.2).
+#pragma once
+
+#include "device.h"
+#include "internal.h"
+
+namespace moe {
+
+struct GemmArgs {
+  const uint8_t* A;
+  size_t lda;           // bytes per A row
+  const float* a_scale; // fp8: [rows][K/128]
+  int a_scale_ld;
+  const uint8_t* B;
+  size_t ldb;           // bytes per B row
+  size_t b_exp;         // bytes per expert
+  const float* b_scale; // fp8: [n_exp][Nb/128][K/128]
+  int b_scale_ld;       // K/128
+  size_t b_scale_exp;   // floats per expert
+  uint8_t* C;
+  size_t ldc;           // bytes per C row
+  float* c_scale;       // fp8 GLU output: [rows][N_out/128]
+  int c_scale_ld;
+  const int32_t* offsets;
+  const int32_t* tp;
+  int n_exp, K, N_out, Nb, glu_I, n_tiles_n;
+};
+
+struct TileInfo {
+  int e, mt, nt, row0, mvalid;
+};
+
+// Logical tile t in expert-major order (expert, then n-tile, then m-tile): the m-tiles that
+// share one weight block are neighbours. tp[e] = m-tiles before expert e (in LDS).
+__device__ __forceinline__ TileInfo decode_tile(int t, const int* tp, const GemmArgs& g, int BM) {
+  TileInfo ti;
+  const int q = t / g.n_tiles_n;
+  int lo = 0, hi = g.n_exp - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tp[mid] <= q)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  ti.e = lo;
+  const int mcount = tp[lo + 1] - tp[lo];
+  const int local = t - tp[lo] * g.n_tiles_n;
+  ti.nt = local / mcount;
+  ti.mt = local - ti.nt * mcount;
+  const int seg0 = g.offsets[lo], seg1 = g.offsets[lo + 1];
+  ti.row0 = seg0 + ti.mt * BM;
+  const int mv = seg1 - ti.row0;
+  ti.mvalid = mv < BM ? mv : BM;
+  return ti;
+}
+
+// Weight row held in row r of the B tile. GLU (Linear-1): 32-row blocks alternate gate / up,
+// so a wave's neighbouring n-blocks hold gate column j and up column j in the same lanes.
+template <bool GLU, int BN>
+__device__ __forceinline__ int weight_row(int r, int nt, const GemmArgs& g) {
+  if (GLU) {
+    const int blk = r >> 5;
+    const int j = nt * (BN / 2) + (blk >> 1) * 32 + (r & 31);
+    return (blk & 1) ? g.glu_I + j : j;
+  }
+  const int n = nt * BN + r;
+  return n < g.Nb ? n : g.Nb - 1;
+}
+
+// SiLU(x) = x * sigmoid(x); the hardware exp's error is far below the bf16 / e4m3 rounding of h.
+__device__ __forceinline__ float silu_fast(float x) { return x / (1.0f + __expf(-x)); }
+
+// LDS tile layout: rows of 128 bytes = 8 chunks of 16 bytes; chunk c of row r is stored at
+// position c ^ (r & 7) so that the 16-byte MFMA operand reads of 8 consecutive rows hit 8
+// different bank groups.
+__device__ __forceinline__ int lds_swz(int row) { return row & 7; }
+
+// Direct-to-LDS tile loads (global_load_lds_dwordx4): one instruction moves 64 x 16 bytes from
+// per-lane global addresses to 1 KB of LDS at a wave-uniform base, lane i writing 16*i.
+// Instance j of wave w therefore fills tile rows (j*NW + w)*8 .. +8; lane i loads the global
+// chunk that the swizzle puts at its LDS slot. off[] holds per-lane byte offsets from a
+// wave-uniform global base; the K step adds a uniform offset.
+template <int J>
+struct TileDma {
+  uint32_t off[J];
+};
+
+template <int NW>
+__device__ __forceinline__ int dma_row(int j, int wave, int lane) { return (j * NW + wave) * 8 + (lane >> 3); }
+
+__device__ __forceinline__ int dma_chunk(int lane) { return (lane & 7) ^ lds_swz(lane >> 3); }
+
+// A macro, so that the builtin sees the __shared__ stage itself (its LDS address space is lost
+// through a function parameter).
+// The builtin only exists on the device pass; on the host pass __shared__ memory has no LDS
+// address space and the call would be ill-formed (which silently drops the kernel templates from
+// the host object), so it is compiled for the device only.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(const void* gptr, void* lptr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(BYTES == 16 || BYTES == 4, "16- or 4-byte transfers");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lptr, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lptr, 4, 0, 0);
+#endif
+}
+
+// The trailing scheduling barrier keeps the loads where they are written: ahead of the MFMAs they
+// are meant to overlap (left alone, the scheduler sinks them to the wait at the end of the step).
+#define MOE_DMA_ISSUE(J, NW, base, d, koff, lds_tile, wave)                                        \
+  do {                                                                                             \
+    _Pragma("unroll") for (int j_ = 0; j_ < (J); ++j_)                                             \
+        dma_to_lds<16>((base) + ((d).off[j_] + (koff)), (lds_tile) + (j_ * (NW) + (wave)) * 64);   \
+    __builtin_amdgcn_sched_barrier(0);                                                             \
+  } while (0)
+
+// Wait for this wave's direct-to-LDS loads, then for every wave (the stage becomes readable).
+__device__ __forceinline__ void dma_wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// Declared launchers (kernels_gemm_*.hip)
+hipError_t launch_gemm_bf16(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,173 @@
+// bf16 grouped GEMMs of the SwiGLU experts on MFMA 32x32x16 (fp32 accumulate).
+//
+// Linear-1 computes gate and up together and applies SwiGLU in the epilogue; Linear-2 is the
+// down projection ("MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", 5.1;
+// expert function from "MoE 路由入门：从 Dense FFN 到 GroupedTopK", section 1).
+//
+// Persistent grid over the expert-major tile list (gemm_common.h); per tile a K loop of
+// 64-channel steps: direct-to-LDS loads of step k+1 into one LDS stage while the MFMAs of step
+// k read the other, one barrier per step. Inside a step the operand fragments of sub-step s+1
+// are read from LDS while the MFMAs of sub-step s run.
+#include "gemm_common.h"
+
+namespace moe {
+
+template <int MB, int NB, int WM, int WN, int ACH>
+__device__ __forceinline__ void mma_step_bf16(const u32x4* st, f32x16 (&acc)[MB][NB], int wm, int wn,
+                                              int lane) {
+  const int lrow = lane & 31, lk = lane >> 5, lsw = lane & 7;
+  const u32x4* la = st + (wm * WM + lrow) * 8;
+  const u32x4* lb = st + ACH + (wn * WN + lrow) * 8;
+  bf16x8 a[2][MB], b[2][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) a[0][mb] = __builtin_bit_cast(bf16x8, la[mb * 256 + (lk ^ lsw)]);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) b[0][nb] = __builtin_bit_cast(bf16x8, lb[nb * 256 + (lk ^ lsw)]);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int cur = ks & 1;
+    if (ks < 3) {
+      const int ch = ((ks + 1) * 2 + lk) ^ lsw;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) a[cur ^ 1][mb] = __builtin_bit_cast(bf16x8, la[mb * 256 + ch]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) b[cur ^ 1][nb] = __builtin_bit_cast(bf16x8, lb[nb * 256 + ch]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mb], b[cur][nb], acc[mb][nb], 0, 0, 0);
+  }
+}
+
+// OUTF32 (plain GEMM only): store the fp32 accumulators instead of rounding them to bf16.
+template <int BM, int BN, int NWM, int NWN, bool GLU, int MINB, bool OUTF32>
+__global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) {
+  constexpr int NT = NWM * NWN * 64, NW = NWM * NWN;
+  constexpr int WM = BM / NWM, WN = BN / NWN, MB = WM / 32, NB = WN / 32;
+  constexpr int ACH = BM * 8, BCH = BN * 8;
+  constexpr int AJ = ACH / NT, BJ = BCH / NT;
+  static_assert(ACH % NT == 0 && BCH % NT == 0, "tile / thread mismatch");
+  static_assert(!GLU || NB % 2 == 0, "GLU needs gate/up block pairs per wave");
+  __shared__ u32x4 st0[ACH + BCH];
+  __shared__ u32x4 st1[ACH + BCH];
+  __shared__ int tp[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  for (int i = tid; i <= g.n_exp; i += NT) tp[i] = g.tp[i];
+  __syncthreads();
+  const int total = tp[g.n_exp] * g.n_tiles_n;
+  const int KT = g.K / 64;
+  const int lrow = lane & 31, lk = lane >> 5;
+  const uint32_t cb = (uint32_t)dma_chunk(lane) * 16;
+
+  for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+    const TileInfo ti = decode_tile(t, tp, g, BM);
+    const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
+    const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
+    TileDma<AJ> da;
+    TileDma<BJ> db;
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) {
+      const int r = dma_row<NW>(j, wave, lane);
+      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      da.off[j] = (uint32_t)rr * (uint32_t)g.lda + cb;
+    }
+#pragma unroll
+    for (int j = 0; j < BJ; ++j)
+      db.off[j] = (uint32_t)weight_row<GLU, BN>(dma_row<NW>(j, wave, lane), ti.nt, g) * (uint32_t)g.ldb + cb;
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+    MOE_DMA_ISSUE(AJ, NW, Ab, da, 0, st0, wave);
+    MOE_DMA_ISSUE(BJ, NW, Be, db, 0, st0 + ACH, wave);
+    dma_wait_and_barrier();
+    for (int kt = 0; kt + 1 < KT; kt += 2) {
+      MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt + 1) * 128u, st1, wave);
+      MOE_DMA_ISSUE(BJ, NW, Be, db, (uint32_t)(kt + 1) * 128u, st1 + ACH, wave);
+      mma_step_bf16<MB, NB, WM, WN, ACH>(st0, acc, wm, wn, lane);
+      dma_wait_and_barrier();
+      if (kt + 2 < KT) {
+        MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt + 2) * 128u, st0, wave);
+        MOE_DMA_ISSUE(BJ, NW, Be, db, (uint32_t)(kt + 2) * 128u, st0 + ACH, wave);
+      }
+      mma_step_bf16<MB, NB, WM, WN, ACH>(st1, acc, wm, wn, lane);
+      dma_wait_and_barrier();
+    }
+    if (KT & 1) {  // odd step count: the last step sits in the first stage
+      mma_step_bf16<MB, NB, WM, WN, ACH>(st0, acc, wm, wn, lane);
+      dma_wait_and_barrier();
+    }
+    // epilogue (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4)
+    if (GLU) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int q = 0; q < NB / 2; ++q) {
+          const int col = ti.nt * (BN / 2) + (wn * (NB / 2) + q) * 32 + lrow;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+            if (r < ti.mvalid) {
+              const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
+              reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(h);
+            }
+          }
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = ti.nt * BN + wn * WN + nb * 32 + lrow;
+          if (col < g.N_out) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+              if (r < ti.mvalid) {
+                uint8_t* p = g.C + (size_t)(ti.row0 + r) * g.ldc;
+                if (OUTF32)
+                  reinterpret_cast<float*>(p)[col] = acc[mb][nb][i];
+                else
+                  reinterpret_cast<uint16_t*>(p)[col] = f32_to_bf16(acc[mb][nb][i]);
+              }
+            }
+          }
+        }
+    }
+  }
+}
+
+template <class K>
+static hipError_t launch_one(const char* name, K kernel, int grid, int threads, const GemmArgs& g,
+                             hipStream_t s) {
+  return timed_launch(name, s, [&] { hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, g); });
+}
+
+static int round8(int v) { return ((v + 7) / 8) * 8; }
+
+// variant 0: 256 x 256 tiles, 8 waves, one workgroup per CU (experts with many rows);
+// variant 1: 32 x 256 tiles, 4 waves, two workgroups per CU (decode-sized row groups).
+hipError_t launch_gemm_bf16(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s) {
+  hipError_t e;
+  if (variant == 0) {
+    const int grid = round8(cus);
+    if ((e = launch_one("gemm_bf16_gateup_swiglu", k_gemm_bf16<256, 256, 2, 4, true, 1, false>, grid, 512,
+                        g1, s)) != hipSuccess)
+      return e;
+    return launch_one("gemm_bf16_down", k_gemm_bf16<256, 256, 2, 4, false, 1, true>, grid, 512, g2, s);
+  }
+  const int grid = round8(cus * 2);
+  if ((e = launch_one("gemm_bf16_gateup_swiglu_m32", k_gemm_bf16<32, 256, 1, 4, true, 2, false>, grid, 256,
+                      g1, s)) != hipSuccess)
+    return e;
+  return launch_one("gemm_bf16_down_m32", k_gemm_bf16<32, 256, 1, 4, false, 2, true>, grid, 256, g2, s);
+}
+
+}  // namespace moe

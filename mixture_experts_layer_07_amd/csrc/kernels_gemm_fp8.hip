@@ -1,0 +1,234 @@
+// fp8 (e4m3) grouped GEMMs of the SwiGLU experts on MFMA 32x32x64 with block-scale promotion.
+//
+// Activations carry one fp32 scale per row per 128 channels, weights one per 128 x 128 block
+// (fp8 scaling: scale into the e4m3 range, compute, scale back; "企业官网建设流程全解析", 3.2 and
+// 4.4, whose body reposts DeepGEMM material). One K step is 128 channels, i.e. one scale block:
+// per 32 x 32 block two MFMAs give the partial sum over those channels, promoted into the fp32
+// accumulator as acc += partial * (row scale * weight block scale).
+// Linear-1 output: h = SiLU(g) * u re-quantised per row per 128 columns ("SwiGLU / FP8 Cast",
+// "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", 5.1): the tile holds exactly
+// one such block (128 h columns), scale = absmax / 448, code = e4m3(h / scale).
+// Pipeline as in the bf16 kernels: direct-to-LDS loads (tiles and the row scales) into two
+// LDS stages, one barrier per K step.
+#include "gemm_common.h"
+
+namespace moe {
+
+__device__ __forceinline__ i32x8 frag32(const u32x4* row, int c0, int c1) {
+  const u32x4 x = row[c0], y = row[c1];
+  return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+}
+
+template <int MB, int NB, int WM, int WN, int ACH>
+__device__ __forceinline__ void mma_step_fp8(const u32x4* st, const float* lsa, const float (&sb)[NB],
+                                             f32x16 (&acc)[MB][NB], int wm, int wn, int lane) {
+  const int lrow = lane & 31, lk = lane >> 5, lsw = lane & 7;
+  const u32x4* la = st + (wm * WM + lrow) * 8;
+  const u32x4* lb = st + ACH + (wn * WN + lrow) * 8;
+  i32x8 b0[NB], b1[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    b0[nb] = frag32(lb + nb * 256, (2 * lk) ^ lsw, (2 * lk + 1) ^ lsw);
+    b1[nb] = frag32(lb + nb * 256, (4 + 2 * lk) ^ lsw, (5 + 2 * lk) ^ lsw);
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const i32x8 a0 = frag32(la + mb * 256, (2 * lk) ^ lsw, (2 * lk + 1) ^ lsw);
+    const i32x8 a1 = frag32(la + mb * 256, (4 + 2 * lk) ^ lsw, (5 + 2 * lk) ^ lsw);
+    float sa[16];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const float4 v = *reinterpret_cast<const float4*>(lsa + wm * WM + mb * 32 + g4 * 8 + lk * 4);
+      sa[g4 * 4 + 0] = v.x;
+      sa[g4 * 4 + 1] = v.y;
+      sa[g4 * 4 + 2] = v.z;
+      sa[g4 * 4 + 3] = v.w;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x16 p;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i] = 0.f;
+      p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0[nb], p, 0, 0, 0, 127, 0, 127);
+      p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1[nb], p, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = fmaf(p[i], sa[i] * sb[nb], acc[mb][nb][i]);
+    }
+  }
+}
+
+template <int BM, int BN, int NWM, int NWN, bool GLU, int MINB>
+__global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
+  constexpr int NT = NWM * NWN * 64, NW = NWM * NWN;
+  constexpr int WM = BM / NWM, WN = BN / NWN, MB = WM / 32, NB = WN / 32;
+  constexpr int ACH = BM * 8, BCH = BN * 8;
+  constexpr int AJ = ACH / NT, BJ = BCH / NT;
+  constexpr int SAW = (BM + 63) / 64;                 // waves that load the row scales
+  constexpr int SAN = SAW * 64;
+  static_assert(ACH % NT == 0 && BCH % NT == 0, "tile / thread mismatch");
+  static_assert(!GLU || (NB % 2 == 0 && BN == 256), "GLU needs gate/up pairs and 128 h columns");
+  static_assert(SAW <= NW, "not enough waves for the row scales");
+  __shared__ u32x4 st0[ACH + BCH];
+  __shared__ u32x4 st1[ACH + BCH];
+  __shared__ __attribute__((aligned(16))) float sa0[SAN];
+  __shared__ __attribute__((aligned(16))) float sa1[SAN];
+  __shared__ int tp[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  for (int i = tid; i <= g.n_exp; i += NT) tp[i] = g.tp[i];
+  __syncthreads();
+  const int total = tp[g.n_exp] * g.n_tiles_n;
+  const int KT = g.K / 128;
+  const int lrow = lane & 31, lk = lane >> 5;
+  const uint32_t cb = (uint32_t)dma_chunk(lane) * 16;
+
+  for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+    const TileInfo ti = decode_tile(t, tp, g, BM);
+    const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
+    const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
+    TileDma<AJ> da;
+    TileDma<BJ> db;
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) {
+      const int r = dma_row<NW>(j, wave, lane);
+      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      da.off[j] = (uint32_t)rr * (uint32_t)g.lda + cb;
+    }
+#pragma unroll
+    for (int j = 0; j < BJ; ++j)
+      db.off[j] = (uint32_t)weight_row<GLU, BN>(dma_row<NW>(j, wave, lane), ti.nt, g) * (uint32_t)g.ldb + cb;
+    // row scales: wave w < SAW loads rows 64w + lane (clamped) for the K step
+    const uint8_t* sab = reinterpret_cast<const uint8_t*>(g.a_scale + (size_t)ti.row0 * g.a_scale_ld);
+    uint32_t soff = 0;
+    {
+      const int r = wave * 64 + lane;
+      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      soff = (uint32_t)rr * (uint32_t)g.a_scale_ld * 4u;
+    }
+    const float* psb[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int wr = weight_row<GLU, BN>(wn * WN + nb * 32, ti.nt, g);
+      psb[nb] = g.b_scale + (size_t)ti.e * g.b_scale_exp + (size_t)(wr >> 7) * g.b_scale_ld;
+    }
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+#define MOE_FP8_ISSUE(kt, st, sa)                                                                   \
+  do {                                                                                              \
+    MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt) * 128u, st, wave);                                 \
+    MOE_DMA_ISSUE(BJ, NW, Be, db, (uint32_t)(kt) * 128u, (st) + ACH, wave);                         \
+    if (wave < SAW)                                                                                 \
+      dma_to_lds<4>(sab + (soff + (uint32_t)(kt) * 4u), (sa) + wave * 64);                            \
+  } while (0)
+    MOE_FP8_ISSUE(0, st0, sa0);
+    dma_wait_and_barrier();
+    for (int kt = 0; kt < KT; kt += 2) {
+      if (kt + 1 < KT) MOE_FP8_ISSUE(kt + 1, st1, sa1);
+      {
+        float sb[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sb[nb] = psb[nb][kt];
+        mma_step_fp8<MB, NB, WM, WN, ACH>(st0, sa0, sb, acc, wm, wn, lane);
+      }
+      dma_wait_and_barrier();
+      if (kt + 1 >= KT) break;
+      if (kt + 2 < KT) MOE_FP8_ISSUE(kt + 2, st0, sa0);
+      {
+        float sb[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sb[nb] = psb[nb][kt + 1];
+        mma_step_fp8<MB, NB, WM, WN, ACH>(st1, sa1, sb, acc, wm, wn, lane);
+      }
+      dma_wait_and_barrier();
+    }
+    if (GLU) {
+      // per-row absmax over the tile's 128 h columns: lanes (32 columns) -> waves (through LDS)
+      float* red = reinterpret_cast<float*>(st0);  // [BM][NWN]; every wave is past the last read
+      float hv[MB][NB / 2][16];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float m = 0.f;
+#pragma unroll
+          for (int q = 0; q < NB / 2; ++q) {
+            hv[mb][q][i] = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
+            m = fmaxf(m, fabsf(hv[mb][q][i]));
+          }
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+          if (lrow == 0) red[r * NWN + wn] = m;
+        }
+      __syncthreads();
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+          float m = 0.f;
+#pragma unroll
+          for (int w = 0; w < NWN; ++w) m = fmaxf(m, red[r * NWN + w]);
+          const float scale = m / 448.0f;
+          if (r < ti.mvalid) {
+            uint8_t* crow = g.C + (size_t)(ti.row0 + r) * g.ldc;
+#pragma unroll
+            for (int q = 0; q < NB / 2; ++q) {
+              const int col = ti.nt * 128 + (wn * (NB / 2) + q) * 32 + lrow;
+              crow[col] = m > 0.f ? (uint8_t)f32_to_e4m3(hv[mb][q][i] / scale) : (uint8_t)0;
+            }
+            if (wn == 0 && lrow == 0) g.c_scale[(size_t)(ti.row0 + r) * g.c_scale_ld + ti.nt] = scale;
+          }
+        }
+      __syncthreads();  // red[] aliases the first stage of the next tile
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = ti.nt * BN + wn * WN + nb * 32 + lrow;
+          if (col < g.N_out) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+              if (r < ti.mvalid)
+                reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(acc[mb][nb][i]);
+            }
+          }
+        }
+    }
+  }
+}
+
+template <class K>
+static hipError_t launch_one(const char* name, K kernel, int grid, int threads, const GemmArgs& g,
+                             hipStream_t s) {
+  return timed_launch(name, s, [&] { hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, g); });
+}
+
+static int round8(int v) { return ((v + 7) / 8) * 8; }
+
+// variant 0: 128 x 256 tiles, 8 waves, one workgroup per CU; variant 1: 32 x 256, 4 waves, two per CU.
+hipError_t launch_gemm_fp8(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s) {
+  hipError_t e;
+  if (variant == 0) {
+    const int grid = round8(cus);
+    if ((e = launch_one("gemm_fp8_gateup_swiglu", k_gemm_fp8<128, 256, 2, 4, true, 1>, grid, 512, g1, s)) !=
+        hipSuccess)
+      return e;
+    return launch_one("gemm_fp8_down", k_gemm_fp8<128, 256, 2, 4, false, 1>, grid, 512, g2, s);
+  }
+  const int grid = round8(cus * 2);
+  if ((e = launch_one("gemm_fp8_gateup_swiglu_m32", k_gemm_fp8<32, 256, 1, 4, true, 2>, grid, 256, g1, s)) !=
+      hipSuccess)
+    return e;
+  return launch_one("gemm_fp8_down_m32", k_gemm_fp8<32, 256, 1, 4, false, 2>, grid, 256, g2, s);
+}
+
+}  // namespace moe
