@@ -143,7 +143,8 @@ def cpu_baseline(cfg, x, w_r, bias, ex, sh, layer, ntok):
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
     if ntok <= 0:
-        ntok = min(cfg.T, 64 if cfg.H * cfg.I <= 2 ** 20 else 32)
+        # about 10-30 s of host work on a 16-core box for the large layers
+        ntok = min(cfg.T, 64 if cfg.H * cfg.I <= 2 ** 20 else 1024)
     toks = np.arange(ntok) * (cfg.T // ntok)
     ids = layer.topk_ids.cpu().numpy()
     used = sorted(set(ids[toks].reshape(-1).tolist()))

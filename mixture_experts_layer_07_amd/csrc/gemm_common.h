@@ -28,8 +28,43 @@ struct GemmArgs {
   int c_scale_ld;
   const int32_t* offsets;
   const int32_t* tp;
+  int32_t* queue;       // kQueues tile counters (zeroed by the tile builder)
   int n_exp, K, N_out, Nb, glu_I, n_tiles_n;
 };
+
+// Tile scheduling: the tile list is cut into kQueues contiguous ranges, one per XCD (workgroups
+// are dispatched round-robin over the 8 XCDs, so workgroup b works on range b % 8); inside a
+// range the workgroups of that XCD pull tiles in order from an integer counter. Neighbouring
+// tiles (the m-tiles of one weight block) thus run at the same time on one XCD and share its L2,
+// and a cheap tile (a ragged last m-tile) frees its workgroup early instead of stalling a fixed
+// round. Every tile is computed by one workgroup from start to end, so results do not depend on
+// the order.
+constexpr int kQueues = 8;
+// Position of the queue counters in the tile-metadata region (after tp[0 .. kMaxExperts]).
+constexpr int kTileQueueOffset = kMaxExperts + 1;
+static_assert(kTileQueueOffset + 2 * kQueues <= 2 * 257, "tile metadata region too small");
+
+struct TileQueue {
+  int beg, end;
+};
+
+__device__ __forceinline__ TileQueue tile_queue(int total) {
+  const int q = blockIdx.x % kQueues;
+  const int per = (total + kQueues - 1) / kQueues;
+  TileQueue r;
+  r.beg = q * per < total ? q * per : total;
+  r.end = r.beg + per < total ? r.beg + per : total;
+  return r;
+}
+
+// Next tile of this workgroup's range, or -1. All threads must call (two barriers).
+__device__ __forceinline__ int next_tile(const GemmArgs& g, const TileQueue& tq, int* s_slot) {
+  if (threadIdx.x == 0) s_slot[0] = tq.beg + atomicAdd(&g.queue[blockIdx.x % kQueues], 1);
+  __syncthreads();
+  const int t = s_slot[0];
+  __syncthreads();
+  return t < tq.end ? t : -1;
+}
 
 struct TileInfo {
   int e, mt, nt, row0, mvalid;
@@ -77,9 +112,12 @@ __device__ __forceinline__ int weight_row(int r, int nt, const GemmArgs& g) {
 __device__ __forceinline__ float silu_fast(float x) { return x / (1.0f + __expf(-x)); }
 
 // LDS tile layout: rows of 128 bytes = 8 chunks of 16 bytes; chunk c of row r is stored at
-// position c ^ (r & 7) so that the 16-byte MFMA operand reads of 8 consecutive rows hit 8
-// different bank groups.
-__device__ __forceinline__ int lds_swz(int row) { return row & 7; }
+// position c ^ ((r >> 1) & 7). The LDS has 64 four-byte banks (256 bytes), so a 128-byte row
+// covers half of them and rows r, r+1 fill the two halves; an MFMA operand read has 16
+// consecutive lanes reading the same logical chunk of 16 consecutive rows, and this swizzle
+// gives those 16 reads 16 different 16-byte bank groups (a plain c ^ (r & 7) pairs rows r and
+// r + 8 on one group: every read a 2-way conflict, as the LDS counters showed).
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
 
 // Direct-to-LDS tile loads (global_load_lds_dwordx4): one instruction moves 64 x 16 bytes from
 // per-lane global addresses to 1 KB of LDS at a wave-uniform base, lane i writing 16*i.
@@ -94,7 +132,9 @@ struct TileDma {
 template <int NW>
 __device__ __forceinline__ int dma_row(int j, int wave, int lane) { return (j * NW + wave) * 8 + (lane >> 3); }
 
-__device__ __forceinline__ int dma_chunk(int lane) { return (lane & 7) ^ lds_swz(lane >> 3); }
+// Logical chunk that lane `lane` fetches so that the swizzle lands it in its LDS slot (lane & 7)
+// of tile row `row`.
+__device__ __forceinline__ int dma_chunk(int row, int lane) { return (lane & 7) ^ lds_swz(row); }
 
 // A macro, so that the builtin sees the __shared__ stage itself (its LDS address space is lost
 // through a function parameter).

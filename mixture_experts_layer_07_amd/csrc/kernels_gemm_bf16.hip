@@ -15,7 +15,7 @@ namespace moe {
 template <int MB, int NB, int WM, int WN, int ACH>
 __device__ __forceinline__ void mma_step_bf16(const u32x4* st, f32x16 (&acc)[MB][NB], int wm, int wn,
                                               int lane) {
-  const int lrow = lane & 31, lk = lane >> 5, lsw = lane & 7;
+  const int lrow = lane & 31, lk = lane >> 5, lsw = lds_swz(lrow);  // tile rows start at multiples of 32
   const u32x4* la = st + (wm * WM + lrow) * 8;
   const u32x4* lb = st + ACH + (wn * WN + lrow) * 8;
   bf16x8 a[2][MB], b[2][NB];
@@ -60,10 +60,12 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) 
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 64;
   const int lrow = lane & 31, lk = lane >> 5;
-  const uint32_t cb = (uint32_t)dma_chunk(lane) * 16;
+  __shared__ int s_slot[1];
+  const TileQueue tq = tile_queue(total);
 
-  for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
     const TileInfo ti = decode_tile(t, tp, g, BM);
+    const bool rows_here = wm * WM < ti.mvalid;  // waves past the expert's last row skip the MFMAs
     const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
     TileDma<AJ> da;
@@ -72,11 +74,13 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) 
     for (int j = 0; j < AJ; ++j) {
       const int r = dma_row<NW>(j, wave, lane);
       const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
-      da.off[j] = (uint32_t)rr * (uint32_t)g.lda + cb;
+      da.off[j] = (uint32_t)rr * (uint32_t)g.lda + (uint32_t)dma_chunk(r, lane) * 16u;
     }
 #pragma unroll
-    for (int j = 0; j < BJ; ++j)
-      db.off[j] = (uint32_t)weight_row<GLU, BN>(dma_row<NW>(j, wave, lane), ti.nt, g) * (uint32_t)g.ldb + cb;
+    for (int j = 0; j < BJ; ++j) {
+      const int r = dma_row<NW>(j, wave, lane);
+      db.off[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + (uint32_t)dma_chunk(r, lane) * 16u;
+    }
     f32x16 acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -91,17 +95,17 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) 
     for (int kt = 0; kt + 1 < KT; kt += 2) {
       MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt + 1) * 128u, st1, wave);
       MOE_DMA_ISSUE(BJ, NW, Be, db, (uint32_t)(kt + 1) * 128u, st1 + ACH, wave);
-      mma_step_bf16<MB, NB, WM, WN, ACH>(st0, acc, wm, wn, lane);
+      if (rows_here) mma_step_bf16<MB, NB, WM, WN, ACH>(st0, acc, wm, wn, lane);
       dma_wait_and_barrier();
       if (kt + 2 < KT) {
         MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt + 2) * 128u, st0, wave);
         MOE_DMA_ISSUE(BJ, NW, Be, db, (uint32_t)(kt + 2) * 128u, st0 + ACH, wave);
       }
-      mma_step_bf16<MB, NB, WM, WN, ACH>(st1, acc, wm, wn, lane);
+      if (rows_here) mma_step_bf16<MB, NB, WM, WN, ACH>(st1, acc, wm, wn, lane);
       dma_wait_and_barrier();
     }
     if (KT & 1) {  // odd step count: the last step sits in the first stage
-      mma_step_bf16<MB, NB, WM, WN, ACH>(st0, acc, wm, wn, lane);
+      if (rows_here) mma_step_bf16<MB, NB, WM, WN, ACH>(st0, acc, wm, wn, lane);
       dma_wait_and_barrier();
     }
     // epilogue (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4)

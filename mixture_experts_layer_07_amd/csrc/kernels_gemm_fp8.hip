@@ -22,7 +22,7 @@ __device__ __forceinline__ i32x8 frag32(const u32x4* row, int c0, int c1) {
 template <int MB, int NB, int WM, int WN, int ACH>
 __device__ __forceinline__ void mma_step_fp8(const u32x4* st, const float* lsa, const float (&sb)[NB],
                                              f32x16 (&acc)[MB][NB], int wm, int wn, int lane) {
-  const int lrow = lane & 31, lk = lane >> 5, lsw = lane & 7;
+  const int lrow = lane & 31, lk = lane >> 5, lsw = lds_swz(lrow);  // tile rows start at multiples of 32
   const u32x4* la = st + (wm * WM + lrow) * 8;
   const u32x4* lb = st + ACH + (wn * WN + lrow) * 8;
   i32x8 b0[NB], b1[NB];
@@ -80,10 +80,12 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 128;
   const int lrow = lane & 31, lk = lane >> 5;
-  const uint32_t cb = (uint32_t)dma_chunk(lane) * 16;
+  __shared__ int s_slot[1];
+  const TileQueue tq = tile_queue(total);
 
-  for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
     const TileInfo ti = decode_tile(t, tp, g, BM);
+    const bool rows_here = wm * WM < ti.mvalid;  // waves past the expert's last row skip the MFMAs
     const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
     TileDma<AJ> da;
@@ -92,11 +94,13 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
     for (int j = 0; j < AJ; ++j) {
       const int r = dma_row<NW>(j, wave, lane);
       const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
-      da.off[j] = (uint32_t)rr * (uint32_t)g.lda + cb;
+      da.off[j] = (uint32_t)rr * (uint32_t)g.lda + (uint32_t)dma_chunk(r, lane) * 16u;
     }
 #pragma unroll
-    for (int j = 0; j < BJ; ++j)
-      db.off[j] = (uint32_t)weight_row<GLU, BN>(dma_row<NW>(j, wave, lane), ti.nt, g) * (uint32_t)g.ldb + cb;
+    for (int j = 0; j < BJ; ++j) {
+      const int r = dma_row<NW>(j, wave, lane);
+      db.off[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + (uint32_t)dma_chunk(r, lane) * 16u;
+    }
     // row scales: wave w < SAW loads rows 64w + lane (clamped) for the K step
     const uint8_t* sab = reinterpret_cast<const uint8_t*>(g.a_scale + (size_t)ti.row0 * g.a_scale_ld);
     uint32_t soff = 0;
@@ -128,23 +132,29 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
   } while (0)
     MOE_FP8_ISSUE(0, st0, sa0);
     dma_wait_and_barrier();
-    for (int kt = 0; kt < KT; kt += 2) {
-      if (kt + 1 < KT) MOE_FP8_ISSUE(kt + 1, st1, sa1);
+    for (int kt = 0; kt + 1 < KT; kt += 2) {
+      MOE_FP8_ISSUE(kt + 1, st1, sa1);
       {
         float sb[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sb[nb] = psb[nb][kt];
-        mma_step_fp8<MB, NB, WM, WN, ACH>(st0, sa0, sb, acc, wm, wn, lane);
+        if (rows_here) mma_step_fp8<MB, NB, WM, WN, ACH>(st0, sa0, sb, acc, wm, wn, lane);
       }
       dma_wait_and_barrier();
-      if (kt + 1 >= KT) break;
       if (kt + 2 < KT) MOE_FP8_ISSUE(kt + 2, st0, sa0);
       {
         float sb[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sb[nb] = psb[nb][kt + 1];
-        mma_step_fp8<MB, NB, WM, WN, ACH>(st1, sa1, sb, acc, wm, wn, lane);
+        if (rows_here) mma_step_fp8<MB, NB, WM, WN, ACH>(st1, sa1, sb, acc, wm, wn, lane);
       }
+      dma_wait_and_barrier();
+    }
+    if (KT & 1) {  // odd step count: the last step sits in the first stage
+      float sb[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sb[nb] = psb[nb][KT - 1];
+      if (rows_here) mma_step_fp8<MB, NB, WM, WN, ACH>(st0, sa0, sb, acc, wm, wn, lane);
       dma_wait_and_barrier();
     }
     if (GLU) {
