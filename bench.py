@@ -28,18 +28,64 @@ def parse():
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = auto)")
+    p.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                   help="after the measurement, run one plain copy-like pass over this many GiB "
+                        "(reference point for the HBM byte counters)")
     return p.parse_args()
 
 
-def kernel_work(cfg, name):
-    """Algorithmic FLOPs and bytes of one launch of the named kernel (routed launches)."""
-    T, H, I, E, K, P = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.P
-    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.dtype]
-    if "gateup" in name:
-        return 4.0 * P * H * I, None
-    if "down" in name:
-        return 2.0 * P * H * I, None
-    return None, None
+def kernel_work(cfg, active):
+    """Algorithmic work of one step, per kernel name: {name: (flops, bytes)}.
+
+    Bytes count each operand once at its stored width (inputs read once, outputs written once);
+    `active` = experts that received at least one pair (only their weights are read).
+    Keys are "stage/kernel" with the kernel's tile-variant suffix removed.
+    """
+    T, H, I, E, K, P, Is = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.P, cfg.I_shared
+    fp8 = cfg.dtype == "fp8"
+    xb = 4 if cfg.dtype == "f32" else 2          # x and out
+    ab = 1 if fp8 else xb                        # GEMM operand bytes (x_perm, weights, h)
+    yb = 2 if fp8 else 4                         # y rows: fp32 (f32/bf16 layers), bf16 (fp8 layers)
+    sc = 4.0 / 128 if fp8 else 0.0               # activation-scale bytes per element
+    wsc = 4.0 / (128 * 128) if fp8 else 0.0      # weight-scale bytes per element
+    w = {}
+
+    def add(name, fl, by):
+        f0, b0 = w.get(name, (0.0, 0.0))
+        w[name] = (f0 + fl, b0 + by)
+
+    kind = {"f32": "gemm_f32", "bf16": "gemm_bf16", "fp8": "gemm_fp8"}[cfg.dtype]
+
+    def ffn(st, rows, nexp, inter):
+        add(st + kind + "_gateup_swiglu", 4.0 * rows * H * inter,
+            rows * H * (ab + sc) + nexp * 2 * inter * H * (ab + wsc) + rows * inter * (ab + sc))
+        add(st + kind + "_down", 2.0 * rows * H * inter,
+            rows * inter * (ab + sc) + nexp * H * inter * (ab + wsc) + rows * H * yb)
+
+    rb = 4 if cfg.dtype == "f32" else 2
+    add("route/router_f32" if cfg.dtype == "f32" else "route/router_bf16", 2.0 * T * H * E,
+        T * H * rb + H * E * rb + T * E * 4)
+    add("route/router_transpose", 0.0, 2.0 * H * E * 2)
+    add("route/topk", 0.0, T * E * 4 + T * K * 8 + (E * 4 if cfg.bias else 0))
+    add("permute/perm_hist", 0.0, P * 4 + E * 4)
+    add("permute/perm_scan", 0.0, E * 8)
+    add("permute/perm_scatter", 0.0, P * 4 + P * 8)
+    add("permute/gather_quant_fp8" if fp8 else "permute/gather", 0.0, P * 4 + P * H * xb + P * H * (ab + sc))
+    add("ffn/build_tiles", 0.0, E * 8)
+    ffn("ffn/", P, active, I)
+    if Is:
+        if fp8:
+            add("shared/quantize_fp8", 0.0, T * H * 2 + T * H * (1 + sc))
+        add("shared/build_tiles", 0.0, 8)
+        ffn("shared/", T, 1, Is)
+    cname = {"f32": "combine_f32", "bf16": "combine_f32_to_bf16", "fp8": "combine_bf16"}[cfg.dtype]
+    add("combine/" + cname, 0.0, P * 4 + T * K * 4 + P * H * yb + (T * H * yb if Is else 0) + T * H * xb)
+    return w
+
+
+def variant_free(name):
+    """Kernel name without its tile-variant suffix (the work model does not depend on it)."""
+    return name[:-4] if name.endswith("_m32") else name
 
 
 def main():
@@ -67,6 +113,7 @@ def main():
     xd = x.to(dev)
     stream = torch.cuda.current_stream()
 
+    print(f"bench: {cfg.name} inputs resident; warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         layer(xd)
     torch.cuda.synchronize()
@@ -81,35 +128,59 @@ def main():
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / args.steps
 
-    # per-kernel durations: HIP events recorded by the library on the launch stream
-    B.profile_reset()
+    # per-kernel durations: HIP events recorded by the library around each launch on the launch
+    # stream, read stage by stage so that routed and shared-expert launches are told apart
+    stages = [("route", lambda: layer.route(xd)), ("permute", lambda: layer.permute(xd)),
+              ("ffn", layer.expert_ffn), ("shared", lambda: layer.shared_ffn(xd)),
+              ("combine", layer.combine)]
     B.profile_enable(True)
+    prof = {}
     for _ in range(args.steps):
-        layer(xd)
-    torch.cuda.synchronize()
-    prof = B.profile_read()
+        for st, fn in stages:
+            B.profile_reset()
+            fn()
+            torch.cuda.synchronize()
+            for k, (t, n) in B.profile_read().items():
+                t0_, n0_ = prof.get(f"{st}/{k}", (0.0, 0))
+                prof[f"{st}/{k}"] = (t0_ + t, n0_ + n)
     B.profile_enable(False)
     B.profile_reset()
-    kernels = {k: {"avg_ms": v[0] / v[1], "launches_per_step": v[1] / args.steps} for k, v in prof.items()}
 
     flops = active_flops(cfg)
     tflops = flops / (ms * 1e-3) / 1e12
     tokens_s = cfg.T / (ms * 1e-3)
     dtype = cfg.dtype
-    # dominant kernel: largest total time
+    active = int((layer.counts > 0).sum().item())
+    work = kernel_work(cfg, active)
+    kernels = {}
+    for k, (tot_ms, n) in prof.items():
+        fl, by = work.get(variant_free(k), (0.0, 0.0))
+        step_ms = tot_ms / args.steps
+        d = {"avg_ms": round(tot_ms / n, 4), "launches_per_step": n / args.steps}
+        if fl:
+            d["tflop_s"] = round(fl / (step_ms * 1e-3) / 1e12, 2)
+        if by:
+            d["gb_s"] = round(by / (step_ms * 1e-3) / 1e9, 1)
+        kernels[k] = d
+    # dominant kernel: largest total time; its bound follows from its arithmetic intensity
     dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
-    fl, _ = kernel_work(cfg, dom)
-    avg = prof[dom][0] / prof[dom][1]
-    if cfg.I_shared and fl is not None:
-        # shared-expert launches use the same kernel; price routed + shared work over all launches
-        per_step = fl + (fl / cfg.P / cfg.I * cfg.T * cfg.I_shared)
-        fl = per_step / (prof[dom][1] / args.steps)
-    roof = {"kernel": dom, "bound": "mfma", "achieved": fl / (avg * 1e-3) / 1e12 if fl else None,
-            "peak": PEAK[dtype], "unit": "TFLOP/s", "traffic": None}
-    roof["frac"] = roof["achieved"] / roof["peak"] if roof["achieved"] else None
+    fl, by = work.get(variant_free(dom), (0.0, 0.0))
+    n_launch = prof[dom][1] / args.steps
+    avg_s = prof[dom][0] / prof[dom][1] * 1e-3
+    mfma = fl > 0 and fl / by >= PEAK[dtype] / HBM_PEAK
+    if mfma:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": fl / n_launch / avg_s / 1e12,
+                "peak": PEAK[dtype], "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": by / n_launch / avg_s / 1e9,
+                "peak": HBM_PEAK, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(cfg.name, dom)
+    roof["algorithmic_per_launch"] = {"flops": fl / n_launch, "bytes": by / n_launch}
 
     cpu = None
     if not args.no_cpu_baseline:
+        print("bench: oracle sample on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(cfg, x, w_r, bias, ex, sh, layer, args.cpu_tokens)
 
     rec = {
@@ -122,13 +193,64 @@ def main():
                    "parallelism": "single-gpu"},
         "tokens_per_s": round(tokens_s, 1),
         "mfma_peak_frac": round(tflops / PEAK[dtype], 4),
+        "active_experts": active,
         "wall_s_timed": round(wall, 3),
-        "kernels": {k: {"avg_ms": round(v["avg_ms"], 4), "launches_per_step": v["launches_per_step"]}
-                    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["avg_ms"])},
+        "kernels": dict(sorted(kernels.items(), key=lambda kv: -kv[1]["avg_ms"] * kv[1]["launches_per_step"])),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec))
+    if args.copy_calibration_gib > 0:
+        copy_calibration(args.copy_calibration_gib, dev)
+    print(json.dumps(rec), flush=True)
+
+
+# Sources whose change invalidates a stored traffic measurement of a kernel.
+KERNEL_SOURCES = {
+    "gemm_bf16": ["kernels_gemm_bf16.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
+    "gemm_fp8": ["kernels_gemm_fp8.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
+    "gemm_f32": ["kernels_ffn.hip", "gemm_common.h", "device.h", "internal.h"],
+}
+
+
+def sources_digest(kernel):
+    import hashlib
+    base = kernel.split("/")[-1]
+    files = next((v for k, v in KERNEL_SOURCES.items() if base.startswith(k)), None)
+    if files is None:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mixture_experts_layer_07_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the stored FETCH_SIZE / WRITE_SIZE counter runs (scaled by the
+    same counters' reading on a copy of known size), or None when none is stored or the kernel's
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_digest(kernel):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def copy_calibration(gib, dev):
+    """A plain elementwise pass (negation) over `gib` GiB of fp32: reads and writes exactly that
+    many bytes once, so the HBM counters' reading on it gives their scale."""
+    import torch
+    n = int(gib * 2 ** 30) // 4
+    a = torch.ones(n, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def cpu_baseline(cfg, x, w_r, bias, ex, sh, layer, ntok):
