@@ -167,7 +167,7 @@ def main():
     fl, by = work.get(variant_free(dom), (0.0, 0.0))
     n_launch = prof[dom][1] / args.steps
     avg_s = prof[dom][0] / prof[dom][1] * 1e-3
-    mfma = fl > 0 and fl / by >= PEAK[dtype] / HBM_PEAK
+    mfma = fl > 0 and fl / by >= PEAK[dtype] * 1e12 / (HBM_PEAK * 1e9)  # FLOP per byte at the ridge
     if mfma:
         roof = {"kernel": dom, "bound": "mfma", "achieved": fl / n_launch / avg_s / 1e12,
                 "peak": PEAK[dtype], "unit": "TFLOP/s"}

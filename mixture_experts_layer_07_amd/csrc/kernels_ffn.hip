@@ -210,15 +210,16 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
     g2.b_scale_exp = (size_t)(H / 128) * (I / 128);
   }
   // Tile shape from the mean rows per expert (a host-side choice; the API has no knob): large M
-  // tiles when experts are well filled (weights then stream once per n-tile), 32-row tiles for
-  // decode-sized row groups.
+  // tiles when experts are well filled (weights then stream once per n-tile) and the large tiles
+  // still cover every CU, 32-row tiles for decode-sized row groups.
   const int avg = a.n_rows / a.n_exp;
+  auto enough = [&](int bm) { return (long)((a.n_rows + bm - 1) / bm) * g1.n_tiles_n >= cus; };
   if (!fp8) {
-    const int variant = avg >= 128 ? 0 : 1;
+    const int variant = avg >= 128 && enough(256) ? 0 : 1;
     if ((e = build_tiles(a, variant == 0 ? 256 : 32, a.tiles, s)) != hipSuccess) return e;
     return launch_gemm_bf16(g1, g2, variant, cus, s);
   }
-  const int variant = avg >= 64 ? 0 : 1;
+  const int variant = avg >= 64 && enough(128) ? 0 : 1;
   if ((e = build_tiles(a, variant == 0 ? 128 : 32, a.tiles, s)) != hipSuccess) return e;
   return launch_gemm_fp8(g1, g2, variant, cus, s);
 }

@@ -148,6 +148,199 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) 
   }
 }
 
+
+// ============================================================================ 256 x 256 tiles
+// Four waves (2 x 2), each owning a 128 x 128 block of the tile: 16 accumulators of 32 x 32 in
+// the accumulation registers, one wave per SIMD. K advances 64 channels per step through two
+// LDS stages (A 256 rows + B 256 rows of 128 bytes = full cache lines, plus a 1 KiB sink),
+// filled by direct-to-LDS loads. Within step k:
+//   sub-steps 0..2: MFMAs of sub-step s while the fragments of s+1 are read;
+//   then: this wave's reads of the stage are complete and its loads of step k+1 have landed;
+//         a workgroup barrier (no memory fence: the waits are explicit) extends both to all waves;
+//   sub-step 3: MFMAs while the first fragments of step k+1 are read and the loads of step k+2
+//         go into the stage just released.
+// Rows of A past the tile's valid rows are not fetched: their loads read one cached line and land
+// in the sink, and their LDS rows are zeroed once per tile (a zero operand also draws less power
+// in the MFMA pipes). Their accumulators are never stored.
+namespace w4 {
+constexpr int kStage = 4096 + 64;  // u32x4 per stage: A 2048 + B 2048 + 64 (sink)
+constexpr int kSink = 4096;
+
+template <int MB, int NB>
+__device__ __forceinline__ void frags(const u32x4* st, int ks, int wm, int wn, int lane, bf16x8 (&a)[MB],
+                                      bf16x8 (&b)[NB]) {
+  const int lrow = lane & 31, lk = lane >> 5;
+  const int slot = (ks * 2 + lk) ^ lds_swz(lrow);  // block rows start at multiples of 32
+  const u32x4* la = st + (wm * 128 + lrow) * 8 + slot;
+  const u32x4* lb = st + 2048 + (wn * 128 + lrow) * 8 + slot;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) a[mb] = __builtin_bit_cast(bf16x8, la[mb * 256]);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) b[nb] = __builtin_bit_cast(bf16x8, lb[nb * 256]);
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void mfmas(f32x16 (&acc)[MB][NB], const bf16x8 (&a)[MB], const bf16x8 (&b)[NB]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+}
+}  // namespace w4
+
+// Scheduling groups: 0x008 MFMA, 0x010 vector memory, 0x100 LDS read.
+#define MOE_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
+// The 16 direct-to-LDS loads of one step (8 of A, 8 of B) into `stage`.
+#define MOE_W4_LOADS(stage, kk)                                                                  \
+  do {                                                                                           \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_)                                             \
+        dma_to_lds<16>(Ab + (oa[j_] + (uint32_t)(kk) * 128u), (stage) + la_off[j_]);            \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_)                                             \
+        dma_to_lds<16>(Be + (ob[j_] + (uint32_t)(kk) * 128u), (stage) + 2048 + (j_ * 4 + wave) * 64); \
+  } while (0)
+
+// One step on stage `cur`; NEXT: read the first fragments of `nxt`; LOADS: refill `cur` with k+2.
+#define MOE_W4_STEP(cur, nxt, k, LOADS, NEXT)                                                   \
+  w4::frags<4, 4>(cur, 1, wm, wn, lane, a1, b1);                                                \
+  w4::mfmas<4, 4>(acc, a0, b0);                                                                 \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); }    \
+  MOE_SGB(0x008, 8);                                                                            \
+  __builtin_amdgcn_sched_barrier(0);                                                            \
+  w4::frags<4, 4>(cur, 2, wm, wn, lane, a0, b0);                                                \
+  w4::mfmas<4, 4>(acc, a1, b1);                                                                 \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); }    \
+  MOE_SGB(0x008, 8);                                                                            \
+  __builtin_amdgcn_sched_barrier(0);                                                            \
+  w4::frags<4, 4>(cur, 3, wm, wn, lane, a1, b1);                                                \
+  w4::mfmas<4, 4>(acc, a0, b0);                                                                 \
+  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); }    \
+  MOE_SGB(0x008, 8);                                                                            \
+  __builtin_amdgcn_sched_barrier(0);                                                            \
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");         \
+  __builtin_amdgcn_sched_barrier(0);                                                            \
+  if (NEXT) w4::frags<4, 4>(nxt, 0, wm, wn, lane, a0, b0);                                      \
+  if (LOADS) MOE_W4_LOADS(cur, (k) + 2);                                                        \
+  w4::mfmas<4, 4>(acc, a1, b1);                                                                 \
+  if (NEXT) {                                                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); }  \
+  } else {                                                                                      \
+    MOE_SGB(0x008, 8);                                                                          \
+  }                                                                                             \
+  if (LOADS) {                                                                                  \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x010, 2); }  \
+  } else {                                                                                      \
+    MOE_SGB(0x008, 8);                                                                          \
+  }                                                                                             \
+  __builtin_amdgcn_sched_barrier(0);
+
+template <bool GLU, bool OUTF32>
+__global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
+  constexpr int BM = 256, BN = 256;
+  __shared__ u32x4 st0[w4::kStage];
+  __shared__ u32x4 st1[w4::kStage];
+  __shared__ int tp[kMaxExperts + 1];
+  __shared__ int s_slot[1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS offsets in SGPRs
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = lane & 31, lk = lane >> 5;
+  for (int i = tid; i <= g.n_exp; i += 256) tp[i] = g.tp[i];
+  __syncthreads();
+  const int total = tp[g.n_exp] * g.n_tiles_n;
+  const int KT = g.K / 64;  // K is a multiple of 128: KT is even
+  const TileQueue tq = tile_queue(total);
+
+  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
+    TileInfo ti = decode_tile(t, tp, g, BM);
+    // the same for every lane: keep it in scalar registers
+    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
+    ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
+    ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
+    ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
+    const int arows = (ti.mvalid + 7) & ~7;  // A rows fetched (8 rows per load instruction)
+    const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
+    const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
+    uint32_t oa[8], ob[8];
+    int la_off[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (j * 4 + wave) * 8 + (lane >> 3);
+      const uint32_t ch = (uint32_t)dma_chunk(r, lane) * 16u;
+      const bool live = (j * 4 + wave) * 8 < arows;  // wave-uniform
+      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      oa[j] = live ? (uint32_t)rr * (uint32_t)g.lda + ch : 0u;
+      la_off[j] = live ? (j * 4 + wave) * 64 : w4::kSink;
+      ob[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + ch;
+    }
+    if (arows < BM) {  // zero the A rows that are not fetched, in both stages
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int i = arows * 8 + tid; i < BM * 8; i += 256) {
+        st0[i] = z;
+        st1[i] = z;
+      }
+    }
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+    MOE_W4_LOADS(st0, 0);
+    MOE_W4_LOADS(st1, 1);
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    w4::frags<4, 4>(st0, 0, wm, wn, lane, a0, b0);
+    for (int k = 0; k < KT - 2; k += 2) {
+      MOE_W4_STEP(st0, st1, k, true, true)
+      MOE_W4_STEP(st1, st0, k + 1, true, true)
+    }
+    MOE_W4_STEP(st0, st1, KT - 2, false, true)
+    MOE_W4_STEP(st1, st0, KT - 1, false, false)
+
+    // epilogue (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4)
+    if (GLU) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int col = ti.nt * (BN / 2) + (wn * 2 + q) * 32 + lrow;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = wm * 128 + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+            if (r < ti.mvalid) {
+              const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
+              reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(h);
+            }
+          }
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int col = ti.nt * BN + wn * 128 + nb * 32 + lrow;
+          if (col < g.N_out) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = wm * 128 + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+              if (r < ti.mvalid) {
+                uint8_t* p = g.C + (size_t)(ti.row0 + r) * g.ldc;
+                if (OUTF32)
+                  reinterpret_cast<float*>(p)[col] = acc[mb][nb][i];
+                else
+                  reinterpret_cast<uint16_t*>(p)[col] = f32_to_bf16(acc[mb][nb][i]);
+              }
+            }
+          }
+        }
+    }
+  }
+}
+
 template <class K>
 static hipError_t launch_one(const char* name, K kernel, int grid, int threads, const GemmArgs& g,
                              hipStream_t s) {
@@ -156,16 +349,15 @@ static hipError_t launch_one(const char* name, K kernel, int grid, int threads, 
 
 static int round8(int v) { return ((v + 7) / 8) * 8; }
 
-// variant 0: 256 x 256 tiles, 8 waves, one workgroup per CU (experts with many rows);
+// variant 0: 256 x 256 tiles, 4 waves of 128 x 128, one workgroup per CU (experts with many rows);
 // variant 1: 32 x 256 tiles, 4 waves, two workgroups per CU (decode-sized row groups).
 hipError_t launch_gemm_bf16(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s) {
   hipError_t e;
   if (variant == 0) {
     const int grid = round8(cus);
-    if ((e = launch_one("gemm_bf16_gateup_swiglu", k_gemm_bf16<256, 256, 2, 4, true, 1, false>, grid, 512,
-                        g1, s)) != hipSuccess)
+    if ((e = launch_one("gemm_bf16_gateup_swiglu", k_gemm_bf16_w4<true, false>, grid, 256, g1, s)) != hipSuccess)
       return e;
-    return launch_one("gemm_bf16_down", k_gemm_bf16<256, 256, 2, 4, false, 1, true>, grid, 512, g2, s);
+    return launch_one("gemm_bf16_down", k_gemm_bf16_w4<false, true>, grid, 256, g2, s);
   }
   const int grid = round8(cus * 2);
   if ((e = launch_one("gemm_bf16_gateup_swiglu_m32", k_gemm_bf16<32, 256, 1, 4, true, 2, false>, grid, 256,

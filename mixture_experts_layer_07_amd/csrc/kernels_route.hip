@@ -168,15 +168,36 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
   if (t >= p.T) return;  // whole wave leaves together; no workgroup barrier below
   const int E = p.E;
   float z[4], sc[4], key[4];
+  // Sum the split-K partial logits in split order. Four splits are loaded before they are
+  // added, so up to 16 loads per lane are in flight (a decode-sized batch has many splits and
+  // few tokens: this loop is latency-bound).
+  {
+    const float* src = logits + (size_t)t * E + lane;
+    const size_t stride = (size_t)p.T * E;
+    bool in[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    float v = -INFINITY;
-    if (e < E) {
-      v = 0.f;
-      for (int s = 0; s < p.splits; ++s) v += logits[((size_t)s * p.T + t) * E + e];
+    for (int j = 0; j < 4; ++j) {
+      in[j] = lane + 64 * j < E;
+      z[j] = 0.f;
     }
-    z[j] = v;
+    int s = 0;
+    for (; s + 4 <= p.splits; s += 4) {
+      float v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[u][j] = in[j] ? src[(size_t)(s + u) * stride + 64 * j] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[j] += v[u][j];
+    }
+    for (; s < p.splits; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[j] += in[j] ? src[(size_t)s * stride + 64 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (!in[j]) z[j] = -INFINITY;
   }
   if (!p.sigmoid) {
     float m = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));

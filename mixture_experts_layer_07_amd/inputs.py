@@ -14,6 +14,7 @@ Recipe (weights drawn N(0, 1/fan_in), i.e. variance 1/fan_in):
   shared   one more expert of intermediate size I_shared, drawn the same way
   fp8      weights drawn in fp32 as above, then per 128x128 block scale = absmax/448
            and codes = e4m3(w / scale) via torch's float8_e4m3fn cast.
+Generator seed: (seed << 24) | (tensor_id << 16) | expert.
 x, W_r and the bias are drawn on the CPU (so every machine sees the same
 values); the expert weights are drawn on `device` with one generator per
 (tensor, expert), so any single expert can be regenerated on its own.
@@ -31,8 +32,11 @@ _TID = {"x": 1, "w_r": 2, "bias": 3, "w13": 4, "w2": 5, "w13s": 6, "w2s": 7}
 
 
 def _gen(seed, tensor, expert, device):
+    # torch's CPU generator keeps only the low 32 bits of its seed, so every field fits there
+    if not (0 <= seed < 256 and 0 <= expert < 65536):
+        raise ValueError("seed must be < 256 and expert < 65536")
     g = torch.Generator(device=device)
-    g.manual_seed((int(seed) << 32) | (_TID[tensor] << 20) | int(expert))
+    g.manual_seed((int(seed) << 24) | (_TID[tensor] << 16) | int(expert))
     return g
 
 
