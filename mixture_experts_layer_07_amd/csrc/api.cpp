@@ -219,6 +219,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_ro
   a.h = at<void>(ws, L.h);
   a.h_scale = fp8 ? at<float>(ws, L.hscale) : nullptr;
   a.tiles = at<int32_t>(ws, L.tiles);
+  a.part = at<float>(ws, L.part);
   MOE_HIP(launch_expert_ffn(a, static_cast<hipStream_t>(stream)), "expert_ffn");
   return MOE_OK;
 }

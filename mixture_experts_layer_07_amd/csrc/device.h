@@ -85,4 +85,7 @@ __device__ __forceinline__ int block_exscan_256(int v, int* sbuf4, int* tot) {
 // (x * G/8 + j) is placed on physical id (j * 8 + x), i.e. on XCD x.
 __device__ __forceinline__ int xcd_local_id(int b, int G) { return (b & 7) * (G >> 3) + (b >> 3); }
 
+// Id of the XCD this wave runs on (hardware register XCC_ID, bits [3:0]).
+__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7; }
+
 }  // namespace moe

@@ -29,6 +29,8 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* tp;
   int32_t* queue;       // kQueues tile counters (zeroed by the tile builder)
+  int32_t* split_cnt;   // kMaxSplitItems arrival counters of K-split tiles (zeroed by the tile builder)
+  float* part;          // kMaxSplitItems partial tiles of 256 x 256 fp32 (K-split tiles)
   int n_exp, K, N_out, Nb, glu_I, n_tiles_n;
 };
 
@@ -40,9 +42,16 @@ struct GemmArgs {
 // round. Every tile is computed by one workgroup from start to end, so results do not depend on
 // the order.
 constexpr int kQueues = 8;
-// Position of the queue counters in the tile-metadata region (after tp[0 .. kMaxExperts]).
+// Tile-metadata region: tp[0 .. kMaxExperts], then the queue counters of both GEMMs, then the
+// split-tile arrival counters of both GEMMs.
 constexpr int kTileQueueOffset = kMaxExperts + 1;
-static_assert(kTileQueueOffset + 2 * kQueues <= 2 * 257, "tile metadata region too small");
+constexpr int kMaxSplitItems = 256;  // K-split work items per GEMM launch (32 per XCD range)
+constexpr int kSplitCntOffset = kTileQueueOffset + 2 * kQueues;
+static_assert(kSplitCntOffset + 2 * kMaxSplitItems <= kTileMetaInts, "tile metadata region too small");
+constexpr int kPartFloats = 256 * 256;  // one partial 256 x 256 tile
+#ifndef MOE_MAX_K_PIECES
+#define MOE_MAX_K_PIECES 4  // most pieces a tail tile is cut into along K
+#endif
 
 struct TileQueue {
   int beg, end;
@@ -64,6 +73,90 @@ __device__ __forceinline__ int next_tile(const GemmArgs& g, const TileQueue& tq,
   const int t = s_slot[0];
   __syncthreads();
   return t < tq.end ? t : -1;
+}
+
+// Tile queue whose last round is split along K. A range of R tiles served by C workgroups takes
+// F = R / C full rounds; the R - F*C tiles left would keep only part of the XCD busy for a whole
+// tile, so each is cut into S pieces of K (S*tail <= C), one work item each. The pieces write
+// fp32 partial tiles; the last piece to arrive (an atomic counter per tile) sums them in piece
+// order, so the result does not depend on timing, and runs the epilogue.
+struct SplitQueue {
+  int beg;     // first tile of the range
+  int nfull;   // items [0, nfull) are whole tiles beg + item
+  int S;       // pieces per tail tile
+  int items;   // items in the range
+  int slot0;   // first partial-tile slot of the range
+  int q;       // range (= XCD) index
+};
+
+// The queue (range) is chosen by the XCD the workgroup runs on, so that every piece of a split
+// tile is computed under one L2. With one workgroup per CU all workgroups are resident and every
+// XCD serves its range.
+__device__ __forceinline__ SplitQueue split_queue(int total, int KT, int min_steps) {
+  const int q = xcc_id();
+  const int per = (total + kQueues - 1) / kQueues;
+  const int beg = q * per < total ? q * per : total;
+  const int end = beg + per < total ? beg + per : total;
+  const int R = end - beg;
+  const int C = gridDim.x / kQueues;  // workgroups serving this range
+  const int F = R / C, tail = R - F * C;
+  int S = 1;
+  // Only long K loops are cut: a piece pays a fixed cost (its own prologue, the partial tile
+  // written and read back through L2, the summation), which a short loop does not repay.
+  if (F > 0 && tail > 0 && KT >= 128 && C * kQueues <= kMaxSplitItems) {
+    S = C / tail;
+    if (S > MOE_MAX_K_PIECES) S = MOE_MAX_K_PIECES;
+    if (S > KT / min_steps) S = KT / min_steps;
+    if (S < 1) S = 1;
+  }
+  SplitQueue sq;
+  sq.beg = beg;
+  sq.S = S;
+  sq.nfull = S > 1 ? F * C : R;
+  sq.items = sq.nfull + (R - sq.nfull) * S;
+  sq.slot0 = q * C;
+  sq.q = q;
+  return sq;
+}
+
+struct WorkItem {
+  int tile;   // tile index in the expert-major list
+  int piece;  // -1: whole tile; else the K piece of a split tile
+  int k0, k1; // K steps [k0, k1)
+  int slot;   // partial-tile slot of this piece
+  int first;  // slot of piece 0 of the same tile (its arrival counter index as well)
+};
+
+// Next work item of this workgroup's range, or item.tile = -1. All threads must call (two barriers).
+// K steps are counted in units of `step`; pieces keep an even number of steps.
+__device__ __forceinline__ WorkItem next_item(const GemmArgs& g, const SplitQueue& sq, int KT, int* s_slot) {
+  if (threadIdx.x == 0) s_slot[0] = atomicAdd(&g.queue[sq.q], 1);
+  __syncthreads();
+  const int it = s_slot[0];
+  __syncthreads();
+  WorkItem w;
+  if (it >= sq.items) {
+    w.tile = -1;
+    return w;
+  }
+  if (it < sq.nfull) {
+    w.tile = sq.beg + it;
+    w.piece = -1;
+    w.k0 = 0;
+    w.k1 = KT;
+    w.slot = w.first = 0;
+    return w;
+  }
+  const int j = it - sq.nfull;
+  const int tt = j / sq.S;
+  w.tile = sq.beg + sq.nfull + tt;
+  w.piece = j - tt * sq.S;
+  const int chunk = (KT / sq.S) & ~1;
+  w.k0 = w.piece * chunk;
+  w.k1 = w.piece == sq.S - 1 ? KT : w.k0 + chunk;
+  w.first = sq.slot0 + tt * sq.S;
+  w.slot = w.first + w.piece;
+  return w;
 }
 
 struct TileInfo {

@@ -23,13 +23,14 @@ namespace moe {
 //   h        [max_rows][max_I] SwiGLU output (fp32 / bf16 / e4m3 codes)
 //   hscale   [max_rows][max_I/128] fp32 (fp8 layer)
 struct WsLayout {
-  size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, h = 0, hscale = 0, total = 0;
+  size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, part = 0, h = 0, hscale = 0, total = 0;
   int route_splits = 1;
   int perm_blocks = 0;
 };
 
 constexpr int kPermBlock = 256;   // pairs per block in the permutation kernels
 constexpr int kMaxExperts = 256;
+constexpr int kTileMetaInts = 1024;  // tile metadata of the expert GEMMs (prefix, queues, counters)
 
 // Validation; returns MOE_OK or the failure status with a reason in *why.
 moe_status check_config(const moe_config* c, std::string* why);
@@ -102,7 +103,8 @@ struct FfnArgs {
   void* y = nullptr;
   void* h = nullptr;          // workspace
   float* h_scale = nullptr;   // workspace (fp8)
-  int32_t* tiles = nullptr;   // workspace, [2][257]
+  int32_t* tiles = nullptr;   // workspace, kTileMetaInts
+  float* part = nullptr;      // workspace, partial tiles of K-split GEMM tiles
 };
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s);
 // combine

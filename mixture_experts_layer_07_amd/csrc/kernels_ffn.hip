@@ -28,8 +28,8 @@ __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__
   const int ex = block_exscan_256(c, sbuf, &tot);
   if (tid < n_exp) tp[tid] = ex;
   if (tid == 0) tp[n_exp] = tot;
-  // the tile-queue counters of both GEMMs that follow (kTileQueueOffset .. + 2 * kQueues)
-  if (tid < 2 * kQueues) tp[kTileQueueOffset + tid] = 0;
+  // the tile-queue and split-tile counters of both GEMMs that follow
+  for (int i = tid; i < 2 * kQueues + 2 * kMaxSplitItems; i += 256) tp[kTileQueueOffset + i] = 0;
 }
 
 // ============================================================================ fp32 (VALU)
@@ -137,6 +137,9 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
   g1.tp = g2.tp = a.tiles;
   g1.queue = a.tiles + kTileQueueOffset;
   g2.queue = a.tiles + kTileQueueOffset + kQueues;
+  g1.split_cnt = a.tiles + kSplitCntOffset;
+  g2.split_cnt = a.tiles + kSplitCntOffset + kMaxSplitItems;
+  g1.part = g2.part = a.part;  // the two GEMMs run one after the other on the stream
   g1.n_exp = g2.n_exp = a.n_exp;
   // Linear-1 (gate + up) with the SwiGLU epilogue: [rows,H] x [2I,H]^T -> h [rows,I]
   g1.K = H;

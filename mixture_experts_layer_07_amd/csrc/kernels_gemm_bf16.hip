@@ -235,6 +235,35 @@ __device__ __forceinline__ void mfmas(f32x16 (&acc)[MB][NB], const bf16x8 (&a)[M
   }                                                                                             \
   __builtin_amdgcn_sched_barrier(0);
 
+// Partial tiles of K-split work items: float4 v of thread t at [v][t] (coalesced 4 KiB rows).
+// All pieces of a tile run on one XCD (the split queue is chosen by the XCD id), so the partials
+// meet in that XCD's L2: plain stores completed before the arrival counter is incremented, and
+// plain loads after it (no L1 line of another piece's partial is ever read before in a launch).
+__device__ __forceinline__ void store_partial(float* part, const f32x16 (&acc)[4][4], int tid) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = {acc[mb][nb][4 * c], acc[mb][nb][4 * c + 1], acc[mb][nb][4 * c + 2], acc[mb][nb][4 * c + 3]};
+        reinterpret_cast<f32x4*>(part)[((mb * 4 + nb) * 4 + c) * 256 + tid] = v;
+      }
+}
+
+__device__ __forceinline__ void add_partial(const float* part, f32x16 (&acc)[4][4], int tid) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = reinterpret_cast<const f32x4*>(part)[((mb * 4 + nb) * 4 + c) * 256 + tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mb][nb][4 * c + e] += v[e];
+      }
+}
+
 template <bool GLU, bool OUTF32>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   constexpr int BM = 256, BN = 256;
@@ -250,15 +279,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   __syncthreads();
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 64;  // K is a multiple of 128: KT is even
-  const TileQueue tq = tile_queue(total);
+  const SplitQueue sq = split_queue(total, KT, 16);
 
-  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
-    TileInfo ti = decode_tile(t, tp, g, BM);
+  for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {
+    TileInfo ti = decode_tile(w.tile, tp, g, BM);
     // the same for every lane: keep it in scalar registers
     ti.e = __builtin_amdgcn_readfirstlane(ti.e);
     ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
     ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
     ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
+    const int k0 = __builtin_amdgcn_readfirstlane(w.k0), k1 = __builtin_amdgcn_readfirstlane(w.k1);
     const int arows = (ti.mvalid + 7) & ~7;  // A rows fetched (8 rows per load instruction)
     const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
@@ -289,19 +319,43 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 
-    MOE_W4_LOADS(st0, 0);
-    MOE_W4_LOADS(st1, 1);
+    MOE_W4_LOADS(st0, k0);
+    MOE_W4_LOADS(st1, k0 + 1);
     asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     bf16x8 a0[4], b0[4], a1[4], b1[4];
     w4::frags<4, 4>(st0, 0, wm, wn, lane, a0, b0);
-    for (int k = 0; k < KT - 2; k += 2) {
+    for (int k = k0; k < k1 - 2; k += 2) {
       MOE_W4_STEP(st0, st1, k, true, true)
       MOE_W4_STEP(st1, st0, k + 1, true, true)
     }
-    MOE_W4_STEP(st0, st1, KT - 2, false, true)
-    MOE_W4_STEP(st1, st0, KT - 1, false, false)
+    MOE_W4_STEP(st0, st1, k1 - 2, false, true)
+    MOE_W4_STEP(st1, st0, k1 - 1, false, false)
 
-    // epilogue (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4)
+    if (w.piece >= 0) {
+      // K-split tile: publish this piece; the last piece to arrive sums all of them in piece order
+      // (every store of this workgroup has completed before its counter increment)
+      store_partial(g.part + (size_t)w.slot * kPartFloats, acc, tid);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) s_slot[0] = atomicAdd(&g.split_cnt[w.first], 1);
+      __syncthreads();
+      const int arrived = s_slot[0];
+      __syncthreads();
+      if (arrived != sq.S - 1) continue;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+      for (int pc = 0; pc < sq.S; ++pc) add_partial(g.part + (size_t)(w.first + pc) * kPartFloats, acc, tid);
+    }
+
+    // epilogue (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4).
+    // The row base passes through an empty asm so that the row indices are formed here, per tile,
+    // instead of being hoisted out of the tile loop and held in registers across the K loop.
+    int rbase = wm * 128 + lk * 4;
+    asm volatile("" : "+v"(rbase));
     if (GLU) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
@@ -310,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
           const int col = ti.nt * (BN / 2) + (wn * 2 + q) * 32 + lrow;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int r = wm * 128 + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+            const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
             if (r < ti.mvalid) {
               const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
               reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(h);
@@ -326,7 +380,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
           if (col < g.N_out) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int r = wm * 128 + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
+              const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
               if (r < ti.mvalid) {
                 uint8_t* p = g.C + (size_t)(ti.row0 + r) * g.ldc;
                 if (OUTF32)
