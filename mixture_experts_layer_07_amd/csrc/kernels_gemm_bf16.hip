@@ -150,29 +150,33 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) 
 
 
 // ============================================================================ 256 x 256 tiles
-// Four waves (2 x 2), each owning a 128 x 128 block of the tile: 16 accumulators of 32 x 32 in
-// the accumulation registers, one wave per SIMD. K advances 64 channels per step through two
-// LDS stages (A 256 rows + B 256 rows of 128 bytes = full cache lines, plus a 1 KiB sink),
-// filled by direct-to-LDS loads. Within step k:
+// Four waves, one per SIMD. K advances 64 channels per step through two LDS stages (A 256 rows +
+// B 256 rows of 128 bytes = full cache lines, plus a 1 KiB sink), filled by direct-to-LDS loads.
+// Within step k:
 //   sub-steps 0..2: MFMAs of sub-step s while the fragments of s+1 are read;
 //   then: this wave's reads of the stage are complete and its loads of step k+1 have landed;
 //         a workgroup barrier (no memory fence: the waits are explicit) extends both to all waves;
 //   sub-step 3: MFMAs while the first fragments of step k+1 are read and the loads of step k+2
 //         go into the stage just released.
-// Rows of A past the tile's valid rows are not fetched: their loads read one cached line and land
-// in the sink, and their LDS rows are zeroed once per tile (a zero operand also draws less power
-// in the MFMA pipes). Their accumulators are never stored.
+// The wave layout follows the tile's valid rows h (the last m-tile of an expert is ragged):
+//   h > 128: 2 x 2 waves of 128 x 128 (16 accumulators of 32 x 32 each);
+//   h <= 128, 64, 32: 1 x 4 waves of h' x 64 (h' = 128, 64, 32), so that the MFMA work follows
+//   the rows while the 256 weight rows stream once.
+// Rows of A past the valid rows are not fetched: their loads read one cached line and land in the
+// sink, and their LDS rows are zeroed once per tile (a zero operand also draws less power in the
+// MFMA pipes). Accumulators of rows past h are never stored.
 namespace w4 {
 constexpr int kStage = 4096 + 64;  // u32x4 per stage: A 2048 + B 2048 + 64 (sink)
 constexpr int kSink = 4096;
 
+// Fragments of sub-step ks: A rows r0 + 32 mb + (lane & 31), B rows c0 + 32 nb + (lane & 31).
 template <int MB, int NB>
-__device__ __forceinline__ void frags(const u32x4* st, int ks, int wm, int wn, int lane, bf16x8 (&a)[MB],
+__device__ __forceinline__ void frags(const u32x4* st, int ks, int r0, int c0, int lane, bf16x8 (&a)[MB],
                                       bf16x8 (&b)[NB]) {
   const int lrow = lane & 31, lk = lane >> 5;
   const int slot = (ks * 2 + lk) ^ lds_swz(lrow);  // block rows start at multiples of 32
-  const u32x4* la = st + (wm * 128 + lrow) * 8 + slot;
-  const u32x4* lb = st + 2048 + (wn * 128 + lrow) * 8 + slot;
+  const u32x4* la = st + (r0 + lrow) * 8 + slot;
+  const u32x4* lb = st + 2048 + (c0 + lrow) * 8 + slot;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) a[mb] = __builtin_bit_cast(bf16x8, la[mb * 256]);
 #pragma unroll
@@ -187,82 +191,189 @@ __device__ __forceinline__ void mfmas(f32x16 (&acc)[MB][NB], const bf16x8 (&a)[M
     for (int nb = 0; nb < NB; ++nb)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
 }
+
+// Partial tiles of K-split work items (2 x 2 layout): float4 v of thread t at [v][t] (coalesced
+// 4 KiB rows). All pieces of a tile run on one XCD (the split queue is chosen by the XCD id), so
+// the partials meet in that XCD's L2: plain stores completed before the arrival counter is
+// incremented, and plain loads after it (no L1 line of another piece's partial is ever read
+// before in a launch).
+template <int MB, int NB>
+__device__ __forceinline__ void store_partial(float* part, const f32x16 (&acc)[MB][NB], int tid) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = {acc[mb][nb][4 * c], acc[mb][nb][4 * c + 1], acc[mb][nb][4 * c + 2], acc[mb][nb][4 * c + 3]};
+        reinterpret_cast<f32x4*>(part)[((mb * NB + nb) * 4 + c) * 256 + tid] = v;
+      }
+}
+
+template <int MB, int NB>
+__device__ __forceinline__ void add_partial(const float* part, f32x16 (&acc)[MB][NB], int tid) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = reinterpret_cast<const f32x4*>(part)[((mb * NB + nb) * 4 + c) * 256 + tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mb][nb][4 * c + e] += v[e];
+      }
+}
+
+// Epilogue of a wave's MB x NB blocks at rows r0.., columns c0.. of the 256-row weight tile
+// (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4).
+// GLU: blocks 2q, 2q+1 hold gate and up columns of the same h column.
+template <int MB, int NB, bool GLU, bool OUTF32>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, const f32x16 (&acc)[MB][NB],
+                                         int r0, int c0, int lane) {
+  const int lrow = lane & 31, lk = lane >> 5;
+  // The row base passes through an empty asm so that the row indices are formed here, per tile,
+  // instead of being hoisted out of the tile loop and held in registers across the K loop.
+  int rbase = r0 + lk * 4;
+  asm volatile("" : "+v"(rbase));
+  if (GLU) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < NB / 2; ++q) {
+        const int col = ti.nt * 128 + c0 / 2 + q * 32 + lrow;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
+          if (r < ti.mvalid) {
+            const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
+            reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(h);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = ti.nt * 256 + c0 + nb * 32 + lrow;
+        if (col < g.N_out) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
+            if (r < ti.mvalid) {
+              uint8_t* p = g.C + (size_t)(ti.row0 + r) * g.ldc;
+              if (OUTF32)
+                reinterpret_cast<float*>(p)[col] = acc[mb][nb][i];
+              else
+                reinterpret_cast<uint16_t*>(p)[col] = f32_to_bf16(acc[mb][nb][i]);
+            }
+          }
+        }
+      }
+  }
+}
 }  // namespace w4
 
 // Scheduling groups: 0x008 MFMA, 0x010 vector memory, 0x100 LDS read.
 #define MOE_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 
-// The 16 direct-to-LDS loads of one step (8 of A, 8 of B) into `stage`.
-#define MOE_W4_LOADS(stage, kk)                                                                  \
+// The direct-to-LDS loads of one step into `stage`: AJ_ of A (rows below 32 * AJ_; a path for
+// shorter tiles issues fewer) and 8 of B.
+#define MOE_W4_LOADS(stage, kk, AJ_)                                                             \
   do {                                                                                           \
-    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_)                                             \
+    _Pragma("unroll") for (int j_ = 0; j_ < (AJ_); ++j_)                                         \
         dma_to_lds<16>(Ab + (oa[j_] + (uint32_t)(kk) * 128u), (stage) + la_off[j_]);            \
     _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_)                                             \
         dma_to_lds<16>(Be + (ob[j_] + (uint32_t)(kk) * 128u), (stage) + 2048 + (j_ * 4 + wave) * 64); \
   } while (0)
 
-// One step on stage `cur`; NEXT: read the first fragments of `nxt`; LOADS: refill `cur` with k+2.
-#define MOE_W4_STEP(cur, nxt, k, LOADS, NEXT)                                                   \
-  w4::frags<4, 4>(cur, 1, wm, wn, lane, a1, b1);                                                \
-  w4::mfmas<4, 4>(acc, a0, b0);                                                                 \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); }    \
-  MOE_SGB(0x008, 8);                                                                            \
-  __builtin_amdgcn_sched_barrier(0);                                                            \
-  w4::frags<4, 4>(cur, 2, wm, wn, lane, a0, b0);                                                \
-  w4::mfmas<4, 4>(acc, a1, b1);                                                                 \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); }    \
-  MOE_SGB(0x008, 8);                                                                            \
-  __builtin_amdgcn_sched_barrier(0);                                                            \
-  w4::frags<4, 4>(cur, 3, wm, wn, lane, a1, b1);                                                \
-  w4::mfmas<4, 4>(acc, a0, b0);                                                                 \
-  _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); }    \
-  MOE_SGB(0x008, 8);                                                                            \
-  __builtin_amdgcn_sched_barrier(0);                                                            \
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");         \
-  __builtin_amdgcn_sched_barrier(0);                                                            \
-  if (NEXT) w4::frags<4, 4>(nxt, 0, wm, wn, lane, a0, b0);                                      \
-  if (LOADS) MOE_W4_LOADS(cur, (k) + 2);                                                        \
-  w4::mfmas<4, 4>(acc, a1, b1);                                                                 \
-  if (NEXT) {                                                                                   \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); }  \
-  } else {                                                                                      \
-    MOE_SGB(0x008, 8);                                                                          \
-  }                                                                                             \
-  if (LOADS) {                                                                                  \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x010, 2); }  \
-  } else {                                                                                      \
-    MOE_SGB(0x008, 8);                                                                          \
-  }                                                                                             \
+// A sub-step's MFMAs interleaved with the fragment reads of the next (pairs while both last).
+#define MOE_W4_SUB(MB_, NB_)                                                                     \
+  _Pragma("unroll") for (int i_ = 0; i_ < ((MB_) * (NB_) < (MB_) + (NB_) ? (MB_) * (NB_) : (MB_) + (NB_)); ++i_) { \
+    MOE_SGB(0x008, 1);                                                                           \
+    MOE_SGB(0x100, 1);                                                                           \
+  }                                                                                              \
+  if ((MB_) * (NB_) > (MB_) + (NB_)) MOE_SGB(0x008, (MB_) * (NB_) - (MB_) - (NB_));              \
   __builtin_amdgcn_sched_barrier(0);
 
-// Partial tiles of K-split work items: float4 v of thread t at [v][t] (coalesced 4 KiB rows).
-// All pieces of a tile run on one XCD (the split queue is chosen by the XCD id), so the partials
-// meet in that XCD's L2: plain stores completed before the arrival counter is incremented, and
-// plain loads after it (no L1 line of another piece's partial is ever read before in a launch).
-__device__ __forceinline__ void store_partial(float* part, const f32x16 (&acc)[4][4], int tid) {
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 v = {acc[mb][nb][4 * c], acc[mb][nb][4 * c + 1], acc[mb][nb][4 * c + 2], acc[mb][nb][4 * c + 3]};
-        reinterpret_cast<f32x4*>(part)[((mb * 4 + nb) * 4 + c) * 256 + tid] = v;
-      }
-}
+// One step on stage `cur`; NEXT: read the first fragments of `nxt`; LOADS: refill `cur` with k+2.
+#define MOE_W4_STEP(MB_, NB_, cur, nxt, k, LOADS, NEXT)                                          \
+  w4::frags<MB_, NB_>(cur, 1, r0, c0, lane, a1, b1);                                             \
+  w4::mfmas<MB_, NB_>(acc, a0, b0);                                                              \
+  MOE_W4_SUB(MB_, NB_)                                                                           \
+  w4::frags<MB_, NB_>(cur, 2, r0, c0, lane, a0, b0);                                             \
+  w4::mfmas<MB_, NB_>(acc, a1, b1);                                                              \
+  MOE_W4_SUB(MB_, NB_)                                                                           \
+  w4::frags<MB_, NB_>(cur, 3, r0, c0, lane, a1, b1);                                             \
+  w4::mfmas<MB_, NB_>(acc, a0, b0);                                                              \
+  MOE_W4_SUB(MB_, NB_)                                                                           \
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");          \
+  __builtin_amdgcn_sched_barrier(0);                                                             \
+  if (NEXT) w4::frags<MB_, NB_>(nxt, 0, r0, c0, lane, a0, b0);                                   \
+  if (LOADS) MOE_W4_LOADS(cur, (k) + 2, (MB_) * (NB_) == 16 ? 8 : (MB_));                        \
+  w4::mfmas<MB_, NB_>(acc, a1, b1);                                                              \
+  if ((MB_) * (NB_) == 16) {                                                                     \
+    /* 16 MFMAs: the first 8 carry the next fragments, the last 8 the 16 loads */               \
+    if (NEXT) {                                                                                  \
+      _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); } \
+    } else {                                                                                     \
+      MOE_SGB(0x008, 8);                                                                         \
+    }                                                                                            \
+    if (LOADS) {                                                                                 \
+      _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x010, 2); } \
+    } else {                                                                                     \
+      MOE_SGB(0x008, 8);                                                                         \
+    }                                                                                            \
+  } else if (LOADS) {                                                                            \
+    /* few MFMAs: the loads go first */                                                          \
+    MOE_SGB(0x010, 8 + (MB_));                                                                   \
+  }                                                                                              \
+  __builtin_amdgcn_sched_barrier(0);
 
-__device__ __forceinline__ void add_partial(const float* part, f32x16 (&acc)[4][4], int tid) {
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 v = reinterpret_cast<const f32x4*>(part)[((mb * 4 + nb) * 4 + c) * 256 + tid];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[mb][nb][4 * c + e] += v[e];
-      }
-}
+// One tile (or K piece of a tile) with waves of MB x NB blocks: rows r0.., weight rows c0...
+#define MOE_W4_TILE(MB_, NB_, r0_, c0_, SPLIT)                                                   \
+  {                                                                                              \
+    const int r0 = (r0_), c0 = (c0_);                                                            \
+    constexpr int AJ = (MB_) * (NB_) == 16 ? 8 : (MB_); /* A load instructions per wave, step */ \
+    f32x16 acc[MB_][NB_];                                                                        \
+    _Pragma("unroll") for (int mb = 0; mb < (MB_); ++mb)                                         \
+      _Pragma("unroll") for (int nb = 0; nb < (NB_); ++nb)                                       \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;                     \
+    MOE_W4_LOADS(st0, k0, AJ);                                                                   \
+    MOE_W4_LOADS(st1, k0 + 1, AJ);                                                               \
+    /* wait for step k0's loads: the AJ + 8 of step k0 + 1 may still be in flight */             \
+    if (AJ == 8) asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+    else if (AJ == 4) asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+    else if (AJ == 2) asm volatile("s_waitcnt vmcnt(10)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
+    else asm volatile("s_waitcnt vmcnt(9)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  \
+    bf16x8 a0[MB_], b0[NB_], a1[MB_], b1[NB_];                                                   \
+    w4::frags<MB_, NB_>(st0, 0, r0, c0, lane, a0, b0);                                           \
+    for (int k = k0; k < k1 - 2; k += 2) {                                                       \
+      MOE_W4_STEP(MB_, NB_, st0, st1, k, true, true)                                             \
+      MOE_W4_STEP(MB_, NB_, st1, st0, k + 1, true, true)                                         \
+    }                                                                                            \
+    MOE_W4_STEP(MB_, NB_, st0, st1, k1 - 2, false, true)                                         \
+    MOE_W4_STEP(MB_, NB_, st1, st0, k1 - 1, false, false)                                        \
+    bool store = true;                                                                           \
+    if (SPLIT && w.piece >= 0) {                                                                 \
+      /* K piece: publish it; the last piece to arrive sums all of them in piece order */        \
+      w4::store_partial(g.part + (size_t)w.slot * kPartFloats, acc, tid);                        \
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                           \
+      __syncthreads();                                                                           \
+      if (tid == 0) s_slot[0] = atomicAdd(&g.split_cnt[w.first], 1);                             \
+      __syncthreads();                                                                           \
+      store = s_slot[0] == sq.S - 1;                                                             \
+      __syncthreads();                                                                           \
+      if (store) {                                                                               \
+        _Pragma("unroll") for (int mb = 0; mb < (MB_); ++mb)                                     \
+          _Pragma("unroll") for (int nb = 0; nb < (NB_); ++nb)                                   \
+            _Pragma("unroll") for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;                 \
+        for (int pc = 0; pc < sq.S; ++pc)                                                        \
+          w4::add_partial(g.part + (size_t)(w.first + pc) * kPartFloats, acc, tid);              \
+      }                                                                                          \
+    }                                                                                            \
+    if (store) w4::epilogue<MB_, NB_, GLU, OUTF32>(g, ti, acc, r0, c0, lane);                    \
+  }
 
 template <bool GLU, bool OUTF32>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
@@ -273,8 +384,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   __shared__ int s_slot[1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS offsets in SGPRs
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = lane & 31, lk = lane >> 5;
   for (int i = tid; i <= g.n_exp; i += 256) tp[i] = g.tp[i];
   __syncthreads();
   const int total = tp[g.n_exp] * g.n_tiles_n;
@@ -311,86 +420,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
         st1[i] = z;
       }
     }
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-
-    MOE_W4_LOADS(st0, k0);
-    MOE_W4_LOADS(st1, k0 + 1);
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
-    w4::frags<4, 4>(st0, 0, wm, wn, lane, a0, b0);
-    for (int k = k0; k < k1 - 2; k += 2) {
-      MOE_W4_STEP(st0, st1, k, true, true)
-      MOE_W4_STEP(st1, st0, k + 1, true, true)
-    }
-    MOE_W4_STEP(st0, st1, k1 - 2, false, true)
-    MOE_W4_STEP(st1, st0, k1 - 1, false, false)
-
-    if (w.piece >= 0) {
-      // K-split tile: publish this piece; the last piece to arrive sums all of them in piece order
-      // (every store of this workgroup has completed before its counter increment)
-      store_partial(g.part + (size_t)w.slot * kPartFloats, acc, tid);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (tid == 0) s_slot[0] = atomicAdd(&g.split_cnt[w.first], 1);
-      __syncthreads();
-      const int arrived = s_slot[0];
-      __syncthreads();
-      if (arrived != sq.S - 1) continue;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-      for (int pc = 0; pc < sq.S; ++pc) add_partial(g.part + (size_t)(w.first + pc) * kPartFloats, acc, tid);
-    }
-
-    // epilogue (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4).
-    // The row base passes through an empty asm so that the row indices are formed here, per tile,
-    // instead of being hoisted out of the tile loop and held in registers across the K loop.
-    int rbase = wm * 128 + lk * 4;
-    asm volatile("" : "+v"(rbase));
-    if (GLU) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int col = ti.nt * (BN / 2) + (wn * 2 + q) * 32 + lrow;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
-            if (r < ti.mvalid) {
-              const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
-              reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(h);
-            }
-          }
-        }
+    // K pieces always take the 2 x 2 layout (their partial tiles share one shape)
+    if (w.piece >= 0 || ti.mvalid > 128) {
+      MOE_W4_TILE(4, 4, (wave >> 1) * 128, (wave & 1) * 128, true)
+    } else if (ti.mvalid > 64) {
+      MOE_W4_TILE(4, 2, 0, wave * 64, false)
+    } else if (ti.mvalid > 32) {
+      MOE_W4_TILE(2, 2, 0, wave * 64, false)
     } else {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int col = ti.nt * BN + wn * 128 + nb * 32 + lrow;
-          if (col < g.N_out) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
-              if (r < ti.mvalid) {
-                uint8_t* p = g.C + (size_t)(ti.row0 + r) * g.ldc;
-                if (OUTF32)
-                  reinterpret_cast<float*>(p)[col] = acc[mb][nb][i];
-                else
-                  reinterpret_cast<uint16_t*>(p)[col] = f32_to_bf16(acc[mb][nb][i]);
-              }
-            }
-          }
-        }
+      MOE_W4_TILE(1, 2, 0, wave * 64, false)
     }
   }
 }
