@@ -85,7 +85,10 @@ def kernel_work(cfg, active):
 
 def variant_free(name):
     """Kernel name without its tile-variant suffix (the work model does not depend on it)."""
-    return name[:-4] if name.endswith("_m32") else name
+    for suf in ("_m32", "_m128"):
+        if name.endswith(suf):
+            return name[:-len(suf)]
+    return name
 
 
 def main():

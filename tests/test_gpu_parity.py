@@ -81,6 +81,50 @@ def test_permute_skewed_ids_and_ragged_experts():
     assert B.moe_get_device_error(L.ws) == 0
 
 
+def _skewed_ids(T, counts):
+    """[T, 2] ids with the given per-expert pair counts (distinct experts per token)."""
+    counts = list(counts)
+    assert sum(counts) == 2 * T and counts[0] <= T
+    first = [0] * counts[0]
+    rest = [e for e, c in enumerate(counts) if e > 0 for _ in range(c)]
+    first += rest[:T - counts[0]]
+    second = rest[T - counts[0]:]
+    ids = torch.tensor([first, second], dtype=torch.int32).t().contiguous()
+    assert (ids[:, 0] != ids[:, 1]).all()
+    return ids
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_large_tile_paths(dtype):
+    """Row groups that select the 256 x 256-tile kernels and every valid-row height of their last
+    m-tile (full, <= 128, <= 64, <= 32 rows), with caller-supplied ids; sampled rows of every
+    expert against the oracle."""
+    base = CONFIGS[2] if dtype == "bf16" else CONFIGS[5]
+    cfg = base.scaled(T=2048, H=256, I=2048, E=8, K=2, score="softmax", renorm=True, route_scale=1.0,
+                      n_group=1, topk_group=1, bias=None, I_shared=0)
+    counts = [2000, 800, 500, 300, 220, 150, 90, 36]   # last m-tiles: 208, 32, 244, 44, 220, 150, 90, 36
+    case = Case(cfg)
+    L = case.layer
+    ids = _skewed_ids(cfg.T, counts)
+    L.topk_ids.copy_(ids)
+    L.permute(case.xd)
+    L.expert_ffn()
+    torch.cuda.synchronize()
+    _, offsets, _, _ = orc.permute(ids.numpy(), cfg.E)
+    assert (np.diff(offsets) == counts).all()
+    rng = np.random.default_rng(7)
+    rows = set()
+    for e in range(cfg.E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        last_tile = lo + (hi - lo - 1) // 256 * 256
+        rows.update([lo, hi - 1, last_tile, min(last_tile + 31, hi - 1)])
+        rows.update(rng.integers(lo, hi, 4).tolist())
+    rep = {}
+    check_ffn(case, offsets, np.array(sorted(rows)), rep)
+    assert B.moe_get_device_error(L.ws) == 0
+    print(dtype, rep)
+
+
 def test_out_of_range_ids_set_the_device_error():
     cfg = CONFIGS[2].scaled(T=64, H=256, I=128, E=8, K=2)
     case = Case(cfg)
