@@ -70,7 +70,7 @@ __device__ __forceinline__ TileQueue tile_queue(int total) {
 __device__ __forceinline__ int next_tile(const GemmArgs& g, const TileQueue& tq, int* s_slot) {
   if (threadIdx.x == 0) s_slot[0] = tq.beg + atomicAdd(&g.queue[blockIdx.x % kQueues], 1);
   __syncthreads();
-  const int t = s_slot[0];
+  const int t = __builtin_amdgcn_readfirstlane(s_slot[0]);  // uniform: scalar registers
   __syncthreads();
   return t < tq.end ? t : -1;
 }
@@ -132,7 +132,8 @@ struct WorkItem {
 __device__ __forceinline__ WorkItem next_item(const GemmArgs& g, const SplitQueue& sq, int KT, int* s_slot) {
   if (threadIdx.x == 0) s_slot[0] = atomicAdd(&g.queue[sq.q], 1);
   __syncthreads();
-  const int it = s_slot[0];
+  // the same for every lane; readfirstlane tells the compiler so (scalar registers, uniform branches)
+  const int it = __builtin_amdgcn_readfirstlane(s_slot[0]);
   __syncthreads();
   WorkItem w;
   if (it >= sq.items) {
@@ -165,20 +166,24 @@ struct TileInfo {
 
 // Logical tile t in expert-major order (expert, then n-tile, then m-tile): the m-tiles that
 // share one weight block are neighbours. tp[e] = m-tiles before expert e (in LDS).
+// Every value is the same for all lanes; readfirstlane says so to the compiler, which then keeps
+// them in scalar registers and reads `offsets` with scalar loads.
 __device__ __forceinline__ TileInfo decode_tile(int t, const int* tp, const GemmArgs& g, int BM) {
   TileInfo ti;
+  t = __builtin_amdgcn_readfirstlane(t);
   const int q = t / g.n_tiles_n;
   int lo = 0, hi = g.n_exp - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (tp[mid] <= q)
+    if (__builtin_amdgcn_readfirstlane(tp[mid]) <= q)
       lo = mid;
     else
       hi = mid - 1;
   }
   ti.e = lo;
-  const int mcount = tp[lo + 1] - tp[lo];
-  const int local = t - tp[lo] * g.n_tiles_n;
+  const int tp0 = __builtin_amdgcn_readfirstlane(tp[lo]);
+  const int mcount = __builtin_amdgcn_readfirstlane(tp[lo + 1]) - tp0;
+  const int local = t - tp0 * g.n_tiles_n;
   ti.nt = local / mcount;
   ti.mt = local - ti.nt * mcount;
   const int seg0 = g.offsets[lo], seg1 = g.offsets[lo + 1];

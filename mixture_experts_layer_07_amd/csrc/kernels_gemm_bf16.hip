@@ -227,11 +227,18 @@ __device__ __forceinline__ void add_partial(const float* part, f32x16 (&acc)[MB]
 // Epilogue of a wave's MB x NB blocks at rows r0.., columns c0.. of the 256-row weight tile
 // (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4).
 // GLU: blocks 2q, 2q+1 hold gate and up columns of the same h column.
+// Stores go through a buffer resource spanning the tile's valid rows: the hardware drops those of
+// rows past them, with no per-element branch.
 template <int MB, int NB, bool GLU, bool OUTF32>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, const f32x16 (&acc)[MB][NB],
                                          int r0, int c0, int lane) {
   const int lrow = lane & 31, lk = lane >> 5;
-  // The row base passes through an empty asm so that the row indices are formed here, per tile,
+  const int ldc = (int)g.ldc;
+  // (uniform values: readfirstlane keeps the resource in scalar registers, as the instruction needs)
+  const int row0 = __builtin_amdgcn_readfirstlane(ti.row0), mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc(g.C + (size_t)row0 * g.ldc, (short)0, mvalid * ldc, 0x00020000);
+  // The row base passes through an empty asm so that the row offsets are formed here, per tile,
   // instead of being hoisted out of the tile loop and held in registers across the K loop.
   int rbase = r0 + lk * 4;
   asm volatile("" : "+v"(rbase));
@@ -244,10 +251,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
-          if (r < ti.mvalid) {
-            const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
-            reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(h);
-          }
+          const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
+          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), rc, r * ldc + col * 2, 0, 0);
         }
       }
   } else {
@@ -260,13 +265,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, 
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
-            if (r < ti.mvalid) {
-              uint8_t* p = g.C + (size_t)(ti.row0 + r) * g.ldc;
-              if (OUTF32)
-                reinterpret_cast<float*>(p)[col] = acc[mb][nb][i];
-              else
-                reinterpret_cast<uint16_t*>(p)[col] = f32_to_bf16(acc[mb][nb][i]);
-            }
+            if (OUTF32)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mb][nb][i]), rc, r * ldc + col * 4, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[mb][nb][i]), rc, r * ldc + col * 2, 0, 0);
           }
         }
       }
@@ -362,7 +364,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, 
       __syncthreads();                                                                           \
       if (tid == 0) s_slot[0] = atomicAdd(&g.split_cnt[w.first], 1);                             \
       __syncthreads();                                                                           \
-      store = s_slot[0] == sq.S - 1;                                                             \
+      store = __builtin_amdgcn_readfirstlane(s_slot[0]) == sq.S - 1;                             \
       __syncthreads();                                                                           \
       if (store) {                                                                               \
         _Pragma("unroll") for (int mb = 0; mb < (MB_); ++mb)                                     \
