@@ -95,10 +95,14 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer is not sharded "
-              "across GPUs in this build.", file=sys.stderr)
+              "across GPUs.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
+
+    from mixture_experts_layer_07_amd.configs import ROUTE_CONFIGS
+    if args.config in ROUTE_CONFIGS:
+        return bench_route(args, ROUTE_CONFIGS[args.config])
 
     from mixture_experts_layer_07_amd import binding as B
     from mixture_experts_layer_07_amd.configs import CONFIGS, active_flops
@@ -204,6 +208,102 @@ def main():
     }
     if args.copy_calibration_gib > 0:
         copy_calibration(args.copy_calibration_gib, dev)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_route(args, cfg):
+    """Routing-only workload: one step = scores + grouped top-K on [T,E] fp32 logits resident in
+    HBM (moe_route_logits), then one loss-free bias update over E expert loads (moe_update_bias).
+    Both kernels take microseconds, so the timed steps are replayed from a HIP graph (the eager
+    rate, host launches included, is reported beside it); the step is latency-bound."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_07_amd import binding as B
+    from mixture_experts_layer_07_amd.inputs import make_router_logits
+
+    torch.cuda.set_device(0)
+    z_host = make_router_logits(cfg)
+    z = z_host.cuda()
+    ids = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device="cuda")
+    bias = torch.zeros(cfg.E, dtype=torch.float32, device="cuda")
+    B.moe_route_logits(cfg, z, None, ids, w)
+    counts = torch.bincount(ids.reshape(-1).long(), minlength=cfg.E).to(torch.int32)  # input only
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.moe_route_logits(cfg, z, None, ids, w)
+        B.moe_update_bias(cfg.E, counts, bias, 1e-3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = t0.elapsed_time(t1) / args.steps
+    # the same steps captured once in a HIP graph and replayed: no host launch cost per kernel
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    B.profile_enable(True)
+    B.profile_reset()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = B.profile_read()
+    B.profile_enable(False)
+    by = {"route/topk": cfg.T * cfg.E * 4 + cfg.T * cfg.K * 8, "route/update_bias": cfg.E * 8}
+    kernels = {}
+    for k, (tot, n) in prof.items():
+        name = "route/" + k
+        d = {"avg_ms": round(tot / n, 5), "launches_per_step": n / args.steps}
+        if name in by:
+            d["gb_s"] = round(by[name] / (tot / n * 1e-3) / 1e9, 3)
+        kernels[name] = d
+    tk = prof["topk"]
+    avg_s = tk[0] / tk[1] * 1e-3
+    roof = {"kernel": "route/topk", "bound": "hbm", "achieved": by["route/topk"] / avg_s / 1e9,
+            "peak": HBM_PEAK, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / HBM_PEAK
+    roof["traffic"] = None
+    roof["algorithmic_per_launch"] = {"flops": 0.0, "bytes": by["route/topk"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        zz = z_host.double().numpy()
+        reps, t_c = 0, time.perf_counter()
+        while time.perf_counter() - t_c < 2.0 or reps < 3:
+            ids_o, w_o = orc.route(zz, cfg.score, cfg.K, None, cfg.n_group, cfg.topk_group, cfg.group_rule,
+                                   cfg.renorm, cfg.route_scale)
+            orc.update_bias(np.zeros(cfg.E, np.float32), np.bincount(ids_o.reshape(-1), minlength=cfg.E), 1e-3)
+            reps += 1
+        sec = (time.perf_counter() - t_c) / reps
+        cpu = {"value": round(cfg.T / sec, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"all {cfg.T} tokens, {reps} repetitions (numpy, one thread of Python loops)"}
+    rec = {
+        "metric": "routing tokens/s (GroupedTopK on resident logits + loss-free bias update)",
+        "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic", "ms_per_step_eager": round(ms_eager, 5),
+        "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "K": cfg.K, "n_group": cfg.n_group,
+                   "topk_group": cfg.topk_group, "score": cfg.score, "group_rule": cfg.group_rule,
+                   "global_batch": cfg.T, "parallelism": "single-gpu"},
+        "kernels": kernels, "roofline": roof, "cpu_baseline": cpu,
+    }
     print(json.dumps(rec), flush=True)
 
 

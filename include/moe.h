@@ -95,6 +95,31 @@ size_t moe_workspace_size(const moe_config* cfg);
 moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
                      int32_t* topk_ids, float* topk_weights, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_route_logits -- scores and (grouped) top-K on router logits the caller already holds.
+ * "MoE 路由入门", sections 3, 4, 7 and 10 (the GroupedTopK operator: [T,E] logits in, only the
+ * K weights and ids of each token out; the hidden states are not read). Same selection,
+ * weights and tie rule as moe_route; reads only T, E, K, score_fn, renorm, route_scale,
+ * n_group, topk_group and group_score of cfg (the other fields are not checked).
+ *   logits       device [T,E] fp32, row-major
+ *   bias         device [E] fp32 added to the scores for selection only, or NULL
+ *   topk_ids     device [T,K] int32 out
+ *   topk_weights device [T,K] fp32 out
+ * Needs no workspace. Errors: MOE_ERR_INVALID_ARG for a bad routing field or a NULL buffer
+ * (checked before any device call). */
+moe_status moe_route_logits(const moe_config* cfg, const float* logits, const float* bias,
+                            int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* moe_update_bias -- one step of loss-free load balancing ("MoE" chapter README,
+ * llm-infra-atlas.github.io/moe, section 2.2): the selection bias of expert e moves by gamma
+ * towards balance, bias[e] += gamma * sign(mean load - counts[e]), the mean taken over the
+ * n_experts entries. The direction is decided exactly (integer comparison of the total load
+ * with n_experts * counts[e]); the update is one fp32 rounding of bias[e] +- gamma, in place.
+ *   counts  device [n_experts] int32 loads (e.g. the counts of moe_permute)
+ *   bias    device [n_experts] fp32, updated in place
+ * 1 <= n_experts <= 256; gamma finite. Errors: MOE_ERR_INVALID_ARG, before any device call. */
+moe_status moe_update_bias(int32_t n_experts, const int32_t* counts, float* bias, float gamma,
+                           void* stream);
+
 /* moe_permute -- bucket the P = T*K (token, expert) pairs by expert ("MoE 路由入门", 5.1).
  * Pair p = t*K + k has expert topk_ids[p].
  *   topk_ids     device [T,K] int32 in; ids outside [0,E) set the device error word

@@ -44,6 +44,8 @@ _SIGS = {
     "moe_check_config": (_I, [_P]),
     "moe_workspace_size": (ctypes.c_size_t, [_P]),
     "moe_route": (_I, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_route_logits": (_I, [_P, _P, _P, _P, _P, _P]),
+    "moe_update_bias": (_I, [_I, _P, _P, ctypes.c_float, _P]),
     "moe_permute": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _P, _P, _P]),
@@ -130,6 +132,17 @@ def moe_route(cfg, x, w_router, bias, topk_ids, topk_weights, ws, stream=None):
     c, pc = _cfg(cfg)
     _check(lib().moe_route(pc, _p(x), _p(w_router), _p(bias), _p(topk_ids), _p(topk_weights),
                            _p(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_route")
+
+
+def moe_route_logits(cfg, logits, bias, topk_ids, topk_weights, stream=None):
+    c, pc = _cfg(cfg)
+    _check(lib().moe_route_logits(pc, _p(logits), _p(bias), _p(topk_ids), _p(topk_weights),
+                                  _stream(stream)), "moe_route_logits")
+
+
+def moe_update_bias(n_experts, counts, bias, gamma, stream=None):
+    _check(lib().moe_update_bias(int(n_experts), _p(counts), _p(bias), float(gamma), _stream(stream)),
+           "moe_update_bias")
 
 
 def moe_permute(cfg, topk_ids, counts, offsets, sorted_pair, pair_pos, x, x_perm, x_perm_scale, ws,

@@ -56,6 +56,17 @@ CONFIGS = {
 }
 
 
+# Routing-only workload: the default shape of the GroupedTopK operator in section 10 of
+# "MoE 路由入门": 83 tokens, softmax over 256 experts, 8 groups of 32 ranked by their maximum,
+# keep 4 groups, top-8, renormalised. Its input is the [T,E] logits (the hidden states of that
+# operator's interface are not read). H and I are the fine-grained layer's, unused here.
+ROUTE_CONFIGS = {
+    6: LayerConfig("grouped-topk-83", T=83, H=7168, I=2048, E=256, K=8, score="softmax",
+                   renorm=True, route_scale=1.0, n_group=8, topk_group=4, group_rule="max",
+                   bias=None, dtype="bf16", I_shared=0, seed=5),
+}
+
+
 def active_flops(cfg: LayerConfig) -> float:
     """Router GEMM + routed SwiGLU GEMMs (6*H*I per pair) + shared expert (6*H*I_s per token)."""
     return 2.0 * cfg.T * cfg.H * cfg.E + 6.0 * cfg.H * cfg.I * cfg.P + 6.0 * cfg.H * cfg.I_shared * cfg.T

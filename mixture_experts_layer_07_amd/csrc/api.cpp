@@ -143,6 +143,29 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* w_router,
   return MOE_OK;
 }
 
+moe_status moe_route_logits(const moe_config* cfg, const float* logits, const float* bias,
+                            int32_t* topk_ids, float* topk_weights, void* stream) {
+  std::string why;
+  const moe_status cs = check_routing(cfg, &why);
+  if (cs != MOE_OK) return fail(cs, why);
+  if (!logits || !topk_ids || !topk_weights) return fail(MOE_ERR_INVALID_ARG, "moe_route_logits: NULL buffer");
+  MOE_TRY(ensure_device());
+  MOE_HIP(launch_topk(*cfg, logits, 1, bias, topk_ids, topk_weights, static_cast<hipStream_t>(stream)), "topk");
+  return MOE_OK;
+}
+
+moe_status moe_update_bias(int32_t n_experts, const int32_t* counts, float* bias, float gamma,
+                           void* stream) {
+  if (n_experts < 1 || n_experts > kMaxExperts)
+    return fail(MOE_ERR_INVALID_ARG, "moe_update_bias: n_experts must be in [1, 256]");
+  if (!counts || !bias) return fail(MOE_ERR_INVALID_ARG, "moe_update_bias: NULL buffer");
+  if (!(gamma == gamma) || gamma > 3.0e38f || gamma < -3.0e38f)
+    return fail(MOE_ERR_INVALID_ARG, "moe_update_bias: gamma must be finite");
+  MOE_TRY(ensure_device());
+  MOE_HIP(launch_update_bias(counts, n_experts, bias, gamma, static_cast<hipStream_t>(stream)), "update_bias");
+  return MOE_OK;
+}
+
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
                        void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,

@@ -33,6 +33,7 @@ constexpr int kMaxExperts = 256;
 constexpr int kTileMetaInts = 1024;  // tile metadata of the expert GEMMs (prefix, queues, counters)
 
 // Validation; returns MOE_OK or the failure status with a reason in *why.
+moe_status check_routing(const moe_config* c, std::string* why);
 moe_status check_config(const moe_config* c, std::string* why);
 // Workspace layout of a valid config.
 WsLayout layout(const moe_config& c);
@@ -77,6 +78,7 @@ hipError_t launch_router_bf16(const void* x, const void* wrt, float* logits, int
 hipError_t launch_topk(const moe_config& c, const float* logits, int splits, const float* bias,
                        int32_t* ids, float* weights, hipStream_t s);
 // permute
+hipError_t launch_update_bias(const int32_t* counts, int E, float* bias, float gamma, hipStream_t s);
 hipError_t launch_clear_words(int32_t* p, int n, hipStream_t s);
 hipError_t launch_perm_hist(const int32_t* ids, int P, int E, int32_t* hist, int32_t* err,
                             hipStream_t s);

@@ -354,4 +354,35 @@ hipError_t launch_topk(const moe_config& c, const float* logits, int splits, con
   });
 }
 
+// ------------------------------------------------------------------ loss-free bias update
+// The aux-free balancing step of the "MoE" chapter README (llm-infra-atlas.github.io/moe, 2.2):
+// each expert's selection bias moves by a fixed step towards balance,
+// b_e <- b_e + gamma * sign(mean load - load_e). The bias only changes which experts are chosen,
+// never the weights. mean load - load_e has the sign of (sum of loads) - E * load_e, compared in
+// 64-bit integers, so the direction is decided exactly; the step is one fp32 rounding of
+// b_e +- gamma. One workgroup; thread e owns expert e.
+__global__ __launch_bounds__(256) void k_update_bias(const int32_t* __restrict__ counts, int E,
+                                                     float* __restrict__ bias, float gamma) {
+  __shared__ long long part[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long c = tid < E ? (long long)counts[tid] : 0;
+  long long v = c;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  const long long total = part[0] + part[1] + part[2] + part[3];
+  if (tid < E) {
+    const long long d = total - (long long)E * c;
+    const float b = bias[tid];
+    bias[tid] = d > 0 ? b + gamma : (d < 0 ? b - gamma : b);
+  }
+}
+
+hipError_t launch_update_bias(const int32_t* counts, int E, float* bias, float gamma, hipStream_t s) {
+  return timed_launch("update_bias", s, [&] {
+    hipLaunchKernelGGL(k_update_bias, dim3(1), dim3(256), 0, s, counts, E, bias, gamma);
+  });
+}
+
 }  // namespace moe

@@ -10,14 +10,15 @@ namespace moe {
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-moe_status check_config(const moe_config* c, std::string* why) {
+// The fields scoring and selection read: T, E, K, the score function, renorm, route_scale and
+// the group rule.
+moe_status check_routing(const moe_config* c, std::string* why) {
   auto bad = [&](moe_status s, const char* msg) {
     if (why) *why = msg;
     return s;
   };
   if (!c) return bad(MOE_ERR_INVALID_ARG, "config is NULL");
-  if (c->T < 1 || c->H < 1 || c->I < 1 || c->E < 1 || c->K < 1)
-    return bad(MOE_ERR_INVALID_ARG, "T, H, I, E and K must be positive");
+  if (c->T < 1 || c->E < 1 || c->K < 1) return bad(MOE_ERR_INVALID_ARG, "T, E and K must be positive");
   if (c->K > c->E) return bad(MOE_ERR_INVALID_ARG, "K must not exceed E");
   if (c->E > kMaxExperts) return bad(MOE_ERR_UNSUPPORTED, "E above 256 is not supported");
   if (c->score_fn != MOE_SOFTMAX && c->score_fn != MOE_SIGMOID)
@@ -25,8 +26,6 @@ moe_status check_config(const moe_config* c, std::string* why) {
   if (c->renorm != 0 && c->renorm != 1) return bad(MOE_ERR_INVALID_ARG, "renorm must be 0 or 1");
   if (!(c->route_scale == c->route_scale) || c->route_scale > 3.0e38f || c->route_scale < -3.0e38f)
     return bad(MOE_ERR_INVALID_ARG, "route_scale must be finite");
-  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8_E4M3)
-    return bad(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (c->n_group < 1 || c->E % c->n_group != 0)
     return bad(MOE_ERR_INVALID_ARG, "n_group must be >= 1 and divide E");
   if (c->n_group > 1) {
@@ -39,6 +38,20 @@ moe_status check_config(const moe_config* c, std::string* why) {
     if (c->group_score == MOE_GROUP_TOP2_SUM && c->E / c->n_group < 2)
       return bad(MOE_ERR_INVALID_ARG, "top-2-sum group score needs >= 2 experts per group");
   }
+  if ((int64_t)c->T * c->K >= (int64_t(1) << 31)) return bad(MOE_ERR_INVALID_ARG, "T*K must be below 2^31");
+  return MOE_OK;
+}
+
+moe_status check_config(const moe_config* c, std::string* why) {
+  auto bad = [&](moe_status s, const char* msg) {
+    if (why) *why = msg;
+    return s;
+  };
+  const moe_status r = check_routing(c, why);
+  if (r != MOE_OK) return r;
+  if (c->H < 1 || c->I < 1) return bad(MOE_ERR_INVALID_ARG, "T, H, I, E and K must be positive");
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8_E4M3)
+    return bad(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (c->I_shared < 0) return bad(MOE_ERR_INVALID_ARG, "I_shared must be >= 0");
   const int q = (c->dtype == MOE_F32) ? 4 : 128;
   if (c->H % q || c->I % q || c->I_shared % q)

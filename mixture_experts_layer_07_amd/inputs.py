@@ -12,6 +12,7 @@ Recipe (weights drawn N(0, 1/fan_in), i.e. variance 1/fan_in):
   W13      [E, 2I, H], N(0,1/H): gate rows [0,I) then up rows [I,2I)
   W2       [E, H, I],  N(0,1/I)
   shared   one more expert of intermediate size I_shared, drawn the same way
+  logits   (routing-only workloads) N(0,1) [T,E] fp32, the unit logit spread of the layers
   fp8      weights drawn in fp32 as above, then per 128x128 block scale = absmax/448
            and codes = e4m3(w / scale) via torch's float8_e4m3fn cast.
 Generator seed: (seed << 24) | (tensor_id << 16) | expert.
@@ -28,7 +29,7 @@ from .configs import LayerConfig
 _ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ZIPF_BIAS_FILE = os.path.join(_ROOT, "tests", "golden", "decode_zipf_bias.txt")
 
-_TID = {"x": 1, "w_r": 2, "bias": 3, "w13": 4, "w2": 5, "w13s": 6, "w2s": 7}
+_TID = {"x": 1, "w_r": 2, "bias": 3, "w13": 4, "w2": 5, "w13s": 6, "w2s": 7, "logits": 8}
 
 
 def _gen(seed, tensor, expert, device):
@@ -128,3 +129,8 @@ def make_expert_weights(cfg: LayerConfig, device="cpu", shared=False):
     for e in range(n):
         w13[e], w2[e] = expert_weights(cfg, e, device, shared)
     return {"w13": w13, "w2": w2, "w13_scale": None, "w2_scale": None}
+
+
+def make_router_logits(cfg: LayerConfig) -> torch.Tensor:
+    """[T,E] fp32 router logits N(0,1) for the routing-only workloads (CPU)."""
+    return _randn((cfg.T, cfg.E), 1.0, cfg.seed, "logits")

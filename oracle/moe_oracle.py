@@ -40,6 +40,9 @@ transposed operand fails at least one of them:
     computed independently; brute-force dense mixing over all E experts with
     non-selected weights zeroed ([primer] §2) equals the sparse combine;
   * score: softmax rows sum to one, are order preserving, sigmoid closed forms;
+  * update_bias: the fixed step and direction of [atlas] §2.2 (an expert above the
+    mean load loses exactly gamma, one below gains it), no move at exactly the mean
+    load, and repeated steps with a fixed router shrink the spread of a skewed load;
   * e4m3 codec: all 256 codes against the format's bit-level definition, encode
     against exhaustive nearest-value search and torch's float8_e4m3fn;
   * quantize_rows_fp8: exactly representable rows round-trip, zero blocks,
@@ -53,7 +56,7 @@ import numpy as np
 __all__ = [
     "NEAR_TIE_GAP", "E4M3_MAX", "FP8_BLOCK",
     "router_logits", "score", "select_topk", "group_scores", "grouped_select",
-    "route", "near_tie_tokens", "permute", "gather_rows",
+    "route", "near_tie_tokens", "update_bias", "permute", "gather_rows",
     "e4m3_decode", "e4m3_decode_array", "e4m3_encode",
     "quantize_rows_fp8", "dequantize_rows_fp8", "dequantize_weight_blocks",
     "silu", "swiglu_hidden", "swiglu_expert", "expert_ffn", "combine",
@@ -203,6 +206,22 @@ def near_tie_tokens(z, fn, K, bias=None, n_group=1, topk_group=1, group_rule="to
         if se.size > 1 and np.min(se[:-1] - se[1:]) < gap:
             flags[t] = True
     return flags
+
+
+def update_bias(bias, counts, gamma):
+    """One loss-free balancing step ([atlas] §2.2): b_e <- b_e + gamma * sign(mean load - load_e).
+
+    The mean is taken over the E entries of `counts`. An expert above the mean load
+    has its selection bias lowered, one below it raised, one exactly at it left
+    alone. The bias is a stored fp32 vector: the new value is the exact sum
+    b_e + gamma * sign(...) (formed in fp64, where it is exact) rounded once to fp32.
+    Returns the new bias [E] fp32.
+    """
+    b = np.asarray(bias, np.float32).astype(np.float64)
+    c = np.asarray(counts, np.float64)
+    mean = c.sum() / c.size
+    step = np.sign(mean - c) * float(np.float32(gamma))
+    return (b + step).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------- dispatch

@@ -104,6 +104,16 @@ def test_entry_points_validate_before_device(lib):
     assert lib.moe_quantize_fp8(4, 100, FAKE, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_fp8(4, 256, None, FAKE, FAKE, None) == INVALID
     assert lib.moe_get_device_error(None, ctypes.byref(ctypes.c_int32()), None) == INVALID
+    # logits-only routing reads only the routing fields: H, I and dtype are not checked
+    cr = cfg(3, T=83, E=256, K=8, n_group=8, topk_group=4)
+    cr.H, cr.I, cr.dtype = 0, 0, 9
+    assert lib.moe_route_logits(ctypes.byref(cr), None, None, FAKE, FAKE, None) == INVALID
+    cr.K = 200
+    assert lib.moe_route_logits(ctypes.byref(cr), FAKE, None, FAKE, FAKE, None) == INVALID
+    assert lib.moe_update_bias(0, FAKE, FAKE, ctypes.c_float(0.01), None) == INVALID
+    assert lib.moe_update_bias(257, FAKE, FAKE, ctypes.c_float(0.01), None) == INVALID
+    assert lib.moe_update_bias(16, None, FAKE, ctypes.c_float(0.01), None) == INVALID
+    assert lib.moe_update_bias(16, FAKE, FAKE, ctypes.c_float(float("nan")), None) == INVALID
     assert lib.moe_status_string(3) == b"workspace too small"
 
 

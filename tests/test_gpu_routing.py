@@ -1,0 +1,110 @@
+"""GPU parity of the routing-only entry points (through the C ABI) against the CPU oracle:
+scores + (grouped) top-K on caller-held logits, and the loss-free bias update."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from mixture_experts_layer_07_amd import binding as B
+from mixture_experts_layer_07_amd.configs import ROUTE_CONFIGS
+from mixture_experts_layer_07_amd.inputs import make_router_logits
+
+pytestmark = pytest.mark.gpu
+
+KS = ROUTE_CONFIGS[6]
+ROUTE_CASES = {
+    # the GroupedTopK operator's default shape: softmax, group maximum, 4 of 8 groups, top-8
+    "grouped-topk-83": (KS, False),
+    # the fine-grained layers' rule on logits: sigmoid + selection bias, top-2-sum groups, x2.5
+    "sigmoid-bias-top2sum": (KS.scaled(T=1000, score="sigmoid", group_rule="top2_sum", route_scale=2.5), True),
+    # plain top-K over softmax, one token
+    "softmax-plain-T1": (KS.scaled(T=1, n_group=1, topk_group=1), False),
+    # E not a multiple of the wave width, groups of 9
+    "E72-groups-of-9": (KS.scaled(T=300, E=72, K=6, n_group=8, topk_group=3, seed=6), True),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTE_CASES))
+def test_route_logits(name):
+    cfg, with_bias = ROUTE_CASES[name]
+    print(f"route_logits case {name}", flush=True)
+    z = make_router_logits(cfg)
+    bias = (torch.from_numpy(np.random.default_rng(cfg.seed).normal(0, 0.1, cfg.E).astype(np.float32))
+            if with_bias else None)
+    ids = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device="cuda")
+    B.moe_route_logits(cfg, z.cuda(), None if bias is None else bias.cuda(), ids, w)
+    torch.cuda.synchronize()
+    ids_g = ids.cpu().numpy().astype(np.int64)
+    w_g = w.cpu().numpy().astype(np.float64)
+    zb = z.double().numpy()
+    bb = None if bias is None else bias.double().numpy()
+    ids_o, w_o = orc.route(zb, cfg.score, cfg.K, bb, cfg.n_group, cfg.topk_group, cfg.group_rule,
+                           cfg.renorm, cfg.route_scale)
+    ties = orc.near_tie_tokens(zb, cfg.score, cfg.K, bb, cfg.n_group, cfg.topk_group, cfg.group_rule)
+    mism = (ids_g != ids_o).any(1)
+    assert not (mism & ~ties).any(), f"{int((mism & ~ties).sum())} non-tie tokens differ"
+    ok = ~mism
+    assert np.abs(w_g - w_o)[ok].max() <= 1e-5 * cfg.route_scale
+    assert ((ids_g >= 0) & (ids_g < cfg.E)).all()
+    assert all(len(set(r)) == cfg.K for r in ids_g.tolist())
+    np.testing.assert_allclose(w_g.sum(1), cfg.route_scale, rtol=2e-6)
+    if cfg.n_group > 1:
+        gs = cfg.E // cfg.n_group
+        assert max(len(set((r // gs).tolist())) for r in ids_g) <= cfg.topk_group
+
+
+@pytest.mark.parametrize("E", [256, 72, 1])
+def test_update_bias_bit_exact(E):
+    print(f"update_bias E={E}", flush=True)
+    rng = np.random.default_rng(E)
+    p = rng.zipf(1.3, E).astype(np.float64)
+    counts = rng.multinomial(1024 * 8, p / p.sum()).astype(np.int32)
+    bias = rng.normal(0, 0.1, E).astype(np.float32)
+    bias[: min(E, 3)] = [1e-9, -0.0, 3.0][: min(E, 3)]
+    c_d = torch.from_numpy(counts).cuda()
+    b_d = torch.from_numpy(bias.copy()).cuda()
+    want = bias
+    for gamma in [1e-3, 0.25]:           # two steps in a row, the second on the updated bias
+        B.moe_update_bias(E, c_d, b_d, gamma)
+        want = orc.update_bias(want, counts, gamma)
+    torch.cuda.synchronize()
+    got = b_d.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # a balanced load leaves the bias alone
+    B.moe_update_bias(E, torch.full((E,), 7, dtype=torch.int32, device="cuda"), b_d, 0.5)
+    torch.cuda.synchronize()
+    assert np.array_equal(b_d.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+def test_routing_step_graph_replays_match_eager():
+    """The routing step captured in a HIP graph (as the benchmark replays it): every replay, with
+    eager work and synchronisations between replays, matches the eager result, and the bias
+    update accumulates exactly as repeated oracle steps."""
+    cfg = KS
+    z = make_router_logits(cfg).cuda()
+    ids = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device="cuda")
+    B.moe_route_logits(cfg, z, None, ids, w)
+    torch.cuda.synchronize()
+    ids_e, w_e = ids.clone(), w.clone()
+    counts = torch.bincount(ids_e.reshape(-1).long(), minlength=cfg.E).to(torch.int32)
+    bias = torch.zeros(cfg.E, dtype=torch.float32, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.moe_route_logits(cfg, z, None, ids, w)
+        B.moe_update_bias(cfg.E, counts, bias, 1e-3)
+    torch.cuda.synchronize()
+    bias.zero_()  # capture does not run the kernels; start the replays from zero
+    want = np.zeros(cfg.E, np.float32)
+    c_host = counts.cpu().numpy()
+    for r in range(4):
+        ids.fill_(-1)
+        w.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = orc.update_bias(want, c_host, 1e-3)
+        assert torch.equal(ids, ids_e) and torch.equal(w, w_e), f"replay {r}"
+        assert np.array_equal(bias.cpu().numpy().view(np.uint32), want.view(np.uint32)), f"replay {r}"
+        _ = (z * 2).sum().item()  # eager work between replays

@@ -354,3 +354,42 @@ def test_near_tie_flags():
     zz = np.log(keys / (1 - keys + 1e-300) + 1e-300)              # sigmoid^-1
     assert orc.near_tie_tokens(zz, "sigmoid", 1, None, 3, 1, "max").tolist() == [False]
     assert orc.near_tie_tokens(zz, "sigmoid", 1, None, 3, 2, "max").tolist() == [True]
+
+
+def test_update_bias_step_and_direction():
+    # [atlas] §2.2: a fixed step gamma, against the load: above the mean -> down, below -> up
+    counts = np.array([10, 2, 6, 6, 1, 11], np.int64)  # mean 6
+    b0 = np.array([0.5, -0.25, 0.125, 0.0, 1.0, -1.0], np.float32)
+    g = np.float32(0.0625)
+    b1 = orc.update_bias(b0, counts, g)
+    assert b1.dtype == np.float32
+    d = b1.astype(np.float64) - b0.astype(np.float64)
+    assert np.all(d[counts > 6] == -0.0625)
+    assert np.all(d[counts < 6] == 0.0625)
+    assert np.all(d[counts == 6] == 0.0)
+    # exactly balanced load: nothing moves, whatever gamma
+    assert np.array_equal(orc.update_bias(b0, np.full(6, 7), 0.3), b0)
+    # the new value is the fp32 rounding of the exact sum
+    tiny = np.array([1.0, 1.0], np.float32)
+    got = orc.update_bias(tiny, np.array([0, 5]), np.float32(2.0 ** -30))
+    assert got[0] == np.float32(1.0) and got[1] == np.float32(1.0)
+
+
+def test_update_bias_balances_a_fixed_router():
+    # repeated steps against one fixed batch of sigmoid scores: the spread of the loads shrinks
+    rng = np.random.default_rng(7)
+    T, E, K = 512, 16, 2
+    z = rng.standard_normal((T, E))
+    z[:, :3] += 1.0  # three popular experts
+    b = np.zeros(E, np.float32)
+
+    def loads(bias):
+        ids, _ = orc.route(z, "sigmoid", K, bias=bias, renorm=True)
+        return np.bincount(ids.reshape(-1), minlength=E)
+
+    c0 = loads(b)
+    for _ in range(200):
+        b = orc.update_bias(b, loads(b), 1e-2)
+    c1 = loads(b)
+    assert c0.max() - c0.min() > 3 * (c1.max() - c1.min())
+    assert (b[:3] < 0).all()  # the popular experts were priced down
