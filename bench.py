@@ -27,6 +27,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--x-perm", action="store_true",
+                   help="time the path that writes the permuted activations x_perm instead of "
+                        "gathering the token rows in Linear-1")
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = auto)")
     p.add_argument("--copy-calibration-gib", type=float, default=0.0,
                    help="after the measurement, run one plain copy-like pass over this many GiB "
@@ -34,11 +37,13 @@ def parse():
     return p.parse_args()
 
 
-def kernel_work(cfg, active):
+def kernel_work(cfg, active, gather=True):
     """Algorithmic work of one step, per kernel name: {name: (flops, bytes)}.
 
     Bytes count each operand once at its stored width (inputs read once, outputs written once);
     `active` = experts that received at least one pair (only their weights are read).
+    gather: Linear-1 of the routed experts reads x ([T,H], fp8: its codes) in place, so its A
+    operand is T rows; otherwise the permute stage writes x_perm ([P,H]) and Linear-1 reads it.
     Keys are "stage/kernel" with the kernel's tile-variant suffix removed.
     """
     T, H, I, E, K, P, Is = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.P, cfg.I_shared
@@ -56,9 +61,9 @@ def kernel_work(cfg, active):
 
     kind = {"f32": "gemm_f32", "bf16": "gemm_bf16", "fp8": "gemm_fp8"}[cfg.dtype]
 
-    def ffn(st, rows, nexp, inter):
+    def ffn(st, rows, nexp, inter, a_rows):
         add(st + kind + "_gateup_swiglu", 4.0 * rows * H * inter,
-            rows * H * (ab + sc) + nexp * 2 * inter * H * (ab + wsc) + rows * inter * (ab + sc))
+            a_rows * H * (ab + sc) + nexp * 2 * inter * H * (ab + wsc) + rows * inter * (ab + sc))
         add(st + kind + "_down", 2.0 * rows * H * inter,
             rows * inter * (ab + sc) + nexp * H * inter * (ab + wsc) + rows * H * yb)
 
@@ -70,14 +75,19 @@ def kernel_work(cfg, active):
     add("permute/perm_hist", 0.0, P * 4 + E * 4)
     add("permute/perm_scan", 0.0, E * 8)
     add("permute/perm_scatter", 0.0, P * 4 + P * 8)
-    add("permute/gather_quant_fp8" if fp8 else "permute/gather", 0.0, P * 4 + P * H * xb + P * H * (ab + sc))
-    add("ffn/build_tiles", 0.0, E * 8)
-    ffn("ffn/", P, active, I)
-    if Is:
+    if gather:
         if fp8:
+            add("permute/quantize_fp8", 0.0, T * H * 2 + T * H * (1 + sc))
+    else:
+        add("permute/gather_quant_fp8" if fp8 else "permute/gather", 0.0,
+            P * 4 + P * H * xb + P * H * (ab + sc))
+    add("ffn/build_tiles", 0.0, E * 8)
+    ffn("ffn/", P, active, I, T if gather else P)
+    if Is:
+        if fp8 and not gather:
             add("shared/quantize_fp8", 0.0, T * H * 2 + T * H * (1 + sc))
         add("shared/build_tiles", 0.0, 8)
-        ffn("shared/", T, 1, Is)
+        ffn("shared/", T, 1, Is, T)
     cname = {"f32": "combine_f32", "bf16": "combine_f32_to_bf16", "fp8": "combine_bf16"}[cfg.dtype]
     add("combine/" + cname, 0.0, P * 4 + T * K * 4 + P * H * yb + (T * H * yb if Is else 0) + T * H * xb)
     return w
@@ -116,7 +126,8 @@ def main():
     ex = make_expert_weights(cfg, dev)
     sh = make_expert_weights(cfg, dev, shared=True) if cfg.I_shared else None
     clean = lambda d: None if d is None else {k: v for k, v in d.items() if v is not None}  # noqa: E731
-    layer = MoELayer(cfg, w_r.to(dev), None if bias is None else bias.to(dev), clean(ex), clean(sh), dev)
+    layer = MoELayer(cfg, w_r.to(dev), None if bias is None else bias.to(dev), clean(ex), clean(sh), dev,
+                     gather=not args.x_perm)
     xd = x.to(dev)
     stream = torch.cuda.current_stream()
 
@@ -138,7 +149,7 @@ def main():
     # per-kernel durations: HIP events recorded by the library around each launch on the launch
     # stream, read stage by stage so that routed and shared-expert launches are told apart
     stages = [("route", lambda: layer.route(xd)), ("permute", lambda: layer.permute(xd)),
-              ("ffn", layer.expert_ffn), ("shared", lambda: layer.shared_ffn(xd)),
+              ("ffn", lambda: layer.expert_ffn(xd)), ("shared", lambda: layer.shared_ffn(xd)),
               ("combine", layer.combine)]
     B.profile_enable(True)
     prof = {}
@@ -158,7 +169,7 @@ def main():
     tokens_s = cfg.T / (ms * 1e-3)
     dtype = cfg.dtype
     active = int((layer.counts > 0).sum().item())
-    work = kernel_work(cfg, active)
+    work = kernel_work(cfg, active, layer.gather)
     kernels = {}
     for k, (tot_ms, n) in prof.items():
         fl, by = work.get(variant_free(k), (0.0, 0.0))
@@ -197,7 +208,8 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[dtype], "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
                    "I_shared": cfg.I_shared, "global_batch": cfg.T, "seq_len": cfg.T,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu",
+                   "linear1_input": "x_perm copy" if args.x_perm else "token rows gathered in place"},
         "tokens_per_s": round(tokens_s, 1),
         "mfma_peak_frac": round(tflops / PEAK[dtype], 4),
         "active_experts": active,

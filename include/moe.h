@@ -159,6 +159,24 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_ro
                           const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* moe_expert_ffn_gather -- moe_expert_ffn whose Linear-1 reads the activations in place:
+ * grouped row i is x row sorted_pair[i] / cfg->K (the token of pair sorted_pair[i]), so the
+ * permuted copy x_perm is neither written nor read. The dispatch feeding the first GEMM
+ * directly is the layout idea of "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4",
+ * section 3.6.2; the arithmetic is that of moe_expert_ffn, row for row.
+ *   sorted_pair device [n_rows] int32: moe_permute's sorted_pair (values in [0, T*K); a value
+ *               outside is clamped to the last token, so no read leaves x)
+ *   x           device [T,H]: fp32 / bf16, or e4m3 codes (MOE_FP8_E4M3, e.g. moe_quantize_fp8 of
+ *               the layer input, the same codes the shared expert reads)
+ *   x_scale     device [T,H/128] fp32 (MOE_FP8_E4M3), else NULL
+ * Other arguments, outputs and errors as moe_expert_ffn; MOE_ERR_UNSUPPORTED if x is 4 GiB or
+ * more (the per-row offsets are 32-bit). */
+moe_status moe_expert_ffn_gather(const moe_config* cfg, int32_t n_experts, int32_t n_rows,
+                                 int32_t inter, const int32_t* offsets, const int32_t* sorted_pair,
+                                 const void* x, const float* x_scale, const void* w13,
+                                 const float* w13_scale, const void* w2, const float* w2_scale,
+                                 void* y_rows, void* ws, size_t ws_bytes, void* stream);
+
 /* moe_combine -- weighted combine back to [T,H] ("MoE 路由入门", section 5.3; shared expert
  * added before the residual, "MoE" chapter README, section 0).
  *   pair_pos     device [P] int32 from moe_permute

@@ -48,6 +48,8 @@ _SIGS = {
     "moe_update_bias": (_I, [_I, _P, _P, ctypes.c_float, _P]),
     "moe_permute": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_ffn_gather": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                   _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_fp8": (_I, [_I, _I, _P, _P, _P, _P]),
     "moe_get_device_error": (_I, [_P, ctypes.POINTER(_I), _P]),
@@ -159,6 +161,15 @@ def moe_expert_ffn(cfg, n_experts, n_rows, inter, offsets, x_rows, x_scale, w13,
     _check(lib().moe_expert_ffn(pc, n_experts, n_rows, inter, _p(offsets), _p(x_rows), _p(x_scale),
                                 _p(w13), _p(w13_scale), _p(w2), _p(w2_scale), _p(y_rows), _p(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)), "moe_expert_ffn")
+
+
+def moe_expert_ffn_gather(cfg, n_experts, n_rows, inter, offsets, sorted_pair, x, x_scale, w13,
+                          w13_scale, w2, w2_scale, y_rows, ws, stream=None):
+    c, pc = _cfg(cfg)
+    _check(lib().moe_expert_ffn_gather(pc, n_experts, n_rows, inter, _p(offsets), _p(sorted_pair), _p(x),
+                                       _p(x_scale), _p(w13), _p(w13_scale), _p(w2), _p(w2_scale),
+                                       _p(y_rows), _p(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)), "moe_expert_ffn_gather")
 
 
 def moe_combine(cfg, pair_pos, topk_weights, y_perm, y_shared, out, stream=None):

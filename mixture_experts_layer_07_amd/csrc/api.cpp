@@ -196,31 +196,39 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
   return MOE_OK;
 }
 
-moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_rows, int32_t inter,
-                          const int32_t* offsets, const void* x_rows, const float* x_scale,
-                          const void* w13, const float* w13_scale, const void* w2,
-                          const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
-                          void* stream) {
+}  // extern "C"
+
+// Shared body of moe_expert_ffn and moe_expert_ffn_gather (gather: Linear-1 row i reads x row
+// gather[i] / cfg->K, x holding T rows).
+static moe_status expert_ffn(const char* where, const moe_config* cfg, int32_t n_experts,
+                             int32_t n_rows, int32_t inter, const int32_t* offsets,
+                             const int32_t* gather, const void* x, const float* x_scale,
+                             const void* w13, const float* w13_scale, const void* w2,
+                             const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                             void* stream) {
   MOE_TRY(checked_config(cfg));
   const moe_config& c = *cfg;
+  const std::string w(where);
   if (n_experts < 1 || n_experts > kMaxExperts)
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_experts must be in [1, 256]");
+    return fail(MOE_ERR_INVALID_ARG, w + ": n_experts must be in [1, 256]");
   const int64_t P = (int64_t)c.T * c.K;
-  if (n_rows < 0 || n_rows > P)
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_rows must be in [0, T*K]");
+  if (n_rows < 0 || n_rows > P) return fail(MOE_ERR_INVALID_ARG, w + ": n_rows must be in [0, T*K]");
   const int maxI = c.I > c.I_shared ? c.I : c.I_shared;
   const int q = c.dtype == MOE_F32 ? 4 : 128;
   if (inter < 1 || inter > maxI || inter % q)
     return fail(MOE_ERR_INVALID_ARG,
-                "moe_expert_ffn: inter must be in [1, max(I, I_shared)] and a multiple of 128 "
-                "(4 for fp32)");
-  if (!offsets || !x_rows || !w13 || !w2 || !y_rows)
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: NULL buffer");
+                w + ": inter must be in [1, max(I, I_shared)] and a multiple of 128 (4 for fp32)");
+  if (!offsets || !x || !w13 || !w2 || !y_rows) return fail(MOE_ERR_INVALID_ARG, w + ": NULL buffer");
   const bool fp8 = c.dtype == MOE_FP8_E4M3;
   if (fp8 && (!x_scale || !w13_scale || !w2_scale))
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: fp8 layers need x_scale, w13_scale, w2_scale");
+    return fail(MOE_ERR_INVALID_ARG, w + ": fp8 layers need x_scale, w13_scale, w2_scale");
   if (!fp8 && (x_scale || w13_scale || w2_scale))
-    return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: scales are only for fp8 layers");
+    return fail(MOE_ERR_INVALID_ARG, w + ": scales are only for fp8 layers");
+  if (gather) {
+    const int64_t xb = c.dtype == MOE_F32 ? 4 : (fp8 ? 1 : 2);
+    if ((int64_t)c.T * c.H * xb >= (int64_t(1) << 32))
+      return fail(MOE_ERR_UNSUPPORTED, w + ": x above 4 GiB cannot be gathered (use moe_permute's x_perm)");
+  }
   WsLayout L;
   MOE_TRY(check_ws(c, ws, ws_bytes, &L));
   if (n_rows == 0) return MOE_OK;
@@ -232,8 +240,11 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_ro
   a.H = c.H;
   a.I = inter;
   a.offsets = offsets;
-  a.x = x_rows;
+  a.x = x;
   a.x_scale = x_scale;
+  a.x_rows_index = gather;
+  a.x_rows_div = c.K;
+  a.x_rows_limit = c.T;
   a.w13 = w13;
   a.w13_scale = w13_scale;
   a.w2 = w2;
@@ -245,6 +256,27 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_ro
   a.part = at<float>(ws, L.part);
   MOE_HIP(launch_expert_ffn(a, static_cast<hipStream_t>(stream)), "expert_ffn");
   return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_rows, int32_t inter,
+                          const int32_t* offsets, const void* x_rows, const float* x_scale,
+                          const void* w13, const float* w13_scale, const void* w2,
+                          const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return expert_ffn("moe_expert_ffn", cfg, n_experts, n_rows, inter, offsets, nullptr, x_rows, x_scale,
+                    w13, w13_scale, w2, w2_scale, y_rows, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_ffn_gather(const moe_config* cfg, int32_t n_experts, int32_t n_rows,
+                                 int32_t inter, const int32_t* offsets, const int32_t* sorted_pair,
+                                 const void* x, const float* x_scale, const void* w13,
+                                 const float* w13_scale, const void* w2, const float* w2_scale,
+                                 void* y_rows, void* ws, size_t ws_bytes, void* stream) {
+  if (!sorted_pair) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_gather: NULL buffer");
+  return expert_ffn("moe_expert_ffn_gather", cfg, n_experts, n_rows, inter, offsets, sorted_pair, x,
+                    x_scale, w13, w13_scale, w2, w2_scale, y_rows, ws, ws_bytes, stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const float* topk_weights,

@@ -27,6 +27,8 @@ struct GemmArgs {
   float* c_scale;       // fp8 GLU output: [rows][N_out/128]
   int c_scale_ld;
   const int32_t* offsets;
+  const int32_t* a_rows;  // gathered A rows (Linear-1 on the activations in place), or nullptr
+  int a_div, a_limit;     // grouped row i reads A row min(a_rows[i] / a_div, a_limit - 1)
   const int32_t* tp;
   int32_t* queue;       // kQueues tile counters (zeroed by the tile builder)
   int32_t* split_cnt;   // kMaxSplitItems arrival counters of K-split tiles (zeroed by the tile builder)
@@ -191,6 +193,27 @@ __device__ __forceinline__ TileInfo decode_tile(int t, const int* tp, const Gemm
   const int mv = seg1 - ti.row0;
   ti.mvalid = mv < BM ? mv : BM;
   return ti;
+}
+
+// A operand rows. Plain (a_rows == nullptr): grouped row i is A row i. Gathered: grouped row i is
+// A row a_rows[i] / a_div. With A = the [T,H] activations, a_rows = the expert-sorted pair list
+// and a_div = K that is the token of pair a_rows[i], so Linear-1 reads the tokens where they are
+// and no permuted copy of the activations is written or read ("MoE 优化的探索：从 MiniMax-01、
+// Comet、FlashMoE 到 DeepSeek-V4", 3.6.2: the dispatch can feed the first GEMM directly).
+// The row is clamped into A, so a corrupt list cannot read outside it.
+// a_base: base of the tile's A rows (uniform); a_row(r): row of tile row r (r < mvalid) from it.
+// Byte offsets from the base are formed in 32 bits: the host only gathers from A below 4 GiB.
+__device__ __forceinline__ const uint8_t* a_base(const GemmArgs& g, const TileInfo& ti) {
+  return g.a_rows ? g.A : g.A + (size_t)ti.row0 * g.lda;
+}
+__device__ __forceinline__ int a_row(const GemmArgs& g, const TileInfo& ti, int r) {
+  if (!g.a_rows) return r;
+  const unsigned v = (unsigned)g.a_rows[ti.row0 + r] / (unsigned)g.a_div;
+  return v < (unsigned)g.a_limit ? (int)v : g.a_limit - 1;
+}
+// The fp8 row scales [rows][a_scale_ld] follow the same rows.
+__device__ __forceinline__ const float* a_scale_base(const GemmArgs& g, const TileInfo& ti) {
+  return g.a_rows ? g.a_scale : g.a_scale + (size_t)ti.row0 * g.a_scale_ld;
 }
 
 // Weight row held in row r of the B tile. GLU (Linear-1): 32-row blocks alternate gate / up,

@@ -98,6 +98,8 @@ struct FfnArgs {
   const int32_t* offsets = nullptr;
   const void* x = nullptr;
   const float* x_scale = nullptr;
+  const int32_t* x_rows_index = nullptr;  // Linear-1 gathers row i from x row x_rows_index[i] / x_rows_div
+  int x_rows_div = 1, x_rows_limit = 0;
   const void* w13 = nullptr;
   const float* w13_scale = nullptr;
   const void* w2 = nullptr;

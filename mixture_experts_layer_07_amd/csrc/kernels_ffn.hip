@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
   for (int t = xcd_local_id(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
     const TileInfo ti = decode_tile(t, tp, g, BM);
     const int ra_ = lr < ti.mvalid ? lr : ti.mvalid - 1;
-    const float* pa = reinterpret_cast<const float*>(g.A + (size_t)(ti.row0 + ra_) * g.lda);
+    const float* pa = reinterpret_cast<const float*>(a_base(g, ti) + (size_t)a_row(g, ti, ra_) * g.lda);
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
     const float* pg;
     const float* pu = nullptr;
@@ -134,6 +134,12 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
   const int H = a.H, I = a.I;
   GemmArgs g1{}, g2{};
   g1.offsets = g2.offsets = a.offsets;
+  // Linear-1 may gather its rows from the activations; Linear-2 reads h in grouped order
+  g1.a_rows = a.x_rows_index;
+  g1.a_div = a.x_rows_div;
+  g1.a_limit = a.x_rows_limit;
+  g2.a_rows = nullptr;
+  g2.a_div = g2.a_limit = 1;
   g1.tp = g2.tp = a.tiles;
   g1.queue = a.tiles + kTileQueueOffset;
   g2.queue = a.tiles + kTileQueueOffset + kQueues;

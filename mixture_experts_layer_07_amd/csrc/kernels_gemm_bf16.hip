@@ -66,14 +66,14 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) 
   for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
     const TileInfo ti = decode_tile(t, tp, g, BM);
     const bool rows_here = wm * WM < ti.mvalid;  // waves past the expert's last row skip the MFMAs
-    const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
+    const uint8_t* Ab = a_base(g, ti);
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
     TileDma<AJ> da;
     TileDma<BJ> db;
 #pragma unroll
     for (int j = 0; j < AJ; ++j) {
       const int r = dma_row<NW>(j, wave, lane);
-      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
       da.off[j] = (uint32_t)rr * (uint32_t)g.lda + (uint32_t)dma_chunk(r, lane) * 16u;
     }
 #pragma unroll
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
     ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
     const int k0 = __builtin_amdgcn_readfirstlane(w.k0), k1 = __builtin_amdgcn_readfirstlane(w.k1);
     const int arows = (ti.mvalid + 7) & ~7;  // A rows fetched (8 rows per load instruction)
-    const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
+    const uint8_t* Ab = a_base(g, ti);
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
     uint32_t oa[8], ob[8];
     int la_off[8];
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
       const int r = (j * 4 + wave) * 8 + (lane >> 3);
       const uint32_t ch = (uint32_t)dma_chunk(r, lane) * 16u;
       const bool live = (j * 4 + wave) * 8 < arows;  // wave-uniform
-      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      const int rr = live ? a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1) : 0;
       oa[j] = live ? (uint32_t)rr * (uint32_t)g.lda + ch : 0u;
       la_off[j] = live ? (j * 4 + wave) * 64 : w4::kSink;
       ob[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + ch;

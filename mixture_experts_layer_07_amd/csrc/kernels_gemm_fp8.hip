@@ -86,14 +86,14 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
   for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
     const TileInfo ti = decode_tile(t, tp, g, BM);
     const bool rows_here = wm * WM < ti.mvalid;  // waves past the expert's last row skip the MFMAs
-    const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
+    const uint8_t* Ab = a_base(g, ti);
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
     TileDma<AJ> da;
     TileDma<BJ> db;
 #pragma unroll
     for (int j = 0; j < AJ; ++j) {
       const int r = dma_row<NW>(j, wave, lane);
-      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
       da.off[j] = (uint32_t)rr * (uint32_t)g.lda + (uint32_t)dma_chunk(r, lane) * 16u;
     }
 #pragma unroll
@@ -102,11 +102,11 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
       db.off[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + (uint32_t)dma_chunk(r, lane) * 16u;
     }
     // row scales: wave w < SAW loads rows 64w + lane (clamped) for the K step
-    const uint8_t* sab = reinterpret_cast<const uint8_t*>(g.a_scale + (size_t)ti.row0 * g.a_scale_ld);
+    const uint8_t* sab = reinterpret_cast<const uint8_t*>(a_scale_base(g, ti));
     uint32_t soff = 0;
     {
       const int r = wave * 64 + lane;
-      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
       soff = (uint32_t)rr * (uint32_t)g.a_scale_ld * 4u;
     }
     const float* psb[NB];
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_w8(GemmArgs g) {
     ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
     ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
     const int arows = (ti.mvalid + 7) & ~7;
-    const uint8_t* Ab = g.A + (size_t)ti.row0 * g.lda;
+    const uint8_t* Ab = a_base(g, ti);
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
     uint32_t oa[4], ob[4];
     int la_off[4];
@@ -457,17 +457,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm_fp8_w8(GemmArgs g) {
       const int r = (j * 8 + wave) * 8 + (lane >> 3);
       const uint32_t ch = (uint32_t)dma_chunk(r, lane) * 16u;
       const bool live = (j * 8 + wave) * 8 < arows;  // wave-uniform
-      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      const int rr = live ? a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1) : 0;
       oa[j] = live ? (uint32_t)rr * (uint32_t)g.lda + ch : 0u;
       la_off[j] = live ? (j * 8 + wave) * 64 : f8::kSink;
       ob[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + ch;
     }
     // row scales: wave w < 4 loads rows 64w + lane (clamped) of each step
-    const uint8_t* sab = reinterpret_cast<const uint8_t*>(g.a_scale + (size_t)ti.row0 * g.a_scale_ld);
+    const uint8_t* sab = reinterpret_cast<const uint8_t*>(a_scale_base(g, ti));
     uint32_t soff;
     {
       const int r = wave * 64 + lane;
-      const int rr = r < ti.mvalid ? r : ti.mvalid - 1;
+      const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
       soff = (uint32_t)rr * (uint32_t)g.a_scale_ld * 4u;
     }
     if (arows < BM) {  // zero the A rows that are not fetched, in both stages

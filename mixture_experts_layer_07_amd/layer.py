@@ -1,8 +1,11 @@
-"""One MoE layer forward on torch device buffers: the four C-ABI calls in order.
+"""One MoE layer forward on torch device buffers: the C-ABI calls in order.
 
 route -> permute -> expert FFN (routed experts, then the shared expert if any) -> combine.
-Buffers are allocated once at construction and reused by every forward; the calls are
-enqueued on the current stream and none of them waits.
+With gather=True (the default) the permute stage only builds the pair order (and, for fp8,
+quantises the T input rows once) and Linear-1 of the routed experts reads the token rows in
+place (moe_expert_ffn_gather); with gather=False the permute stage also writes the permuted
+copy x_perm that moe_expert_ffn reads. Buffers are allocated once at construction and reused by
+every forward; the calls are enqueued on the current stream and none of them waits.
 """
 import torch
 
@@ -11,9 +14,11 @@ from .configs import LayerConfig
 
 
 class MoELayer:
-    def __init__(self, cfg: LayerConfig, w_router, bias, experts, shared=None, device="cuda"):
+    def __init__(self, cfg: LayerConfig, w_router, bias, experts, shared=None, device="cuda",
+                 gather=True):
         """experts / shared: dicts with w13, w2 (+ w13_scale, w2_scale for fp8) on `device`."""
         self.cfg = cfg
+        self.gather = gather
         self.c = B.make_config(cfg)
         B.moe_check_config(self.c)
         T, H, E, K, P = cfg.T, cfg.H, cfg.E, cfg.K, cfg.P
@@ -33,9 +38,16 @@ class MoELayer:
         self.offsets = torch.empty(E + 1, **i32)
         self.sorted_pair = torch.empty(P, **i32)
         self.pair_pos = torch.empty(P, **i32)
-        self.x_perm = torch.empty((P, H), dtype=torch.uint8 if self.fp8 else act, device=dev)
-        self.x_perm_scale = (torch.empty((P, H // 128), dtype=torch.float32, device=dev)
-                             if self.fp8 else None)
+        self.x_perm = self.x_perm_scale = None
+        if not gather:
+            self.x_perm = torch.empty((P, H), dtype=torch.uint8 if self.fp8 else act, device=dev)
+            if self.fp8:
+                self.x_perm_scale = torch.empty((P, H // 128), dtype=torch.float32, device=dev)
+        self.xq = self.xq_scale = None
+        if self.fp8 and (gather or self.shared is not None):
+            # the e4m3 codes of the T input rows, read by the gathered Linear-1 and the shared expert
+            self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+            self.xq_scale = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
         # expert outputs: fp32 accumulators for fp32 / bf16 layers, bf16 for the fp8 layer
         ydt = torch.bfloat16 if self.fp8 else torch.float32
         self.y_perm = torch.empty((P, H), dtype=ydt, device=dev)
@@ -43,9 +55,6 @@ class MoELayer:
         if self.shared is not None:
             self.y_shared = torch.empty((T, H), dtype=ydt, device=dev)
             self.shared_offsets = torch.tensor([0, T], **i32)
-            if self.fp8:
-                self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
-                self.xq_scale = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
         else:
             self.y_shared = None
 
@@ -53,14 +62,26 @@ class MoELayer:
         B.moe_route(self.c, x, self.w_router, self.bias, self.topk_ids, self.topk_weights, self.ws)
 
     def permute(self, x):
-        B.moe_permute(self.c, self.topk_ids, self.counts, self.offsets, self.sorted_pair,
-                      self.pair_pos, x, self.x_perm, self.x_perm_scale, self.ws)
+        if self.gather:
+            B.moe_permute(self.c, self.topk_ids, self.counts, self.offsets, self.sorted_pair,
+                          self.pair_pos, None, None, None, self.ws)
+            if self.fp8:
+                B.moe_quantize_fp8(self.cfg.T, self.cfg.H, x, self.xq, self.xq_scale)
+        else:
+            B.moe_permute(self.c, self.topk_ids, self.counts, self.offsets, self.sorted_pair,
+                          self.pair_pos, x, self.x_perm, self.x_perm_scale, self.ws)
 
-    def expert_ffn(self):
+    def expert_ffn(self, x):
         ex = self.experts
-        B.moe_expert_ffn(self.c, self.cfg.E, self.cfg.P, self.cfg.I, self.offsets, self.x_perm,
-                         self.x_perm_scale, ex["w13"], ex.get("w13_scale"), ex["w2"],
-                         ex.get("w2_scale"), self.y_perm, self.ws)
+        if self.gather:
+            xs, xs_scale = (self.xq, self.xq_scale) if self.fp8 else (x, None)
+            B.moe_expert_ffn_gather(self.c, self.cfg.E, self.cfg.P, self.cfg.I, self.offsets,
+                                    self.sorted_pair, xs, xs_scale, ex["w13"], ex.get("w13_scale"),
+                                    ex["w2"], ex.get("w2_scale"), self.y_perm, self.ws)
+        else:
+            B.moe_expert_ffn(self.c, self.cfg.E, self.cfg.P, self.cfg.I, self.offsets, self.x_perm,
+                             self.x_perm_scale, ex["w13"], ex.get("w13_scale"), ex["w2"],
+                             ex.get("w2_scale"), self.y_perm, self.ws)
 
     def shared_ffn(self, x):
         if self.shared is None:
@@ -68,7 +89,8 @@ class MoELayer:
         sh = self.shared
         xs, xs_scale = x, None
         if self.fp8:
-            B.moe_quantize_fp8(self.cfg.T, self.cfg.H, x, self.xq, self.xq_scale)
+            if not self.gather:  # (with gather the permute stage has quantised x already)
+                B.moe_quantize_fp8(self.cfg.T, self.cfg.H, x, self.xq, self.xq_scale)
             xs, xs_scale = self.xq, self.xq_scale
         B.moe_expert_ffn(self.c, 1, self.cfg.T, self.cfg.I_shared, self.shared_offsets, xs, xs_scale,
                          sh["w13"], sh.get("w13_scale"), sh["w2"], sh.get("w2_scale"),
@@ -80,7 +102,7 @@ class MoELayer:
     def forward(self, x):
         self.route(x)
         self.permute(x)
-        self.expert_ffn()
+        self.expert_ffn(x)
         self.shared_ffn(x)
         self.combine()
         return self.out

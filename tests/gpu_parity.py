@@ -42,7 +42,7 @@ def row_err(got, ref):
 class Case:
     """A layer config with its inputs on the GPU (expert weights drawn on `wdev`)."""
 
-    def __init__(self, cfg, bias=None, wdev="cpu", dev="cuda"):
+    def __init__(self, cfg, bias=None, wdev="cpu", dev="cuda", gather=True):
         self.cfg = cfg
         self.dev = dev
         x, w_r, b = make_router_inputs(cfg)
@@ -58,7 +58,7 @@ class Case:
             self.sh = None
         clean = lambda d: None if d is None else {k: v for k, v in d.items() if v is not None}  # noqa: E731
         self.layer = MoELayer(cfg, w_r.to(dev), None if b is None else b.to(dev), clean(self.ex),
-                              clean(self.sh), dev)
+                              clean(self.sh), dev, gather=gather)
         self.xd = x.to(dev)
 
     def run(self):
@@ -151,6 +151,15 @@ def check_permute(case, ids_g, rows=None):
     assert (L.pair_pos.cpu().numpy() == pp).all()
     sel = np.arange(c.P) if rows is None else np.asarray(rows)
     src_tok = sp[sel] // c.K
+    if L.gather:
+        # no permuted copy: Linear-1 reads x (fp8: the codes of the T rows) in place
+        if c.dtype == "fp8":
+            toks = np.unique(src_tok)
+            codes, scales = orc.quantize_rows_fp8(case.x[torch.from_numpy(toks)].float().numpy())
+            ti = torch.from_numpy(toks).to(L.xq.device)
+            assert (L.xq_scale[ti].cpu().numpy() == scales).all(), "fp8 activation scales differ"
+            assert (L.xq[ti].cpu().numpy() == codes).all(), "fp8 activation codes differ"
+        return counts, offsets, sp, pp
     idx = torch.from_numpy(sel).to(L.x_perm.device)
     if c.dtype == "fp8":
         codes, scales = orc.quantize_rows_fp8(case.x[torch.from_numpy(src_tok)].float().numpy())
@@ -171,10 +180,15 @@ def check_ffn(case, offsets, rows, report):
     c = case.cfg
     L = case.layer
     rows = np.asarray(rows)
-    idx = torch.from_numpy(rows).to(L.x_perm.device)
-    if c.dtype == "fp8":
+    if L.gather:
+        # the row's token, through the same (bit-exact checked) fp8 quantisation for fp8 layers
+        sp = L.sorted_pair.cpu().numpy()
+        xr = case.x_hat(sp[rows] // c.K)
+    elif c.dtype == "fp8":
+        idx = torch.from_numpy(rows).to(L.x_perm.device)
         xr = orc.dequantize_rows_fp8(L.x_perm[idx].cpu().numpy(), L.x_perm_scale[idx].cpu().numpy())
     else:
+        idx = torch.from_numpy(rows).to(L.x_perm.device)
         xr = L.x_perm[idx].cpu().double().numpy()
     owner = np.searchsorted(np.asarray(offsets), rows, side="right") - 1
     ref = expert_rows(case, xr, owner)

@@ -15,7 +15,7 @@ from mixture_experts_layer_07_amd.configs import CONFIGS
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from gpu_parity import Case, check_ffn, full_check, row_err, sample_rows  # noqa: E402
+    from gpu_parity import Case, check_ffn, full_check, row_err, rows_of, sample_rows  # noqa: E402
 
 
 def zipf_bias(E, s=1.2, seed=0, scale=0.15):
@@ -37,11 +37,14 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("gather", [True, False], ids=["gather", "x_perm"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_layer_parity(name):
+def test_small_layer_parity(name, gather):
+    """gather: Linear-1 reads the token rows in place (the benchmarked path); x_perm: the permute
+    stage writes the permuted copy that Linear-1 reads."""
     cfg, bias = SMALL[name]
     b = zipf_bias(cfg.E) if bias == "zipf" else None
-    case = Case(cfg, bias=b)
+    case = Case(cfg, bias=b, gather=gather)
     rep = full_check(case)
     print(name, rep)
 
@@ -72,7 +75,7 @@ def test_permute_skewed_ids_and_ragged_experts():
     ids = torch.stack([torch.full_like(t, 3), torch.where(t % 3 == 0, 5, 15)], 1).to(torch.int32)
     L.topk_ids.copy_(ids)
     L.permute(case.xd)
-    L.expert_ffn()
+    L.expert_ffn(case.xd)
     torch.cuda.synchronize()
     counts, offsets, sp, pp = orc.permute(ids.numpy(), cfg.E)
     assert (L.offsets.cpu().numpy() == offsets).all()
@@ -94,8 +97,9 @@ def _skewed_ids(T, counts):
     return ids
 
 
+@pytest.mark.parametrize("gather", [True, False], ids=["gather", "x_perm"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_large_tile_paths(dtype):
+def test_large_tile_paths(dtype, gather):
     """Row groups that select the 256 x 256-tile kernels and every valid-row height of their last
     m-tile (full, <= 128, <= 64, <= 32 rows), with caller-supplied ids; sampled rows of every
     expert against the oracle."""
@@ -103,12 +107,12 @@ def test_large_tile_paths(dtype):
     cfg = base.scaled(T=2048, H=256, I=2048, E=8, K=2, score="softmax", renorm=True, route_scale=1.0,
                       n_group=1, topk_group=1, bias=None, I_shared=0)
     counts = [2000, 800, 500, 300, 220, 150, 90, 36]   # last m-tiles: 208, 32, 244, 44, 220, 150, 90, 36
-    case = Case(cfg)
+    case = Case(cfg, gather=gather)
     L = case.layer
     ids = _skewed_ids(cfg.T, counts)
     L.topk_ids.copy_(ids)
     L.permute(case.xd)
-    L.expert_ffn()
+    L.expert_ffn(case.xd)
     torch.cuda.synchronize()
     _, offsets, _, _ = orc.permute(ids.numpy(), cfg.E)
     assert (np.diff(offsets) == counts).all()
@@ -161,11 +165,13 @@ def test_quantize_fp8_bit_exact():
 FULL = [1, 2, 3, 4, 5]
 
 
-@pytest.mark.parametrize("cid", FULL)
-def test_full_size_parity(cid):
-    """Real workload sizes: exact routing / permutation; sampled expert rows and tokens."""
+@pytest.mark.parametrize("cid,gather", [(c, True) for c in FULL] + [(3, False), (5, False)],
+                         ids=[f"{c}-gather" for c in FULL] + ["3-x_perm", "5-x_perm"])
+def test_full_size_parity(cid, gather):
+    """Real workload sizes: exact routing / permutation; sampled expert rows and tokens. The
+    gathered path is the one the benchmark times."""
     cfg = CONFIGS[cid]
-    case = Case(cfg, wdev="cuda")
+    case = Case(cfg, wdev="cuda", gather=gather)
     rng = np.random.default_rng(cid)
     case.run()
     from gpu_parity import (check_combine, check_end_to_end, check_permute, check_route,
@@ -185,3 +191,26 @@ def test_full_size_parity(cid):
     check_combine(case, pp, w_g, toks, rep)
     check_end_to_end(case, ids_g, w_g, toks, rep)
     print(cfg.name, rep, "empty experts:", int((counts == 0).sum()), "max count:", int(counts.max()))
+
+
+def test_gather_clamps_rows_outside_the_activations():
+    """moe_expert_ffn_gather with pair ids past T*K: those rows read the last token (clamped),
+    every other row its own token."""
+    cfg = CONFIGS[2].scaled(T=80, H=256, I=256, E=4, K=2)
+    case = Case(cfg)
+    L = case.layer
+    case.run()
+    torch.cuda.synchronize()
+    sp = L.sorted_pair.clone()
+    sp[3] = cfg.P + 1000
+    sp[cfg.P - 1] = 2 ** 31 - 1
+    L.sorted_pair.copy_(sp)
+    L.expert_ffn(case.xd)
+    torch.cuda.synchronize()
+    offsets = L.offsets.cpu().numpy()
+    rows = np.array([0, 3, 4, cfg.P - 2, cfg.P - 1])
+    tok = np.minimum(sp.cpu().numpy()[rows].astype(np.int64) // cfg.K, cfg.T - 1)
+    owner = np.searchsorted(offsets, rows, side="right") - 1
+    from gpu_parity import assert_rows, expert_rows
+    ref = expert_rows(case, case.x_hat(tok), owner)
+    assert_rows(rows_of(L.y_perm, rows), ref, 2e-2, "clamped", {})
