@@ -5,9 +5,9 @@
 // expert function from "MoE 路由入门：从 Dense FFN 到 GroupedTopK", section 1).
 //
 // Persistent grid over the expert-major tile list (gemm_common.h); per tile a K loop of
-// 64-channel steps: direct-to-LDS loads of step k+1 into one LDS stage while the MFMAs of step
-// k read the other, one barrier per step. Inside a step the operand fragments of sub-step s+1
-// are read from LDS while the MFMAs of sub-step s run.
+// 64-channel steps through two LDS stages, one barrier per step (the 256 x 256 kernel below
+// describes its pipeline). Inside a step the operand fragments of sub-step s+1 are read from LDS
+// while the MFMAs of sub-step s run.
 #include "gemm_common.h"
 
 namespace moe {
@@ -150,14 +150,25 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) 
 
 
 // ============================================================================ 256 x 256 tiles
-// Four waves, one per SIMD. K advances 64 channels per step through two LDS stages (A 256 rows +
-// B 256 rows of 128 bytes = full cache lines, plus a 1 KiB sink), filled by direct-to-LDS loads.
+// Four waves, one per SIMD. K advances 64 channels per step through two LDS stages, each an A
+// array (256 rows of 128 bytes = full cache lines, plus a 1 KiB sink) and a B array (256 weight
+// rows); A and B are separate arrays so that the compiler's tracking of direct-to-LDS writes
+// never confuses the two. A is filled by direct-to-LDS loads one step ahead. The weights, whose
+// first touch comes from HBM, stream through registers two steps ahead: each lane loads its 8
+// chunks of step k+3 with plain 16-byte loads spread over the MFMAs of step k, and writes the
+// chunks of step k+2 (loaded during step k-1) into the stage released in step k. Spread over the
+// step, the loads never queue up behind one another at the address unit, and a weight load has
+// one to two steps to arrive.
 // Within step k:
-//   sub-steps 0..2: MFMAs of sub-step s while the fragments of s+1 are read;
-//   then: this wave's reads of the stage are complete and its loads of step k+1 have landed;
-//         a workgroup barrier (no memory fence: the waits are explicit) extends both to all waves;
-//   sub-step 3: MFMAs while the first fragments of step k+1 are read and the loads of step k+2
-//         go into the stage just released.
+//   sub-steps 0..2: MFMAs of sub-step s while the fragments of s+1 are read and the weight loads
+//         of step k+3 are issued;
+//   then: this wave's LDS reads and writes are complete and its A loads of step k+1 and weight
+//         loads of step k+2 have landed (only the weight loads of step k+3 may be outstanding);
+//         a workgroup barrier (no memory fence: the waits are explicit) extends this to all waves;
+//   sub-step 3: MFMAs while the first fragments of step k+1 are read, the weights of step k+2
+//         are written and the A loads of step k+2 go into the stage just released.
+// The first two steps of a tile are loaded straight into the stages, the weights of the third
+// into registers, so a tile starts after one round trip.
 // The wave layout follows the tile's valid rows h (the last m-tile of an expert is ragged):
 //   h > 128: 2 x 2 waves of 128 x 128 (16 accumulators of 32 x 32 each);
 //   h <= 128, 64, 32: 1 x 4 waves of h' x 64 (h' = 128, 64, 32), so that the MFMA work follows
@@ -166,17 +177,18 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) 
 // sink, and their LDS rows are zeroed once per tile (a zero operand also draws less power in the
 // MFMA pipes). Accumulators of rows past h are never stored.
 namespace w4 {
-constexpr int kStage = 4096 + 64;  // u32x4 per stage: A 2048 + B 2048 + 64 (sink)
-constexpr int kSink = 4096;
+constexpr int kStageA = 2048 + 64;  // u32x4 per A stage: 256 rows of 8 chunks + 64 (sink)
+constexpr int kSink = 2048;
+constexpr int kStageB = 2048;       // u32x4 per B stage
 
 // Fragments of sub-step ks: A rows r0 + 32 mb + (lane & 31), B rows c0 + 32 nb + (lane & 31).
 template <int MB, int NB>
-__device__ __forceinline__ void frags(const u32x4* st, int ks, int r0, int c0, int lane, bf16x8 (&a)[MB],
-                                      bf16x8 (&b)[NB]) {
+__device__ __forceinline__ void frags(const u32x4* sa, const u32x4* sb, int ks, int r0, int c0, int lane,
+                                      bf16x8 (&a)[MB], bf16x8 (&b)[NB]) {
   const int lrow = lane & 31, lk = lane >> 5;
   const int slot = (ks * 2 + lk) ^ lds_swz(lrow);  // block rows start at multiples of 32
-  const u32x4* la = st + (r0 + lrow) * 8 + slot;
-  const u32x4* lb = st + 2048 + (c0 + lrow) * 8 + slot;
+  const u32x4* la = sa + (r0 + lrow) * 8 + slot;
+  const u32x4* lb = sb + (c0 + lrow) * 8 + slot;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) a[mb] = __builtin_bit_cast(bf16x8, la[mb * 256]);
 #pragma unroll
@@ -276,63 +288,113 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, 
 }
 }  // namespace w4
 
-// Scheduling groups: 0x008 MFMA, 0x010 vector memory, 0x100 LDS read.
+// Scheduling groups: 0x008 MFMA, 0x010 vector memory, 0x100 LDS read, 0x200 LDS write.
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) for
+// "all LDS/scalar operations done and at most n vector memory operations outstanding". Written as
+// the builtin, the compiler's own wait insertion sees them and adds no waits of its own after.
+__host__ __device__ constexpr int wait_lgkm0_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0Vm8 = wait_lgkm0_vm(8), kWaitLgkm0Vm0 = wait_lgkm0_vm(0);
 #define MOE_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 
-// The direct-to-LDS loads of one step into `stage`: AJ_ of A (rows below 32 * AJ_; a path for
-// shorter tiles issues fewer) and 8 of B.
-#define MOE_W4_LOADS(stage, kk, AJ_)                                                             \
+// A of one step: AJ_ direct-to-LDS loads into `stage` (rows below 32 * AJ_; a path for shorter
+// tiles issues fewer; rows past the valid ones land in the sink).
+#define MOE_W4_ALOADS(stage, kk, AJ_)                                                            \
   do {                                                                                           \
     _Pragma("unroll") for (int j_ = 0; j_ < (AJ_); ++j_)                                         \
         dma_to_lds<16>(Ab + (oa[j_] + (uint32_t)(kk) * 128u), (stage) + la_off[j_]);            \
-    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_)                                             \
-        dma_to_lds<16>(Be + (ob[j_] + (uint32_t)(kk) * 128u), (stage) + 2048 + (j_ * 4 + wave) * 64); \
   } while (0)
 
-// A sub-step's MFMAs interleaved with the fragment reads of the next (pairs while both last).
-#define MOE_W4_SUB(MB_, NB_)                                                                     \
-  _Pragma("unroll") for (int i_ = 0; i_ < ((MB_) * (NB_) < (MB_) + (NB_) ? (MB_) * (NB_) : (MB_) + (NB_)); ++i_) { \
-    MOE_SGB(0x008, 1);                                                                           \
-    MOE_SGB(0x100, 1);                                                                           \
+// B (weights) of one step: 8 plain 16-byte loads per lane into registers R (the chunks a
+// direct-to-LDS load would bring), written to a stage later; the registers give the weight
+// stream a lead of two steps and let its loads spread over the step.
+#define MOE_W4_BLOAD(R, kk, J0, J1)                                                              \
+  do {                                                                                           \
+    _Pragma("unroll") for (int j_ = (J0); j_ < (J1); ++j_)                                       \
+        R[j_] = *reinterpret_cast<const u32x4*>(Be + (ob[j_] + (uint32_t)(kk) * 128u));          \
+  } while (0)
+// B of one step straight into a stage with direct-to-LDS loads (the first two steps of a tile).
+#define MOE_W4_BDMA(stage, kk)                                                                   \
+  do {                                                                                           \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_)                                             \
+        dma_to_lds<16>(Be + (ob[j_] + (uint32_t)(kk) * 128u), (stage) + j_ * 256 + wave * 64);   \
+  } while (0)
+#define MOE_W4_BWRITE(stage, R)                                                                  \
+  do {                                                                                           \
+    _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) (stage)[bw_off + j_ * 256] = R[j_];          \
+  } while (0)
+
+// One step on stage `cur` (k). LB: load the weights of step k+3 into RL during sub-steps 0-2;
+// W: after the barrier, write the weights of step k+2 (in RW) and issue the A loads of step k+2
+// into `cur`; NEXT: read the first fragments of `nxt`.
+#define MOE_W4_STEP(MB_, NB_, ca, cb, na, nb, k, LB, W, NEXT, RW, RL)                           \
+  w4::frags<MB_, NB_>(ca, cb, 1, r0, c0, lane, a1, b1);                                          \
+  if (LB) MOE_W4_BLOAD(RL, (k) + 3, 0, 3);                                                       \
+  w4::mfmas<MB_, NB_>(acc, a0, b0);                                                              \
+  MOE_W4_SUBL(MB_, NB_, LB, 3)                                                                   \
+  w4::frags<MB_, NB_>(ca, cb, 2, r0, c0, lane, a0, b0);                                          \
+  if (LB) MOE_W4_BLOAD(RL, (k) + 3, 3, 6);                                                       \
+  w4::mfmas<MB_, NB_>(acc, a1, b1);                                                              \
+  MOE_W4_SUBL(MB_, NB_, LB, 3)                                                                   \
+  w4::frags<MB_, NB_>(ca, cb, 3, r0, c0, lane, a1, b1);                                          \
+  if (LB) MOE_W4_BLOAD(RL, (k) + 3, 6, 8);                                                       \
+  w4::mfmas<MB_, NB_>(acc, a0, b0);                                                              \
+  MOE_W4_SUBL(MB_, NB_, LB, 2)                                                                   \
+  /* own fragment reads and weight writes done, A of step k+1 landed (only this step's weight \
+     loads may be outstanding); the barrier extends both to all waves */                       \
+  __builtin_amdgcn_s_waitcnt((LB) ? kWaitLgkm0Vm8 : kWaitLgkm0Vm0);                              \
+  __builtin_amdgcn_s_barrier();                                                                  \
+  __builtin_amdgcn_sched_barrier(0);                                                             \
+  if (NEXT) w4::frags<MB_, NB_>(na, nb, 0, r0, c0, lane, a0, b0);                                \
+  if (W) {                                                                                       \
+    MOE_W4_BWRITE(cb, RW);                                                                       \
+    MOE_W4_ALOADS(ca, (k) + 2, AJ);                                                              \
   }                                                                                              \
-  if ((MB_) * (NB_) > (MB_) + (NB_)) MOE_SGB(0x008, (MB_) * (NB_) - (MB_) - (NB_));              \
+  w4::mfmas<MB_, NB_>(acc, a1, b1);                                                              \
+  MOE_W4_POST(MB_, NB_, W, NEXT)                                                                 \
   __builtin_amdgcn_sched_barrier(0);
 
-// One step on stage `cur`; NEXT: read the first fragments of `nxt`; LOADS: refill `cur` with k+2.
-#define MOE_W4_STEP(MB_, NB_, cur, nxt, k, LOADS, NEXT)                                          \
-  w4::frags<MB_, NB_>(cur, 1, r0, c0, lane, a1, b1);                                             \
-  w4::mfmas<MB_, NB_>(acc, a0, b0);                                                              \
-  MOE_W4_SUB(MB_, NB_)                                                                           \
-  w4::frags<MB_, NB_>(cur, 2, r0, c0, lane, a0, b0);                                             \
-  w4::mfmas<MB_, NB_>(acc, a1, b1);                                                              \
-  MOE_W4_SUB(MB_, NB_)                                                                           \
-  w4::frags<MB_, NB_>(cur, 3, r0, c0, lane, a1, b1);                                             \
-  w4::mfmas<MB_, NB_>(acc, a0, b0);                                                              \
-  MOE_W4_SUB(MB_, NB_)                                                                           \
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");          \
-  __builtin_amdgcn_sched_barrier(0);                                                             \
-  if (NEXT) w4::frags<MB_, NB_>(nxt, 0, r0, c0, lane, a0, b0);                                   \
-  if (LOADS) MOE_W4_LOADS(cur, (k) + 2, (MB_) * (NB_) == 16 ? 8 : (MB_));                        \
-  w4::mfmas<MB_, NB_>(acc, a1, b1);                                                              \
-  if ((MB_) * (NB_) == 16) {                                                                     \
-    /* 16 MFMAs: the first 8 carry the next fragments, the last 8 the 16 loads */               \
-    if (NEXT) {                                                                                  \
-      _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x100, 1); } \
-    } else {                                                                                     \
-      MOE_SGB(0x008, 8);                                                                         \
+// Scheduling of a sub-step: its MFMAs, the fragment reads of the next sub-step one per MFMA, and
+// NL weight loads spread over the remaining MFMAs.
+#define MOE_W4_SUBL(MB_, NB_, LB, NL)                                                            \
+  {                                                                                              \
+    constexpr int nm_ = (MB_) * (NB_), nr_ = (MB_) + (NB_);                                      \
+    constexpr int pr_ = nm_ < nr_ ? nm_ : nr_;                                                   \
+    _Pragma("unroll") for (int i_ = 0; i_ < pr_; ++i_) {                                         \
+      MOE_SGB(0x008, 1);                                                                         \
+      MOE_SGB(0x100, 1);                                                                         \
     }                                                                                            \
-    if (LOADS) {                                                                                 \
-      _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) { MOE_SGB(0x008, 1); MOE_SGB(0x010, 2); } \
-    } else {                                                                                     \
-      MOE_SGB(0x008, 8);                                                                         \
+    if (LB) {                                                                                    \
+      _Pragma("unroll") for (int i_ = 0; i_ < (NL); ++i_) {                                      \
+        if (nm_ > pr_ + i_) MOE_SGB(0x008, 1);                                                   \
+        MOE_SGB(0x010, 1);                                                                       \
+      }                                                                                          \
+      if (nm_ > pr_ + (NL)) MOE_SGB(0x008, nm_ - pr_ - (NL));                                    \
+    } else if (nm_ > pr_) {                                                                      \
+      MOE_SGB(0x008, nm_ - pr_);                                                                 \
     }                                                                                            \
-  } else if (LOADS) {                                                                            \
-    /* few MFMAs: the loads go first */                                                          \
-    MOE_SGB(0x010, 8 + (MB_));                                                                   \
-  }                                                                                              \
-  __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+  }
+
+// After the barrier: MFMAs carry the next fragments' reads, then the weight writes and A loads.
+#define MOE_W4_POST(MB_, NB_, W, NEXT)                                                           \
+  {                                                                                              \
+    constexpr int nm_ = (MB_) * (NB_);                                                           \
+    constexpr int nr_ = (NEXT) ? ((MB_) + (NB_) < nm_ ? (MB_) + (NB_) : nm_) : 0;                \
+    constexpr int nw_ = (W) ? 8 : 0;                                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < nr_; ++i_) {                                         \
+      MOE_SGB(0x008, 1);                                                                         \
+      MOE_SGB(0x100, 1);                                                                         \
+    }                                                                                            \
+    _Pragma("unroll") for (int i_ = 0; i_ < nw_; ++i_) {                                         \
+      if (nr_ + i_ < nm_) MOE_SGB(0x008, 1);                                                     \
+      MOE_SGB(0x200, 1);                                                                         \
+      if (i_ < AJ) MOE_SGB(0x010, 1);                                                            \
+    }                                                                                            \
+    if (nr_ + nw_ < nm_) MOE_SGB(0x008, nm_ - nr_ - nw_);                                        \
+  }
 
 // One tile (or K piece of a tile) with waves of MB x NB blocks: rows r0.., weight rows c0...
+// Steps k0, k0+1 start in the two stages, the weights of k0+2 in registers RB0.
 #define MOE_W4_TILE(MB_, NB_, r0_, c0_, SPLIT)                                                   \
   {                                                                                              \
     const int r0 = (r0_), c0 = (c0_);                                                            \
@@ -341,21 +403,30 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, 
     _Pragma("unroll") for (int mb = 0; mb < (MB_); ++mb)                                         \
       _Pragma("unroll") for (int nb = 0; nb < (NB_); ++nb)                                       \
         _Pragma("unroll") for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;                     \
-    MOE_W4_LOADS(st0, k0, AJ);                                                                   \
-    MOE_W4_LOADS(st1, k0 + 1, AJ);                                                               \
-    /* wait for step k0's loads: the AJ + 8 of step k0 + 1 may still be in flight */             \
-    if (AJ == 8) asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
-    else if (AJ == 4) asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
-    else if (AJ == 2) asm volatile("s_waitcnt vmcnt(10)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
-    else asm volatile("s_waitcnt vmcnt(9)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  \
+    u32x4 RB0[8], RB1[8];                                                                        \
+    MOE_W4_ALOADS(sA0, k0, AJ);                                                                  \
+    MOE_W4_BDMA(sB0, k0);                                                                        \
+    MOE_W4_ALOADS(sA1, k0 + 1, AJ);                                                              \
+    MOE_W4_BDMA(sB1, k0 + 1);                                                                    \
+    /* (a two-step tile loads step k0+1 again: unused, keeps the wait count fixed) */           \
+    MOE_W4_BLOAD(RB0, k0 + 2 < k1 ? k0 + 2 : k1 - 1, 0, 8);                                      \
+    /* step k0 landed (step k0+1 and the weights of k0+2 may still be in flight) */             \
+    __builtin_amdgcn_s_waitcnt(wait_lgkm0_vm(AJ + 16));                                          \
+    __builtin_amdgcn_s_barrier();                                                                \
     bf16x8 a0[MB_], b0[NB_], a1[MB_], b1[NB_];                                                   \
-    w4::frags<MB_, NB_>(st0, 0, r0, c0, lane, a0, b0);                                           \
-    for (int k = k0; k < k1 - 2; k += 2) {                                                       \
-      MOE_W4_STEP(MB_, NB_, st0, st1, k, true, true)                                             \
-      MOE_W4_STEP(MB_, NB_, st1, st0, k + 1, true, true)                                         \
+    w4::frags<MB_, NB_>(sA0, sB0, 0, r0, c0, lane, a0, b0);                                      \
+    int k = k0;                                                                                  \
+    for (; k + 4 < k1; k += 2) {                                                                 \
+      MOE_W4_STEP(MB_, NB_, sA0, sB0, sA1, sB1, k, true, true, true, RB0, RB1)                             \
+      MOE_W4_STEP(MB_, NB_, sA1, sB1, sA0, sB0, k + 1, true, true, true, RB1, RB0)                         \
     }                                                                                            \
-    MOE_W4_STEP(MB_, NB_, st0, st1, k1 - 2, false, true)                                         \
-    MOE_W4_STEP(MB_, NB_, st1, st0, k1 - 1, false, false)                                        \
+    if (k + 4 == k1) {                                                                           \
+      MOE_W4_STEP(MB_, NB_, sA0, sB0, sA1, sB1, k, true, true, true, RB0, RB1)                             \
+      MOE_W4_STEP(MB_, NB_, sA1, sB1, sA0, sB0, k + 1, false, true, true, RB1, RB0)                        \
+      k += 2;                                                                                    \
+    }                                                                                            \
+    MOE_W4_STEP(MB_, NB_, sA0, sB0, sA1, sB1, k, false, false, true, RB0, RB1)                             \
+    MOE_W4_STEP(MB_, NB_, sA1, sB1, sA0, sB0, k + 1, false, false, false, RB1, RB0)                        \
     bool store = true;                                                                           \
     if (SPLIT && w.piece >= 0) {                                                                 \
       /* K piece: publish it; the last piece to arrive sums all of them in piece order */        \
@@ -380,8 +451,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, 
 template <bool GLU, bool OUTF32>
 __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   constexpr int BM = 256, BN = 256;
-  __shared__ u32x4 st0[w4::kStage];
-  __shared__ u32x4 st1[w4::kStage];
+  __shared__ u32x4 sA0[w4::kStageA];
+  __shared__ u32x4 sA1[w4::kStageA];
+  __shared__ u32x4 sB0[w4::kStageB];
+  __shared__ u32x4 sB1[w4::kStageB];
   __shared__ int tp[kMaxExperts + 1];
   __shared__ int s_slot[1];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -415,11 +488,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
       la_off[j] = live ? (j * 4 + wave) * 64 : w4::kSink;
       ob[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + ch;
     }
+    // LDS entry of this lane's weight chunk j: the slot a direct-to-LDS load of lane `lane` fills
+    // (row 32 j + 8 wave + lane / 8, the chunk that the swizzle puts there), + j * 256
+    const int bw_off = wave * 64 + lane;
     if (arows < BM) {  // zero the A rows that are not fetched, in both stages
       const u32x4 z = {0u, 0u, 0u, 0u};
       for (int i = arows * 8 + tid; i < BM * 8; i += 256) {
-        st0[i] = z;
-        st1[i] = z;
+        sA0[i] = z;
+        sA1[i] = z;
       }
     }
     // K pieces always take the 2 x 2 layout (their partial tiles share one shape)
