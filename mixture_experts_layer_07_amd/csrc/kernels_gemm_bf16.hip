@@ -12,143 +12,6 @@
 
 namespace moe {
 
-template <int MB, int NB, int WM, int WN, int ACH>
-__device__ __forceinline__ void mma_step_bf16(const u32x4* st, f32x16 (&acc)[MB][NB], int wm, int wn,
-                                              int lane) {
-  const int lrow = lane & 31, lk = lane >> 5, lsw = lds_swz(lrow);  // tile rows start at multiples of 32
-  const u32x4* la = st + (wm * WM + lrow) * 8;
-  const u32x4* lb = st + ACH + (wn * WN + lrow) * 8;
-  bf16x8 a[2][MB], b[2][NB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) a[0][mb] = __builtin_bit_cast(bf16x8, la[mb * 256 + (lk ^ lsw)]);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) b[0][nb] = __builtin_bit_cast(bf16x8, lb[nb * 256 + (lk ^ lsw)]);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int cur = ks & 1;
-    if (ks < 3) {
-      const int ch = ((ks + 1) * 2 + lk) ^ lsw;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) a[cur ^ 1][mb] = __builtin_bit_cast(bf16x8, la[mb * 256 + ch]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[cur ^ 1][nb] = __builtin_bit_cast(bf16x8, lb[nb * 256 + ch]);
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][mb], b[cur][nb], acc[mb][nb], 0, 0, 0);
-  }
-}
-
-// OUTF32 (plain GEMM only): store the fp32 accumulators instead of rounding them to bf16.
-template <int BM, int BN, int NWM, int NWN, bool GLU, int MINB, bool OUTF32>
-__global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_bf16(GemmArgs g) {
-  constexpr int NT = NWM * NWN * 64, NW = NWM * NWN;
-  constexpr int WM = BM / NWM, WN = BN / NWN, MB = WM / 32, NB = WN / 32;
-  constexpr int ACH = BM * 8, BCH = BN * 8;
-  constexpr int AJ = ACH / NT, BJ = BCH / NT;
-  static_assert(ACH % NT == 0 && BCH % NT == 0, "tile / thread mismatch");
-  static_assert(!GLU || NB % 2 == 0, "GLU needs gate/up block pairs per wave");
-  __shared__ u32x4 st0[ACH + BCH];
-  __shared__ u32x4 st1[ACH + BCH];
-  __shared__ int tp[kMaxExperts + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / NWN, wn = wave % NWN;
-  for (int i = tid; i <= g.n_exp; i += NT) tp[i] = g.tp[i];
-  __syncthreads();
-  const int total = tp[g.n_exp] * g.n_tiles_n;
-  const int KT = g.K / 64;
-  const int lrow = lane & 31, lk = lane >> 5;
-  __shared__ int s_slot[1];
-  const TileQueue tq = tile_queue(total);
-
-  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
-    const TileInfo ti = decode_tile(t, tp, g, BM);
-    const bool rows_here = wm * WM < ti.mvalid;  // waves past the expert's last row skip the MFMAs
-    const uint8_t* Ab = a_base(g, ti);
-    const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
-    TileDma<AJ> da;
-    TileDma<BJ> db;
-#pragma unroll
-    for (int j = 0; j < AJ; ++j) {
-      const int r = dma_row<NW>(j, wave, lane);
-      const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
-      da.off[j] = (uint32_t)rr * (uint32_t)g.lda + (uint32_t)dma_chunk(r, lane) * 16u;
-    }
-#pragma unroll
-    for (int j = 0; j < BJ; ++j) {
-      const int r = dma_row<NW>(j, wave, lane);
-      db.off[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + (uint32_t)dma_chunk(r, lane) * 16u;
-    }
-    f32x16 acc[MB][NB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-
-    MOE_DMA_ISSUE(AJ, NW, Ab, da, 0, st0, wave);
-    MOE_DMA_ISSUE(BJ, NW, Be, db, 0, st0 + ACH, wave);
-    dma_wait_and_barrier();
-    for (int kt = 0; kt + 1 < KT; kt += 2) {
-      MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt + 1) * 128u, st1, wave);
-      MOE_DMA_ISSUE(BJ, NW, Be, db, (uint32_t)(kt + 1) * 128u, st1 + ACH, wave);
-      if (rows_here) mma_step_bf16<MB, NB, WM, WN, ACH>(st0, acc, wm, wn, lane);
-      dma_wait_and_barrier();
-      if (kt + 2 < KT) {
-        MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt + 2) * 128u, st0, wave);
-        MOE_DMA_ISSUE(BJ, NW, Be, db, (uint32_t)(kt + 2) * 128u, st0 + ACH, wave);
-      }
-      if (rows_here) mma_step_bf16<MB, NB, WM, WN, ACH>(st1, acc, wm, wn, lane);
-      dma_wait_and_barrier();
-    }
-    if (KT & 1) {  // odd step count: the last step sits in the first stage
-      if (rows_here) mma_step_bf16<MB, NB, WM, WN, ACH>(st0, acc, wm, wn, lane);
-      dma_wait_and_barrier();
-    }
-    // epilogue (accumulator layout: lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4)
-    if (GLU) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int q = 0; q < NB / 2; ++q) {
-          const int col = ti.nt * (BN / 2) + (wn * (NB / 2) + q) * 32 + lrow;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
-            if (r < ti.mvalid) {
-              const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
-              reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(h);
-            }
-          }
-        }
-    } else {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = ti.nt * BN + wn * WN + nb * 32 + lrow;
-          if (col < g.N_out) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
-              if (r < ti.mvalid) {
-                uint8_t* p = g.C + (size_t)(ti.row0 + r) * g.ldc;
-                if (OUTF32)
-                  reinterpret_cast<float*>(p)[col] = acc[mb][nb][i];
-                else
-                  reinterpret_cast<uint16_t*>(p)[col] = f32_to_bf16(acc[mb][nb][i]);
-              }
-            }
-          }
-        }
-    }
-  }
-}
-
-
 // ============================================================================ 256 x 256 tiles
 // Four waves, one per SIMD. K advances 64 channels per step through two LDS stages, each an A
 // array (256 rows of 128 bytes = full cache lines, plus a 1 KiB sink) and a B array (256 weight
@@ -309,8 +172,11 @@ constexpr int kWaitLgkm0Vm8 = wait_lgkm0_vm(8), kWaitLgkm0Vm0 = wait_lgkm0_vm(0)
 // stream a lead of two steps and let its loads spread over the step.
 #define MOE_W4_BLOAD(R, kk, J0, J1)                                                              \
   do {                                                                                           \
-    _Pragma("unroll") for (int j_ = (J0); j_ < (J1); ++j_)                                       \
-        R[j_] = *reinterpret_cast<const u32x4*>(Be + (ob[j_] + (uint32_t)(kk) * 128u));          \
+    _Pragma("unroll") for (int j_ = (J0); j_ < (J1); ++j_) {                                     \
+      uint32_t o_ = ob[j_];                                                                      \
+      asm volatile("" : "+v"(o_));                                                               \
+      R[j_] = *reinterpret_cast<const u32x4*>(Be + (o_ + (uint32_t)(kk) * 128u));                \
+    }                                                                                            \
   } while (0)
 // B of one step straight into a stage with direct-to-LDS loads (the first two steps of a tile).
 #define MOE_W4_BDMA(stage, kk)                                                                   \
@@ -511,6 +377,74 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   }
 }
 
+// ============================================================================ 32 x 256 tiles
+// Decode-sized row groups (a few rows per expert): the same pipeline as the 256 x 256 kernel with
+// one row block per wave (1 x 4 waves of 32 x 64) and two workgroups per CU. Its cost is the
+// weight stream from HBM; the weights' two-step lead through registers keeps about 128 KiB in
+// flight per CU.
+namespace m32 {
+constexpr int kStageA = 256 + 64;  // 32 rows of 8 chunks + 64 (sink)
+constexpr int kSink = 256;
+}  // namespace m32
+
+template <bool GLU, bool OUTF32>
+__global__ __launch_bounds__(256, 2) void k_gemm_bf16_m32(GemmArgs g) {
+  constexpr int BM = 32, BN = 256;
+  __shared__ u32x4 sA0[m32::kStageA];
+  __shared__ u32x4 sA1[m32::kStageA];
+  __shared__ u32x4 sB0[w4::kStageB];
+  __shared__ u32x4 sB1[w4::kStageB];
+  __shared__ int tp[kMaxExperts + 1];
+  __shared__ int s_slot[1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i <= g.n_exp; i += 256) tp[i] = g.tp[i];
+  __syncthreads();
+  const int total = tp[g.n_exp] * g.n_tiles_n;
+  const int KT = g.K / 64;  // even
+  const TileQueue tq = tile_queue(total);
+  SplitQueue sq{};
+  sq.S = 1;
+  WorkItem w{};
+  w.piece = -1;
+
+  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
+    TileInfo ti = decode_tile(t, tp, g, BM);
+    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
+    ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
+    ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
+    ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
+    const int k0 = 0, k1 = KT;
+    const int arows = (ti.mvalid + 7) & ~7;
+    const uint8_t* Ab = a_base(g, ti);
+    const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
+    uint32_t oa[1], ob[8];
+    int la_off[1];
+    {
+      const int r = wave * 8 + (lane >> 3);
+      const uint32_t ch = (uint32_t)dma_chunk(r, lane) * 16u;
+      const bool live = wave * 8 < arows;  // wave-uniform
+      const int rr = live ? a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1) : 0;
+      oa[0] = live ? (uint32_t)rr * (uint32_t)g.lda + ch : 0u;
+      la_off[0] = live ? wave * 64 : m32::kSink;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (j * 4 + wave) * 8 + (lane >> 3);
+      ob[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + (uint32_t)dma_chunk(r, lane) * 16u;
+    }
+    const int bw_off = wave * 64 + lane;
+    if (arows < BM) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int i = arows * 8 + tid; i < BM * 8; i += 256) {
+        sA0[i] = z;
+        sA1[i] = z;
+      }
+    }
+    MOE_W4_TILE(1, 2, 0, wave * 64, false)
+  }
+}
+
 template <class K>
 static hipError_t launch_one(const char* name, K kernel, int grid, int threads, const GemmArgs& g,
                              hipStream_t s) {
@@ -530,10 +464,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& g1, const GemmArgs& g2, int variant,
     return launch_one("gemm_bf16_down", k_gemm_bf16_w4<false, true>, grid, 256, g2, s);
   }
   const int grid = round8(cus * 2);
-  if ((e = launch_one("gemm_bf16_gateup_swiglu_m32", k_gemm_bf16<32, 256, 1, 4, true, 2, false>, grid, 256,
-                      g1, s)) != hipSuccess)
+  if ((e = launch_one("gemm_bf16_gateup_swiglu_m32", k_gemm_bf16_m32<true, false>, grid, 256, g1, s)) != hipSuccess)
     return e;
-  return launch_one("gemm_bf16_down_m32", k_gemm_bf16<32, 256, 1, 4, false, 2, true>, grid, 256, g2, s);
+  return launch_one("gemm_bf16_down_m32", k_gemm_bf16_m32<false, true>, grid, 256, g2, s);
 }
 
 }  // namespace moe
