@@ -230,7 +230,7 @@ __device__ __forceinline__ int weight_row(int r, int nt, const GemmArgs& g) {
 }
 
 // SiLU(x) = x * sigmoid(x); the hardware exp's error is far below the bf16 / e4m3 rounding of h.
-__device__ __forceinline__ float silu_fast(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu_fast(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // LDS tile layout: rows of 128 bytes = 8 chunks of 16 bytes; chunk c of row r is stored at
 // position c ^ ((r >> 1) & 7). The LDS has 64 four-byte banks (256 bytes), so a 128-byte row
