@@ -8,8 +8,9 @@
 // Linear-1 output: h = SiLU(g) * u re-quantised per row per 128 columns ("SwiGLU / FP8 Cast",
 // "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", 5.1): the tile holds exactly
 // one such block (128 h columns), scale = absmax / 448, code = e4m3(h / scale).
-// Pipeline as in the bf16 kernels: direct-to-LDS loads (tiles and the row scales) into two
-// LDS stages, one barrier per K step.
+// Pipeline as in the bf16 kernels: two LDS stages, one barrier per K step; A and the row scales
+// arrive by direct-to-LDS loads one step ahead, the weights through registers two steps ahead
+// (128- and 32-row kernels) or by direct-to-LDS loads (256-row kernel).
 #include "gemm_common.h"
 
 namespace moe {
@@ -19,12 +20,13 @@ __device__ __forceinline__ i32x8 frag32(const u32x4* row, int c0, int c1) {
   return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
 
-template <int MB, int NB, int WM, int WN, int ACH>
-__device__ __forceinline__ void mma_step_fp8(const u32x4* st, const float* lsa, const float (&sb)[NB],
-                                             f32x16 (&acc)[MB][NB], int wm, int wn, int lane) {
+template <int MB, int NB, int WM, int WN>
+__device__ __forceinline__ void mma_step_fp8(const u32x4* sta, const u32x4* stb, const float* lsa,
+                                             const float (&sb)[NB], f32x16 (&acc)[MB][NB], int wm, int wn,
+                                             int lane) {
   const int lrow = lane & 31, lk = lane >> 5, lsw = lds_swz(lrow);  // tile rows start at multiples of 32
-  const u32x4* la = st + (wm * WM + lrow) * 8;
-  const u32x4* lb = st + ACH + (wn * WN + lrow) * 8;
+  const u32x4* la = sta + (wm * WM + lrow) * 8;
+  const u32x4* lb = stb + (wn * WN + lrow) * 8;
   i32x8 b0[NB], b1[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -57,6 +59,17 @@ __device__ __forceinline__ void mma_step_fp8(const u32x4* st, const float* lsa, 
   }
 }
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) for "all
+// LDS operations done and at most n vector memory operations outstanding"; as the builtin, the
+// compiler's own wait insertion accounts for it.
+__host__ __device__ constexpr int f8_wait_lgkm0_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+// 128- or 32-row tiles, NWM x NWN waves. One K step is 128 channels (one scale block) through two
+// LDS stages, each an A array, a B array and the step's row scales. A and the row scales are
+// filled by direct-to-LDS loads one step ahead; the weights stream through registers two steps
+// ahead: at the start of step k each thread writes the weight chunks of step k+1 (loaded during
+// step k-1) into the stage released at the end of step k-1, then issues the plain loads of step
+// k+2 into the same registers. One barrier per step, after its LDS reads.
 template <int BM, int BN, int NWM, int NWN, bool GLU, int MINB>
 __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
   constexpr int NT = NWM * NWN * 64, NW = NWM * NWN;
@@ -68,12 +81,15 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
   static_assert(ACH % NT == 0 && BCH % NT == 0, "tile / thread mismatch");
   static_assert(!GLU || (NB % 2 == 0 && BN == 256), "GLU needs gate/up pairs and 128 h columns");
   static_assert(SAW <= NW, "not enough waves for the row scales");
-  __shared__ u32x4 st0[ACH + BCH];
-  __shared__ u32x4 st1[ACH + BCH];
+  __shared__ u32x4 sA0[ACH];
+  __shared__ u32x4 sA1[ACH];
+  __shared__ u32x4 sB0[BCH];
+  __shared__ u32x4 sB1[BCH];
   __shared__ __attribute__((aligned(16))) float sa0[SAN];
   __shared__ __attribute__((aligned(16))) float sa1[SAN];
   __shared__ int tp[kMaxExperts + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / NWN, wn = wave % NWN;
   for (int i = tid; i <= g.n_exp; i += NT) tp[i] = g.tp[i];
   __syncthreads();
@@ -84,12 +100,16 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
   const TileQueue tq = tile_queue(total);
 
   for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
-    const TileInfo ti = decode_tile(t, tp, g, BM);
+    TileInfo ti = decode_tile(t, tp, g, BM);
+    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
+    ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
+    ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
+    ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
     const bool rows_here = wm * WM < ti.mvalid;  // waves past the expert's last row skip the MFMAs
     const uint8_t* Ab = a_base(g, ti);
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
     TileDma<AJ> da;
-    TileDma<BJ> db;
+    uint32_t ob[BJ];
 #pragma unroll
     for (int j = 0; j < AJ; ++j) {
       const int r = dma_row<NW>(j, wave, lane);
@@ -99,8 +119,10 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < BJ; ++j) {
       const int r = dma_row<NW>(j, wave, lane);
-      db.off[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + (uint32_t)dma_chunk(r, lane) * 16u;
+      ob[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + (uint32_t)dma_chunk(r, lane) * 16u;
     }
+    // the LDS entry a direct-to-LDS load of this lane fills for weight chunk j: + j * NT
+    const int bw_off = wave * 64 + lane;
     // row scales: wave w < SAW loads rows 64w + lane (clamped) for the K step
     const uint8_t* sab = reinterpret_cast<const uint8_t*>(a_scale_base(g, ti));
     uint32_t soff = 0;
@@ -109,12 +131,22 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
       const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
       soff = (uint32_t)rr * (uint32_t)g.a_scale_ld * 4u;
     }
+    // formed once per tile: the empty asm keeps the compiler from recomputing them (with the
+    // row lookups of a gathered A) inside the K loop
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) asm volatile("" : "+v"(da.off[j]));
+    asm volatile("" : "+v"(soff));
+    // weight block scales of this wave's column blocks: wave-uniform, read with scalar loads one
+    // step ahead
     const float* psb[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int wr = weight_row<GLU, BN>(wn * WN + nb * 32, ti.nt, g);
+      const int wr = __builtin_amdgcn_readfirstlane(weight_row<GLU, BN>(wn * WN + nb * 32, ti.nt, g));
       psb[nb] = g.b_scale + (size_t)ti.e * g.b_scale_exp + (size_t)(wr >> 7) * g.b_scale_ld;
     }
+    float sbA[NB], sbB[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sbA[nb] = psb[nb][0];
     f32x16 acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -122,44 +154,68 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+    u32x4 RB0[BJ], RB1[BJ];
 
-#define MOE_FP8_ISSUE(kt, st, sa)                                                                   \
+// A and row scales of step kt into (sta, ssa) with direct-to-LDS loads
+#define MOE_FP8_AISSUE(kt, sta, ssa)                                                                \
   do {                                                                                              \
-    MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt) * 128u, st, wave);                                 \
-    MOE_DMA_ISSUE(BJ, NW, Be, db, (uint32_t)(kt) * 128u, (st) + ACH, wave);                         \
-    if (wave < SAW)                                                                                 \
-      dma_to_lds<4>(sab + (soff + (uint32_t)(kt) * 4u), (sa) + wave * 64);                            \
+    MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt) * 128u, sta, wave);                                \
+    if (wave < SAW) dma_to_lds<4>(sab + (soff + (uint32_t)(kt) * 4u), (ssa) + wave * 64);           \
   } while (0)
-    MOE_FP8_ISSUE(0, st0, sa0);
-    dma_wait_and_barrier();
-    for (int kt = 0; kt + 1 < KT; kt += 2) {
-      MOE_FP8_ISSUE(kt + 1, st1, sa1);
-      {
-        float sb[NB];
+// weights of step kt (clamped into the loop) into registers R
+#define MOE_FP8_BLOAD(R, kt)                                                                        \
+  do {                                                                                              \
+    const uint32_t ko_ = (uint32_t)((kt) < KT ? (kt) : KT - 1) * 128u;                              \
+    _Pragma("unroll") for (int j_ = 0; j_ < BJ; ++j_) {                                             \
+      uint32_t o_ = ob[j_];                                                                         \
+      asm volatile("" : "+v"(o_));                                                                  \
+      R[j_] = *reinterpret_cast<const u32x4*>(Be + (o_ + ko_));                                     \
+    }                                                                                               \
+  } while (0)
+#define MOE_FP8_BWRITE(stb, R)                                                                      \
+  do {                                                                                              \
+    _Pragma("unroll") for (int j_ = 0; j_ < BJ; ++j_) (stb)[bw_off + j_ * NT] = R[j_];              \
+  } while (0)
+// step kt on stage (ca, cb, cs) with weight scales SB; the other stage (na, nb_, ns) receives
+// step kt+1 first, and SBN the weight scales of step kt+1
+#define MOE_FP8_STEP(kt, ca, cb, cs, na, nb_, ns, RW, SB, SBN)                                      \
+  {                                                                                                 \
+    {                                                                                               \
+      const int kn_ = (kt) + 1 < KT ? (kt) + 1 : (kt);                                              \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) SBN[nb] = psb[nb][kn_];                     \
+    }                                                                                               \
+    if ((kt) + 1 < KT) {                                                                            \
+      MOE_FP8_BWRITE(nb_, RW);                                                                      \
+      MOE_FP8_AISSUE((kt) + 1, na, ns);                                                             \
+    }                                                                                               \
+    MOE_FP8_BLOAD(RW, (kt) + 3);                                                                    \
+    if (rows_here) mma_step_fp8<MB, NB, WM, WN>(ca, cb, cs, SB, acc, wm, wn, lane);                 \
+    __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(BJ));                                               \
+    __builtin_amdgcn_s_barrier();                                                                   \
+  }
+    // prologue: step 0 straight into the first stage, the weights of steps 1 and 2 in registers
+    MOE_FP8_AISSUE(0, sA0, sa0);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sb[nb] = psb[nb][kt];
-        if (rows_here) mma_step_fp8<MB, NB, WM, WN, ACH>(st0, sa0, sb, acc, wm, wn, lane);
-      }
-      dma_wait_and_barrier();
-      if (kt + 2 < KT) MOE_FP8_ISSUE(kt + 2, st0, sa0);
-      {
-        float sb[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sb[nb] = psb[nb][kt + 1];
-        if (rows_here) mma_step_fp8<MB, NB, WM, WN, ACH>(st1, sa1, sb, acc, wm, wn, lane);
-      }
-      dma_wait_and_barrier();
+    for (int j = 0; j < BJ; ++j) dma_to_lds<16>(Be + ob[j], sB0 + (j * NW + wave) * 64);
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_FP8_BLOAD(RB1, 1);
+    MOE_FP8_BLOAD(RB0, 2);
+    // step 0 and the weights of step 1 landed: the loop's steady state, only the newest weight
+    // loads outstanding
+    __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(BJ));
+    __builtin_amdgcn_s_barrier();
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      MOE_FP8_STEP(kt, sA0, sB0, sa0, sA1, sB1, sa1, RB1, sbA, sbB)
+      MOE_FP8_STEP(kt + 1, sA1, sB1, sa1, sA0, sB0, sa0, RB0, sbB, sbA)
     }
-    if (KT & 1) {  // odd step count: the last step sits in the first stage
-      float sb[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sb[nb] = psb[nb][KT - 1];
-      if (rows_here) mma_step_fp8<MB, NB, WM, WN, ACH>(st0, sa0, sb, acc, wm, wn, lane);
-      dma_wait_and_barrier();
+    if (kt < KT) {  // odd step count: the last step sits in the first stage
+      MOE_FP8_STEP(kt, sA0, sB0, sa0, sA1, sB1, sa1, RB1, sbA, sbB)
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (GLU) {
       // per-row absmax over the tile's 128 h columns: lanes (32 columns) -> waves (through LDS)
-      float* red = reinterpret_cast<float*>(st0);  // [BM][NWN]; every wave is past the last read
+      float* red = reinterpret_cast<float*>(sA0);  // [BM][NWN]; every wave is past the last read
       float hv[MB][NB / 2][16];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
