@@ -228,10 +228,10 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
     if ((e = build_tiles(a, variant == 0 ? 256 : 32, a.tiles, s)) != hipSuccess) return e;
     return launch_gemm_bf16(g1, g2, variant, cus, s);
   }
-  // fp8: 256-row tiles for well-filled experts (few ragged tiles), 128-row tiles for moderately
-  // filled ones (a ragged last m-tile wastes less), 32-row tiles for decode-sized groups.
-  const int variant = avg >= 512 && enough(256) ? 0 : (avg >= 64 && enough(128) ? 2 : 1);
-  if ((e = build_tiles(a, variant == 0 ? 256 : (variant == 2 ? 128 : 32), a.tiles, s)) != hipSuccess) return e;
+  // 128-row tiles once experts average 64 rows (a 256-row fp8 kernel, eight waves with their
+  // accumulators in VGPRs for the block-scale promotion, measured slower everywhere), else 32.
+  const int variant = avg >= 64 && enough(128) ? 2 : 1;
+  if ((e = build_tiles(a, variant == 2 ? 128 : 32, a.tiles, s)) != hipSuccess) return e;
   return launch_gemm_fp8(g1, g2, variant, cus, s);
 }
 

@@ -9,8 +9,7 @@
 // "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", 5.1): the tile holds exactly
 // one such block (128 h columns), scale = absmax / 448, code = e4m3(h / scale).
 // Pipeline as in the bf16 kernels: two LDS stages, one barrier per K step; A and the row scales
-// arrive by direct-to-LDS loads one step ahead, the weights through registers two steps ahead
-// (128- and 32-row kernels) or by direct-to-LDS loads (256-row kernel).
+// arrive by direct-to-LDS loads one step ahead, the weights through registers two steps ahead.
 #include "gemm_common.h"
 
 namespace moe {
@@ -272,280 +271,6 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
   }
 }
 
-// ============================================================================ 256 x 256 tiles
-// Eight waves, two per SIMD, over 16 x 16 output blocks (MFMA 16x16x128: one instruction covers a
-// whole 128-channel scale block, so a block's partial sum needs no chaining). The accumulators
-// live in VGPRs: the block-scale promotion acc += partial * (row scale * weight block scale) runs
-// on the vector ALUs, which cannot address the accumulation registers. One K step is 128 channels
-// through two LDS stages (A 256 rows + B 256 rows of 128 bytes, a 1 KiB sink, the step's 256 A row
-// scales), filled by direct-to-LDS loads. Per step, row block rb = 0..RB-1: its A fragment and row
-// scales are read while row block rb-1 computes. The barrier sits after the last A reads of the
-// stage: then the loads of step k+2 go into it, the last row block computes, and the next stage's
-// fragments are read.
-// The wave layout follows the tile's valid rows h (the last m-tile of an expert is ragged):
-//   h > 128: 2 x 4 waves of 128 x 64 (8 x 4 blocks);
-//   h <= 128: 1 x 8 waves of 128 x 32 (8 x 2 blocks), so that MFMA work and A loads halve while
-//   the 256 weight rows stream once. In the Linear-1 (GLU) tile the two column blocks of a wave
-//   are 16 gate and the 16 matching up columns.
-namespace f8 {
-constexpr int kA = 0, kB = 2048, kSink = 4096, kScale = 4160, kStage = 4224;  // u32x4 offsets
-
-// (The lane id passes through an empty asm so that the swizzled LDS addresses are formed at each
-// use instead of being hoisted out of the loops and held, one register per address, across them.)
-// B fragments: weight-tile rows cbase[cb] + (lane & 15), channels 32 (lane >> 4) + 0..31.
-template <int CB>
-__device__ __forceinline__ void bfrags(const u32x4* st, const int (&cbase)[CB], int lane, i32x8 (&b)[CB]) {
-  asm volatile("" : "+v"(lane));
-  const int r = lane & 15, g = lane >> 4, sw = lds_swz(r);
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) b[cb] = frag32(st + kB + (cbase[cb] + r) * 8, (2 * g) ^ sw, (2 * g + 1) ^ sw);
-}
-
-// A fragment of rows `rows` + (lane & 15) and the row scales of the lane's output rows
-// rows + 4 (lane >> 4) + 0..3.
-__device__ __forceinline__ void afrag(const u32x4* st, int rows, int lane, i32x8& a, f32x4& sa) {
-  asm volatile("" : "+v"(lane));
-  const int r = lane & 15, g = lane >> 4, sw = lds_swz(r);
-  a = frag32(st + kA + (rows + r) * 8, (2 * g) ^ sw, (2 * g + 1) ^ sw);
-  sa = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(st + kScale) + rows + 4 * g);
-}
-}  // namespace f8
-
-// The direct-to-LDS loads of one step into `stage`: AJ_ of A (rows below 64 * AJ_), 4 of B and
-// (waves 0-3) the row scales.
-#define MOE_F8_LOADS(stage, kk, AJ_)                                                             \
-  do {                                                                                           \
-    _Pragma("unroll") for (int j_ = 0; j_ < (AJ_); ++j_)                                         \
-        dma_to_lds<16>(Ab + (oa[j_] + (uint32_t)(kk) * 128u), (stage) + la_off[j_]);            \
-    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                             \
-        dma_to_lds<16>(Be + (ob[j_] + (uint32_t)(kk) * 128u), (stage) + f8::kB + (j_ * 8 + wave) * 64); \
-    if (wave < 4) dma_to_lds<4>(sab + (soff + (uint32_t)(kk) * 4u), (stage) + f8::kScale + wave * 16); \
-  } while (0)
-
-// Row block rb: one MFMA per column block, each promoted with this step's scales (column blocks
-// in the upper half of the wave's blocks take the second weight block scale). An empty asm that
-// reads the block's accumulators pins it here: the (memory-free) MFMAs and promotions would
-// otherwise be sunk past the barrier asm that follows.
-#define MOE_F8_BLOCK(CB_, rb_, a_, sa_)                                                          \
-  _Pragma("unroll") for (int cb_ = 0; cb_ < (CB_); ++cb_) {                                      \
-    f32x4 p;                                                                                     \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) p[i_] = 0.f;                                \
-    p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_, b[cb_], p, 0, 0, 0, 127, 0, 127);   \
-    const float sbx = cb_ < (CB_) / 2 ? sb0 : sb1;                                               \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                             \
-        acc[rb_][cb_][i_] = fmaf(p[i_] * sbx, sa_[i_], acc[rb_][cb_][i_]);                      \
-  }                                                                                              \
-  if ((CB_) == 4)                                                                                \
-    asm volatile("" ::"v"(acc[rb_][0]), "v"(acc[rb_][(CB_) > 1 ? 1 : 0]),                        \
-                 "v"(acc[rb_][(CB_) > 2 ? 2 : 0]), "v"(acc[rb_][(CB_) > 3 ? 3 : 0]));             \
-  else                                                                                           \
-    asm volatile("" ::"v"(acc[rb_][0]), "v"(acc[rb_][(CB_) > 1 ? 1 : 0]));                       \
-  __builtin_amdgcn_sched_barrier(0);
-
-// One step on stage `cur` (this step's B fragments, first A fragment and scales in registers).
-#define MOE_F8_STEP(RB_, CB_, AJ_, cur, nxt, k, LOADS, NEXT)                                     \
-  {                                                                                              \
-    _Pragma("unroll") for (int rb = 0; rb < (RB_) - 2; rb += 2) {                                \
-      f8::afrag(cur, r0 + (rb + 1) * 16, lane, aB, saB);                                         \
-      MOE_F8_BLOCK(CB_, rb, aA, saA)                                                             \
-      f8::afrag(cur, r0 + (rb + 2) * 16, lane, aA, saA);                                         \
-      MOE_F8_BLOCK(CB_, rb + 1, aB, saB)                                                         \
-    }                                                                                            \
-    f8::afrag(cur, r0 + ((RB_) - 1) * 16, lane, aB, saB);                                        \
-    MOE_F8_BLOCK(CB_, (RB_) - 2, aA, saA)                                                        \
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");        \
-    if (LOADS) MOE_F8_LOADS(cur, (k) + 2, AJ_);                                                  \
-    MOE_F8_BLOCK(CB_, (RB_) - 1, aB, saB)                                                        \
-    if (NEXT) {                                                                                  \
-      f8::bfrags<CB_>(nxt, cbase, lane, b);                                                      \
-      f8::afrag(nxt, r0, lane, aA, saA);                                                         \
-      sb0 = psb0[(k) + 1];                                                                       \
-      sb1 = psb1[(k) + 1];                                                                       \
-    }                                                                                            \
-  }
-
-// One tile: RB x CB blocks per wave, wave rows r0.., weight-tile column blocks cbase[];
-// NWR waves share a row (the GLU row absmax runs over them).
-#define MOE_F8_TILE(RB_, CB_, AJ_, NWR_, r0_, CBASE_INIT)                                        \
-  {                                                                                              \
-    const int r0 = (r0_);                                                                        \
-    int cbase[CB_];                                                                              \
-    CBASE_INIT;                                                                                  \
-    const float* psb0 = g.b_scale + (size_t)ti.e * g.b_scale_exp +                               \
-                        (size_t)(weight_row<GLU, BN>(cbase[0], ti.nt, g) >> 7) * g.b_scale_ld;   \
-    const float* psb1 = g.b_scale + (size_t)ti.e * g.b_scale_exp +                               \
-                        (size_t)(weight_row<GLU, BN>(cbase[(CB_) - 1], ti.nt, g) >> 7) * g.b_scale_ld; \
-    f32x4 acc[RB_][CB_];                                                                         \
-    _Pragma("unroll") for (int rb = 0; rb < (RB_); ++rb)                                         \
-      _Pragma("unroll") for (int cb = 0; cb < (CB_); ++cb)                                       \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[rb][cb][i] = 0.f;                      \
-    MOE_F8_LOADS(st0, 0, AJ_);                                                                   \
-    if (KT > 1) MOE_F8_LOADS(st1, 1, AJ_);                                                       \
-    /* wait for step 0: step 1's AJ_ + 4 (+1 for waves 0-3) loads may still be in flight */      \
-    if (KT == 1)                                                                                 \
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");      \
-    else if ((AJ_) == 4 && wave < 4)                                                             \
-      asm volatile("s_waitcnt vmcnt(9)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");      \
-    else if ((AJ_) == 4)                                                                         \
-      asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");      \
-    else if (wave < 4)                                                                           \
-      asm volatile("s_waitcnt vmcnt(7)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");      \
-    else                                                                                         \
-      asm volatile("s_waitcnt vmcnt(6)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");      \
-    i32x8 b[CB_], aA, aB;                                                                        \
-    f32x4 saA, saB;                                                                              \
-    float sb0 = psb0[0], sb1 = psb1[0];                                                          \
-    f8::bfrags<CB_>(st0, cbase, lane, b);                                                        \
-    f8::afrag(st0, r0, lane, aA, saA);                                                           \
-    int k = 0;                                                                                   \
-    for (; k + 2 < KT; k += 2) {                                                                 \
-      MOE_F8_STEP(RB_, CB_, AJ_, st0, st1, k, true, true)                                        \
-      MOE_F8_STEP(RB_, CB_, AJ_, st1, st0, k + 1, true, true)                                    \
-    }                                                                                            \
-    if (k + 2 == KT) {                                                                           \
-      MOE_F8_STEP(RB_, CB_, AJ_, st0, st1, k, false, true)                                       \
-      MOE_F8_STEP(RB_, CB_, AJ_, st1, st0, k + 1, false, false)                                  \
-    } else {                                                                                     \
-      MOE_F8_STEP(RB_, CB_, AJ_, st0, st1, k, false, false)                                      \
-    }                                                                                            \
-    f8_epilogue<RB_, CB_, NWR_, GLU>(g, ti, acc, r0, cbase, lane, wave, reinterpret_cast<float*>(st0)); \
-  }
-
-// Epilogue (accumulator layout: lane holds column lane & 15, rows 4*(lane>>4) + i).
-// GLU: h = SiLU(gate) * up (gate blocks q < CB/2 pair with up blocks q + CB/2), re-quantised per
-// row per 128 h columns: the row absmax runs over 16 lanes, the wave's pairs, then the NWR waves
-// sharing the row (through LDS `red`, which aliases the first stage: every wave is past its last
-// read). Plain: bf16 y rows.
-template <int RB, int CB, int NWR, bool GLU>
-__device__ __forceinline__ void f8_epilogue(const GemmArgs& g, const TileInfo& ti, const f32x4 (&acc)[RB][CB],
-                                            int r0, const int (&cbase)[CB], int lane, int wave, float* red) {
-  // Row indices are formed from a base passed through an empty asm, so that they are computed
-  // here, per tile, instead of being hoisted out of the tile loop and held across the K loop.
-  int rbase = r0 + 4 * (lane >> 4);
-  asm volatile("" : "+v"(rbase));
-  const int lc = lane & 15;
-  if (GLU) {
-    constexpr int NQ = CB / 2;
-    const int wr = wave % NWR;
-    float hv[RB][NQ][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float m = 0.f;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          hv[rb][q][i] = silu_fast(acc[rb][q][i]) * acc[rb][q + NQ][i];
-          m = fmaxf(m, fabsf(hv[rb][q][i]));
-        }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        if (lc == 0) red[(rbase + rb * 16 + i) * NWR + wr] = m;
-      }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rbase + rb * 16 + i;
-        float m = 0.f;
-#pragma unroll
-        for (int w = 0; w < NWR; ++w) m = fmaxf(m, red[r * NWR + w]);
-        const float scale = m / 448.0f;
-        if (r < ti.mvalid) {
-          uint8_t* crow = g.C + (size_t)(ti.row0 + r) * g.ldc;
-#pragma unroll
-          for (int q = 0; q < NQ; ++q) {
-            const int t = cbase[q];  // gate row of the weight tile -> h column (32-row gate/up blocks)
-            const int col = ti.nt * 128 + ((t >> 6) << 5) + (t & 31) + lc;
-            crow[col] = m > 0.f ? (uint8_t)f32_to_e4m3(hv[rb][q][i] / scale) : (uint8_t)0;
-          }
-          if (wr == 0 && lc == 0) g.c_scale[(size_t)(ti.row0 + r) * g.c_scale_ld + ti.nt] = scale;
-        }
-      }
-    __syncthreads();  // red[] aliases the first stage of the next tile
-  } else {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int col = ti.nt * 256 + cbase[cb] + lc;
-        if (col < g.N_out) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = rbase + rb * 16 + i;
-            if (r < ti.mvalid)
-              reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(acc[rb][cb][i]);
-          }
-        }
-      }
-  }
-}
-
-template <bool GLU>
-__global__ __launch_bounds__(512, 1) void k_gemm_fp8_w8(GemmArgs g) {
-  constexpr int BM = 256, BN = 256;
-  __shared__ u32x4 st0[f8::kStage];
-  __shared__ u32x4 st1[f8::kStage];
-  __shared__ int tp[kMaxExperts + 1];
-  __shared__ int s_slot[1];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  for (int i = tid; i <= g.n_exp; i += 512) tp[i] = g.tp[i];
-  __syncthreads();
-  const int total = tp[g.n_exp] * g.n_tiles_n;
-  const int KT = g.K / 128;
-  const TileQueue tq = tile_queue(total);
-
-  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
-    TileInfo ti = decode_tile(t, tp, g, BM);
-    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
-    ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
-    ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
-    ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
-    const int arows = (ti.mvalid + 7) & ~7;
-    const uint8_t* Ab = a_base(g, ti);
-    const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
-    uint32_t oa[4], ob[4];
-    int la_off[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = (j * 8 + wave) * 8 + (lane >> 3);
-      const uint32_t ch = (uint32_t)dma_chunk(r, lane) * 16u;
-      const bool live = (j * 8 + wave) * 8 < arows;  // wave-uniform
-      const int rr = live ? a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1) : 0;
-      oa[j] = live ? (uint32_t)rr * (uint32_t)g.lda + ch : 0u;
-      la_off[j] = live ? (j * 8 + wave) * 64 : f8::kSink;
-      ob[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + ch;
-    }
-    // row scales: wave w < 4 loads rows 64w + lane (clamped) of each step
-    const uint8_t* sab = reinterpret_cast<const uint8_t*>(a_scale_base(g, ti));
-    uint32_t soff;
-    {
-      const int r = wave * 64 + lane;
-      const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
-      soff = (uint32_t)rr * (uint32_t)g.a_scale_ld * 4u;
-    }
-    if (arows < BM) {  // zero the A rows that are not fetched, in both stages
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      for (int i = arows * 8 + tid; i < BM * 8; i += 512) {
-        st0[i] = z;
-        st1[i] = z;
-      }
-    }
-    if (ti.mvalid > 128) {
-      MOE_F8_TILE(8, 4, 4, 4, (wave >> 2) * 128,
-                  for (int cb = 0; cb < 4; ++cb) cbase[cb] = (wave & 3) * 64 + cb * 16)
-    } else if (GLU) {
-      // 16 gate columns and their 16 up columns (32-row gate / up blocks of the weight tile)
-      MOE_F8_TILE(8, 2, 2, 8, 0,
-                  cbase[0] = (wave >> 1) * 64 + (wave & 1) * 16; cbase[1] = cbase[0] + 32)
-    } else {
-      MOE_F8_TILE(8, 2, 2, 8, 0, cbase[0] = wave * 32; cbase[1] = cbase[0] + 16)
-    }
-  }
-}
-
 template <class K>
 static hipError_t launch_one(const char* name, K kernel, int grid, int threads, const GemmArgs& g,
                              hipStream_t s) {
@@ -554,17 +279,10 @@ static hipError_t launch_one(const char* name, K kernel, int grid, int threads, 
 
 static int round8(int v) { return ((v + 7) / 8) * 8; }
 
-// variant 0: 256 x 256 tiles, 8 waves of 128 x 64 (or 1 x 8 of 128 x 32), one workgroup per CU;
 // variant 2: 128 x 256 tiles, 8 waves of 64 x 64, one workgroup per CU;
 // variant 1: 32 x 256, 4 waves, two per CU.
 hipError_t launch_gemm_fp8(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s) {
   hipError_t e;
-  if (variant == 0) {
-    const int grid = round8(cus);
-    if ((e = launch_one("gemm_fp8_gateup_swiglu", k_gemm_fp8_w8<true>, grid, 512, g1, s)) != hipSuccess)
-      return e;
-    return launch_one("gemm_fp8_down", k_gemm_fp8_w8<false>, grid, 512, g2, s);
-  }
   if (variant == 2) {
     const int grid = round8(cus);
     if ((e = launch_one("gemm_fp8_gateup_swiglu_m128", k_gemm_fp8<128, 256, 2, 4, true, 1>, grid, 512, g1,

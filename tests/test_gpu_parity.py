@@ -100,9 +100,9 @@ def _skewed_ids(T, counts):
 @pytest.mark.parametrize("gather", [True, False], ids=["gather", "x_perm"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_large_tile_paths(dtype, gather):
-    """Row groups that select the 256 x 256-tile kernels and every valid-row height of their last
-    m-tile (full, <= 128, <= 64, <= 32 rows), with caller-supplied ids; sampled rows of every
-    expert against the oracle."""
+    """Row groups that select the large-tile kernels (bf16: 256 rows, with every valid-row height
+    of the last m-tile: full, <= 128, <= 64, <= 32 rows; fp8: 128 rows) with caller-supplied ids;
+    sampled rows of every expert, the last m-tile's among them, against the oracle."""
     base = CONFIGS[2] if dtype == "bf16" else CONFIGS[5]
     cfg = base.scaled(T=2048, H=256, I=2048, E=8, K=2, score="softmax", renorm=True, route_scale=1.0,
                       n_group=1, topk_group=1, bias=None, I_shared=0)
