@@ -10,6 +10,7 @@ Pages followed, cited by title and section:
   [atlas]  "MoE" chapter README (llm-infra-atlas.github.io/moe)
   [survey] "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4" (wqh011128.github.io)
   [repost] "企业官网建设流程全解析" (cf-1.com; its body reposts MegaMoE / DeepGEMM material)
+  [deepgemm] "DeepGEMM质变：从GEMM库到统一LLM计算原语平台" (itsolotime.com)
 
 Precision: every arithmetic step runs in fp64 over the exact values of the
 inputs (fp32, bf16 and decoded e4m3 are all exact in fp64). The only
@@ -27,6 +28,16 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
   * fp8: OCP e4m3 "fn" (bias 7, max 448, no infinities), round to nearest even,
     saturating at +-448; scale = absmax / 448 per block; all-zero block -> scale 0,
     codes 0.
+  * fp8 x fp4 ([deepgemm] §1.1 and §5.3 name FP8 activations times FP4 weights for
+    both expert GEMMs but define no FP4 scale scheme): the OCP microscaling (MX)
+    formats. A block of 32 consecutive channels of one row shares one E8M0 scale
+    (an unsigned power of two 2^(c-127), code 255 = NaN); weights are MXFP4
+    (e2m1 elements: 1 sign, 2 exponent bits with bias 1, 1 mantissa bit, largest
+    value 6), activations and the SwiGLU output are MXFP8 (e4m3 elements). The
+    block scale exponent is floor(log2(absmax)) - emax of the element format
+    (8 for e4m3, whose largest power of two is 2^8), clamped to the E8M0 range;
+    elements are e4m3(v / scale), round to nearest even, saturating at +-448;
+    an all-zero block (or one whose exponent falls below the range) gets code 0.
 
 Pins (tests/test_oracle.py), so that a dropped term, a wrong sign or index, or a
 transposed operand fails at least one of them:
@@ -47,6 +58,13 @@ transposed operand fails at least one of them:
     against exhaustive nearest-value search and torch's float8_e4m3fn;
   * quantize_rows_fp8: exactly representable rows round-trip, zero blocks,
     saturation and the per-block scale definition.
+  * MX codecs: all 16 e2m1 codes against the format's value table, all 256 E8M0
+    codes against torch's float8_e8m0fnu; the scale exponent at binade edges;
+    quantize_rows_mx: exactly representable blocks round-trip (so a wrong emax,
+    block size or block orientation fails), saturation, zero blocks, the scaled
+    block maximum always in e4m3's top binade, the error bound; the nibble order
+    and block orientation of dequantize_weight_mx on hand-built bytes; an MX layer
+    whose inputs are exactly representable equals the fp64 layer on those values.
 No function here is "parity unpinned".
 """
 import math
@@ -59,6 +77,8 @@ __all__ = [
     "route", "near_tie_tokens", "update_bias", "permute", "gather_rows",
     "e4m3_decode", "e4m3_decode_array", "e4m3_encode",
     "quantize_rows_fp8", "dequantize_rows_fp8", "dequantize_weight_blocks",
+    "E2M1_MAX", "MX_BLOCK", "e2m1_decode", "e2m1_decode_array", "e8m0_decode", "mx_scale_code",
+    "quantize_rows_mx", "dequantize_rows_mx", "unpack_e2m1", "dequantize_weight_mx",
     "silu", "swiglu_hidden", "swiglu_expert", "expert_ffn", "combine",
     "moe_layer", "dense_mix",
 ]
@@ -336,6 +356,95 @@ def dequantize_weight_blocks(codes, scales, block=FP8_BLOCK):
     return vals * np.repeat(np.repeat(s, block, axis=0), block, axis=1)[:N, :K]
 
 
+# ----------------------------------------------------------------------------- MX (fp8 x fp4)
+
+E2M1_MAX = 6.0
+MX_BLOCK = 32         # channels per E8M0 scale (OCP microscaling block)
+MX_EMAX_E4M3 = 8      # exponent of the largest power of two in e4m3 (448 = 1.75 * 2^8)
+
+
+def e2m1_decode(code):
+    """Value of one e2m1 nibble: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+
+    Exponent 0 is subnormal (m * 0.5); otherwise (1 + m/2) * 2^(e-1). No NaN or inf.
+    """
+    code = int(code) & 0xF
+    sign = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return sign * m * 0.5
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+_E2M1_TABLE = np.array([e2m1_decode(c) for c in range(16)], np.float64)
+
+
+def e2m1_decode_array(codes):
+    """Vectorised e2m1_decode over an integer array of nibbles (fp64 values)."""
+    return _E2M1_TABLE[np.asarray(codes).astype(np.int64) & 0xF]
+
+
+def e8m0_decode(code):
+    """E8M0 scale: 2^(code - 127) for codes 0..254, NaN for 255 (fp64, exact)."""
+    code = np.asarray(code).astype(np.int64)
+    return np.where(code == 255, np.nan, np.ldexp(1.0, code - 127))
+
+
+def mx_scale_code(absmax, emax=MX_EMAX_E4M3):
+    """E8M0 code of a block: floor(log2(absmax)) - emax + 127, clamped to [0, 254].
+
+    floor(log2) is taken exactly from the binary exponent (frexp), so no rounding of
+    a logarithm can move a block across a binade edge. absmax == 0 gives code 0.
+    """
+    a = np.asarray(absmax, np.float64)
+    mant, ex = np.frexp(a)                 # a = mant * 2^ex, mant in [0.5, 1)
+    fl = ex.astype(np.int64) - 1           # floor(log2(a)) for a > 0
+    code = np.where(a > 0, fl - emax + 127, 0)
+    return np.clip(code, 0, 254).astype(np.uint8)
+
+
+def quantize_rows_mx(a, block=MX_BLOCK):
+    """MXFP8 quantisation of rows: per row, per `block` consecutive channels.
+
+    a [R,C] is taken in fp32 (the precision the kernels quantise in); per block
+    scale code c = mx_scale_code(absmax) and element codes e4m3(v / 2^(c-127))
+    (the division by a power of two is exact). Returns (codes [R,C] uint8,
+    scale codes [R,C/block] uint8).
+    """
+    a32 = np.asarray(a, np.float32)
+    R, C = a32.shape
+    if C % block:
+        raise ValueError("columns must be a multiple of the block")
+    blocks = a32.astype(np.float64).reshape(R, C // block, block)
+    sc = mx_scale_code(np.abs(blocks).max(axis=-1))
+    q = blocks / e8m0_decode(sc)[..., None]
+    return e4m3_encode(q).reshape(R, C), sc
+
+
+def dequantize_rows_mx(codes, scale_codes, block=MX_BLOCK):
+    """Inverse of quantize_rows_mx in fp64: decode(code) * 2^(scale code - 127)."""
+    vals = e4m3_decode_array(codes)
+    R, C = vals.shape
+    return (vals.reshape(R, C // block, block) * e8m0_decode(scale_codes)[..., None]).reshape(R, C)
+
+
+def unpack_e2m1(packed):
+    """[N, K/2] bytes -> [N, K] nibbles; element 2j is the low nibble of byte j."""
+    p = np.asarray(packed, np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def dequantize_weight_mx(packed, scale_codes, block=MX_BLOCK):
+    """MXFP4 weight [N,K] in fp64 from packed e2m1 codes [N,K/2] and E8M0 codes [N,K/block]."""
+    vals = e2m1_decode_array(unpack_e2m1(packed))
+    N, K = vals.shape
+    return (vals.reshape(N, K // block, block) * e8m0_decode(scale_codes)[..., None]).reshape(N, K)
+
+
 # ----------------------------------------------------------------------------- experts
 
 def silu(g):
@@ -353,23 +462,27 @@ def swiglu_hidden(x, w13):
     return silu(x @ w13[:I].T) * (x @ w13[I:].T)
 
 
-def swiglu_expert(x, w13, w2, fp8_hidden=False):
+def swiglu_expert(x, w13, w2, fp8_hidden=False, mx_hidden=False):
     """One SwiGLU expert on rows of x ([primer] §1, [survey] §1 and §5.1).
 
     x [M,H]; w13 [2I,H] with the gate projection in rows [0,I) and the up
     projection in rows [I,2I) (Linear-1 produces both); w2 [H,I] (Linear-2).
     y = W_down (SiLU(W_gate x) * W_up x) per row. With fp8_hidden the SwiGLU
     output is quantised per row per 128 channels and dequantised before
-    Linear-2, as the fp8 layer does ("SwiGLU / FP8 Cast", [survey] §5.1).
+    Linear-2, as the fp8 layer does ("SwiGLU / FP8 Cast", [survey] §5.1); with
+    mx_hidden it is quantised to MXFP8 (per row per 32 channels) instead.
     """
     a = swiglu_hidden(x, w13)
     if fp8_hidden:
         codes, s = quantize_rows_fp8(a)
         a = dequantize_rows_fp8(codes, s)
+    if mx_hidden:
+        codes, s = quantize_rows_mx(a)
+        a = dequantize_rows_mx(codes, s)
     return a @ np.asarray(w2, np.float64).T
 
 
-def expert_ffn(x_rows, offsets, get_expert, fp8_hidden=False, rows=None):
+def expert_ffn(x_rows, offsets, get_expert, fp8_hidden=False, rows=None, mx_hidden=False):
     """Expert compute over expert-grouped rows ([primer] §5.2).
 
     Rows [offsets[e], offsets[e+1]) of x_rows belong to expert e; get_expert(e)
@@ -386,7 +499,7 @@ def expert_ffn(x_rows, offsets, get_expert, fp8_hidden=False, rows=None):
         if sel.size == 0:
             continue
         w13, w2 = get_expert(e)
-        y = swiglu_expert(np.asarray(x_rows, np.float64)[want[sel]], w13, w2, fp8_hidden)
+        y = swiglu_expert(np.asarray(x_rows, np.float64)[want[sel]], w13, w2, fp8_hidden, mx_hidden)
         if out is None:
             out = np.zeros((want.size, y.shape[1]), np.float64)
         out[sel] = y
@@ -421,14 +534,15 @@ def combine(pair_pos, weights, y_perm, y_shared=None, tokens=None):
 
 def moe_layer(x, w_r, get_expert, fn, K, E, bias=None, n_group=1, topk_group=1,
               group_rule="top2_sum", renorm=True, route_scale=1.0, fp8=False,
-              get_shared=None, tokens=None, ids=None, weights=None):
+              get_shared=None, tokens=None, ids=None, weights=None, mx=False):
     """Whole layer forward for the tokens in `tokens` (default all) ([primer] §5, [atlas] §0).
 
     Router on x (fp64 logits), selection, weights, expert SwiGLU FFNs, weighted
     combine, plus the always-on shared expert when get_shared is given
     (get_shared() -> (w13, w2)). With fp8, x is quantised per token per 128
     channels for the experts (the router reads x itself) and each SwiGLU
-    output is re-quantised before Linear-2. `ids`/`weights` override routing
+    output is re-quantised before Linear-2; with mx the same happens in MXFP8
+    (per 32 channels, E8M0 scales). `ids`/`weights` override routing
     (used to evaluate the layer on a given routing).
     Returns (out [len(tokens),H], ids [T,K], weights [T,K]).
     """
@@ -441,6 +555,9 @@ def moe_layer(x, w_r, get_expert, fn, K, E, bias=None, n_group=1, topk_group=1,
     if fp8:
         codes, s = quantize_rows_fp8(x[toks])
         xe = dequantize_rows_fp8(codes, s)
+    elif mx:
+        codes, s = quantize_rows_mx(x[toks])
+        xe = dequantize_rows_mx(codes, s)
     else:
         xe = np.asarray(x[toks], np.float64)
     H = x.shape[1]
@@ -450,10 +567,10 @@ def moe_layer(x, w_r, get_expert, fn, K, E, bias=None, n_group=1, topk_group=1,
         for i, t in enumerate(toks):
             for k in range(K):
                 if ids[t, k] == e:
-                    out[i] += weights[t, k] * swiglu_expert(xe[i:i + 1], w13, w2, fp8)[0]
+                    out[i] += weights[t, k] * swiglu_expert(xe[i:i + 1], w13, w2, fp8, mx)[0]
     if get_shared is not None:
         w13s, w2s = get_shared()
-        out += swiglu_expert(xe, w13s, w2s, fp8)
+        out += swiglu_expert(xe, w13s, w2s, fp8, mx)
     return out, ids, weights
 
 

@@ -343,6 +343,140 @@ def test_fp8_layer_path_matches_exactly_representable_fp32():
     np.testing.assert_array_equal(orc.dequantize_rows_fp8(q, s), x)
 
 
+
+# ------------------------------------------------------------------ MX (fp8 x fp4) codecs
+
+def test_e2m1_decode_all_codes():
+    # the e2m1 value set of the OCP microscaling formats: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    mine = orc.e2m1_decode_array(np.arange(16))
+    assert mine[:8].tolist() == table
+    assert mine[8:].tolist() == [-v for v in table]
+    assert math.copysign(1, mine[8]) < 0 and mine.max() == orc.E2M1_MAX
+
+
+def test_e8m0_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.e8m0_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(mine[255]) and np.isnan(ref[255])
+    np.testing.assert_array_equal(mine[:255], ref[:255])
+    assert mine[127] == 1.0 and mine[0] == 2.0 ** -127 and mine[254] == 2.0 ** 127
+
+
+def test_mx_scale_code_binade_edges():
+    cases = {1.0: 119, 448.0: 127, 256.0: 127, 511.99: 127, 255.99: 126, 512.0: 128,
+             0.0: 0, 2.0 ** -140: 0, 2.0 ** -119: 0, 2.0 ** -118: 1, 3.0e38: 246}
+    got = orc.mx_scale_code(np.array(list(cases.keys())))
+    assert got.tolist() == list(cases.values())
+    # e2m1 elements (emax 2): a block whose maximum is 6 keeps scale 1
+    assert int(orc.mx_scale_code(6.0, emax=2)) == 127 and int(orc.mx_scale_code(3.99, emax=2)) == 126
+
+
+def test_quantize_rows_mx_roundtrip_of_representable_blocks():
+    # each 32-channel block: e4m3 codes below 256 plus one in [256, 448], times 2^(c-127) with
+    # c differing between neighbouring blocks and rows. Such rows are fixed points of the
+    # quantiser, so a wrong element emax, block size or block orientation changes the result.
+    rng = np.random.default_rng(21)
+    R, C = 5, 256
+    codes = rng.integers(0, 0x78, size=(R, C)).astype(np.uint8)
+    codes |= (rng.integers(0, 2, size=(R, C)) << 7).astype(np.uint8)
+    nb = C // orc.MX_BLOCK
+    top = rng.integers(0, orc.MX_BLOCK, size=(R, nb))
+    for r in range(R):
+        for b in range(nb):
+            codes[r, b * orc.MX_BLOCK + top[r, b]] = rng.integers(0x78, 0x7F) | (rng.integers(0, 2) << 7)
+    sc = rng.integers(100, 150, size=(R, nb)).astype(np.uint8)
+    vals = (orc.e4m3_decode_array(codes).reshape(R, nb, -1) * 2.0 ** (sc.astype(np.int64) - 127)[..., None]).reshape(R, C)
+    q, s = orc.quantize_rows_mx(vals)
+    np.testing.assert_array_equal(s, sc)
+    np.testing.assert_array_equal(q, codes)
+    np.testing.assert_array_equal(orc.dequantize_rows_mx(q, s), vals)
+
+
+def test_quantize_rows_mx_saturation_zero_and_bounds():
+    a = np.zeros((3, 64), np.float32)
+    a[0, :32] = 1.0
+    a[0, 5] = 500.0                  # block absmax 500: scale 2^0, 500 saturates to 448
+    a[0, 6] = -464.0
+    a[1, 40] = -3.0                  # row 1: block 0 all zero, block 1 absmax 3 -> scale 2^-7
+    q, s = orc.quantize_rows_mx(a)
+    assert s[0, 0] == 127 and q[0, 5] == 0x7E and q[0, 6] == 0xFE and q[0, 0] == 0x38
+    assert s[1, 0] == 0 and (q[1, :32] == 0).all()
+    assert s[1, 1] == 127 - 7 and orc.e4m3_decode(q[1, 40]) * 2.0 ** -7 == -3.0
+    assert (s[2] == 0).all() and (q[2] == 0).all()
+    # random rows: the scaled block maximum lies in e4m3's top binade [256, 448]; an element
+    # whose scaled magnitude exceeds 448 decodes to exactly +-448 * scale, every other one is
+    # within half an e4m3 ulp (relative 2^-4) or, below the normal range, 2^-10 * scale
+    rng = np.random.default_rng(22)
+    a = (rng.normal(size=(6, 512)) * np.exp(rng.normal(size=(6, 1)) * 3)).astype(np.float32)
+    q, s = orc.quantize_rows_mx(a)
+    dec = orc.e4m3_decode_array(q).reshape(6, 16, 32)
+    mx = np.abs(dec).max(-1)
+    assert ((mx >= 256) & (mx <= 448)).all()
+    scale = np.repeat(orc.e8m0_decode(s), 32, 1)
+    a64 = a.astype(np.float64)
+    deq = orc.dequantize_rows_mx(q, s)
+    sat = np.abs(a64) / scale > 448
+    assert sat.any() and (deq[sat] == np.sign(a64[sat]) * 448 * scale[sat]).all()
+    err = np.abs(deq - a64)[~sat]
+    assert (err <= np.maximum(np.abs(a64) * 2.0 ** -4, scale * 2.0 ** -10)[~sat]).all()
+
+
+def test_dequantize_weight_mx_nibble_order_and_blocks():
+    packed = np.zeros((2, 32), np.uint8)         # N=2 rows of K=64 elements
+    packed[0, 0] = 0x21                          # element 0 = code 1 (0.5), element 1 = code 2 (1.0)
+    packed[0, 16] = 0xF7                         # element 32 = code 7 (6.0), element 33 = code 15 (-6.0)
+    packed[1, 31] = 0x3C                         # row 1: element 62 = code 12 (-2.0), element 63 = code 3 (1.5)
+    sc = np.array([[127, 129], [126, 120]], np.uint8)
+    w = orc.dequantize_weight_mx(packed, sc)
+    assert w.shape == (2, 64)
+    assert w[0, 0] == 0.5 and w[0, 1] == 1.0 and w[0, 32] == 24.0 and w[0, 33] == -24.0
+    assert w[1, 62] == -2.0 * 2.0 ** -7 and w[1, 63] == 1.5 * 2.0 ** -7
+    assert np.count_nonzero(w) == 6
+
+
+def test_mx_hidden_requantisation_bound():
+    # with mx_hidden the expert output moves by at most |W2| times the hidden's quantisation
+    # error bound, and it does move (the quantiser is on the path)
+    rng = np.random.default_rng(23)
+    M, H, I = 6, 64, 96
+    x = rng.normal(size=(M, H))
+    w13 = rng.normal(size=(2 * I, H)) / 8
+    w2 = rng.normal(size=(H, I)) / 10
+    y = orc.swiglu_expert(x, w13, w2)
+    ymx = orc.swiglu_expert(x, w13, w2, mx_hidden=True)
+    h = orc.swiglu_hidden(x, w13)
+    _, s = orc.quantize_rows_mx(h)
+    sc = np.repeat(orc.e8m0_decode(s), 32, 1)
+    bound = np.maximum(np.maximum(np.abs(h) * 2.0 ** -4, sc * 2.0 ** -10), np.abs(h) - 448 * sc)
+    assert (np.abs(ymx - y) <= bound @ np.abs(w2).T * (1 + 1e-9) + 1e-12).all()
+    assert np.abs(ymx - y).max() > 0
+
+
+def test_mx_layer_path_on_representable_inputs():
+    # x exactly MXFP8-representable: the MX layer's input quantisation is lossless, so with
+    # the hidden re-quantisation as the only rounding the MX layer equals the layer computed
+    # on the decoded values with mx_hidden experts
+    rng = np.random.default_rng(24)
+    T, H, I, E, K = 5, 64, 64, 4, 2
+    codes = rng.integers(0, 0x78, size=(T, H)).astype(np.uint8)
+    codes[:, 0] = 0x7A
+    codes[:, 32] = 0x79
+    x = orc.dequantize_rows_mx(codes, np.full((T, 2), 118, np.uint8))
+    q, s = orc.quantize_rows_mx(x)
+    np.testing.assert_array_equal(orc.dequantize_rows_mx(q, s), x)
+    w_r = rng.normal(size=(H, E))
+    ws = [(rng.normal(size=(2 * I, H)) / 8, rng.normal(size=(H, I)) / 8) for _ in range(E)]
+    out, ids, wts = orc.moe_layer(x, w_r, lambda e: ws[e], "softmax", K, E, mx=True)
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for k in range(K):
+            w13, w2 = ws[ids[t, k]]
+            ref[t] += wts[t, k] * orc.swiglu_expert(x[t:t + 1], w13, w2, mx_hidden=True)[0]
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------ near-tie accounting
 
 def test_near_tie_flags():
