@@ -16,7 +16,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = ("MoE layer active TFLOP/s + tokens/s, % of MFMA peak (prefill) / % HBM BW (decode)")
-PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense TFLOP/s
+# dense TFLOP/s; the MX layer's fp8 x fp4 MFMA issues at the fp8 rate (the slower operand)
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 5000.0, "f32": 157.3}
+DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3", "mxfp4": "mxfp8_e4m3 x mxfp4_e2m1"}
+QUANT = ("fp8", "mxfp4")
 HBM_PEAK = 8000.0                                       # GB/s
 
 
@@ -42,30 +45,35 @@ def kernel_work(cfg, active, gather=True):
 
     Bytes count each operand once at its stored width (inputs read once, outputs written once);
     `active` = experts that received at least one pair (only their weights are read).
-    gather: Linear-1 of the routed experts reads x ([T,H], fp8: its codes) in place, so its A
+    gather: Linear-1 of the routed experts reads x ([T,H], fp8 / MX: its codes) in place, so its A
     operand is T rows; otherwise the permute stage writes x_perm ([P,H]) and Linear-1 reads it.
     Keys are "stage/kernel" with the kernel's tile-variant suffix removed.
     """
     T, H, I, E, K, P, Is = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.P, cfg.I_shared
-    fp8 = cfg.dtype == "fp8"
+    fp8, mx = cfg.dtype == "fp8", cfg.dtype == "mxfp4"
+    q = fp8 or mx
     xb = 4 if cfg.dtype == "f32" else 2          # x and out
-    ab = 1 if fp8 else xb                        # GEMM operand bytes (x_perm, weights, h)
-    yb = 2 if fp8 else 4                         # y rows: fp32 (f32/bf16 layers), bf16 (fp8 layers)
-    sc = 4.0 / 128 if fp8 else 0.0               # activation-scale bytes per element
-    wsc = 4.0 / (128 * 128) if fp8 else 0.0      # weight-scale bytes per element
+    ab = 1 if q else xb                          # activation operand bytes (x_perm, h)
+    wb = 0.5 if mx else ab                       # weight bytes per element (MX: two e2m1 per byte)
+    yb = 2 if q else 4                           # y rows: fp32 (f32/bf16 layers), bf16 (fp8 / MX layers)
+    # scale bytes per element: fp8 one fp32 per 128 activations / per 128x128 weights; MX one
+    # E8M0 byte per 32 elements of either operand
+    sc = 4.0 / 128 if fp8 else (1.0 / 32 if mx else 0.0)
+    wsc = 4.0 / (128 * 128) if fp8 else (1.0 / 32 if mx else 0.0)
+    qn = "mx" if mx else "fp8"
     w = {}
 
     def add(name, fl, by):
         f0, b0 = w.get(name, (0.0, 0.0))
         w[name] = (f0 + fl, b0 + by)
 
-    kind = {"f32": "gemm_f32", "bf16": "gemm_bf16", "fp8": "gemm_fp8"}[cfg.dtype]
+    kind = {"f32": "gemm_f32", "bf16": "gemm_bf16", "fp8": "gemm_fp8", "mxfp4": "gemm_mx"}[cfg.dtype]
 
     def ffn(st, rows, nexp, inter, a_rows):
         add(st + kind + "_gateup_swiglu", 4.0 * rows * H * inter,
-            a_rows * H * (ab + sc) + nexp * 2 * inter * H * (ab + wsc) + rows * inter * (ab + sc))
+            a_rows * H * (ab + sc) + nexp * 2 * inter * H * (wb + wsc) + rows * inter * (ab + sc))
         add(st + kind + "_down", 2.0 * rows * H * inter,
-            rows * inter * (ab + sc) + nexp * H * inter * (ab + wsc) + rows * H * yb)
+            rows * inter * (ab + sc) + nexp * H * inter * (wb + wsc) + rows * H * yb)
 
     rb = 4 if cfg.dtype == "f32" else 2
     add("route/router_f32" if cfg.dtype == "f32" else "route/router_bf16", 2.0 * T * H * E,
@@ -76,19 +84,20 @@ def kernel_work(cfg, active, gather=True):
     add("permute/perm_scan", 0.0, E * 8)
     add("permute/perm_scatter", 0.0, P * 4 + P * 8)
     if gather:
-        if fp8:
-            add("permute/quantize_fp8", 0.0, T * H * 2 + T * H * (1 + sc))
+        if q:
+            add(f"permute/quantize_{qn}", 0.0, T * H * 2 + T * H * (1 + sc))
     else:
-        add("permute/gather_quant_fp8" if fp8 else "permute/gather", 0.0,
+        add(f"permute/gather_quant_{qn}" if q else "permute/gather", 0.0,
             P * 4 + P * H * xb + P * H * (ab + sc))
     add("ffn/build_tiles", 0.0, E * 8)
     ffn("ffn/", P, active, I, T if gather else P)
     if Is:
-        if fp8 and not gather:
-            add("shared/quantize_fp8", 0.0, T * H * 2 + T * H * (1 + sc))
+        if q and not gather:
+            add(f"shared/quantize_{qn}", 0.0, T * H * 2 + T * H * (1 + sc))
         add("shared/build_tiles", 0.0, 8)
         ffn("shared/", T, 1, Is, T)
-    cname = {"f32": "combine_f32", "bf16": "combine_f32_to_bf16", "fp8": "combine_bf16"}[cfg.dtype]
+    cname = {"f32": "combine_f32", "bf16": "combine_f32_to_bf16", "fp8": "combine_bf16",
+             "mxfp4": "combine_bf16"}[cfg.dtype]
     add("combine/" + cname, 0.0, P * 4 + T * K * 4 + P * H * yb + (T * H * yb if Is else 0) + T * H * xb)
     return w
 
@@ -205,7 +214,7 @@ def main():
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[dtype], "data": "synthetic",
+        "dtype": DTYPE_NAME[dtype], "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
                    "I_shared": cfg.I_shared, "global_batch": cfg.T, "seq_len": cfg.T,
                    "parallelism": "single-gpu",
@@ -323,6 +332,7 @@ def bench_route(args, cfg):
 KERNEL_SOURCES = {
     "gemm_bf16": ["kernels_gemm_bf16.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
     "gemm_fp8": ["kernels_gemm_fp8.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
+    "gemm_mx": ["kernels_gemm_mx.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
     "gemm_f32": ["kernels_ffn.hip", "gemm_common.h", "device.h", "internal.h"],
 }
 
@@ -389,7 +399,14 @@ def cpu_baseline(cfg, x, w_r, bias, ex, sh, layer, ntok):
     host = {e: {k: v[e].cpu() for k, v in ex.items() if v is not None} for e in used}
     hsh = None if sh is None else {k: v[0].cpu() for k, v in sh.items() if v is not None}
 
+    def mx_nat(s):
+        """[K/128][N][4] E8M0 array -> [N][K/32] (the oracle's row-major block order)"""
+        return s.permute(1, 0, 2).reshape(s.shape[1], -1).numpy()
+
     def dec(d):
+        if cfg.dtype == "mxfp4":
+            return (orc.dequantize_weight_mx(d["w13"].numpy(), mx_nat(d["w13_scale"])),
+                    orc.dequantize_weight_mx(d["w2"].numpy(), mx_nat(d["w2_scale"])))
         if cfg.dtype == "fp8":
             return (orc.dequantize_weight_blocks(d["w13"].numpy(), d["w13_scale"].numpy()),
                     orc.dequantize_weight_blocks(d["w2"].numpy(), d["w2_scale"].numpy()))
@@ -411,7 +428,7 @@ def cpu_baseline(cfg, x, w_r, bias, ex, sh, layer, ntok):
     orc.moe_layer(xs, wr, lambda e: dec(host[e]), cfg.score, cfg.K, cfg.E, b, cfg.n_group,
                   cfg.topk_group, cfg.group_rule, cfg.renorm, cfg.route_scale, fp8=cfg.dtype == "fp8",
                   get_shared=None if hsh is None else (lambda: dec(hsh)), tokens=toks,
-                  ids=full_ids, weights=full_w)
+                  ids=full_ids, weights=full_w, mx=cfg.dtype == "mxfp4")
     dt = time.perf_counter() - t0
     from mixture_experts_layer_07_amd.configs import active_flops
     fl = active_flops(cfg) / cfg.T * ntok

@@ -53,8 +53,20 @@ typedef enum moe_status {
  *  MOE_FP8_E4M3 x and W_r are bf16; the library quantises x per token per 128 channels to
  *               e4m3 for the experts; expert weights are e4m3 codes with one fp32 scale per
  *               128x128 block; the SwiGLU output is re-quantised per row per 128 channels;
- *               fp32 accumulation; y_perm, y_shared and out are bf16. */
-enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
+ *               fp32 accumulation; y_perm, y_shared and out are bf16.
+ *  MOE_MXFP4    FP8 activations times FP4 weights ("DeepGEMM质变：从GEMM库到统一LLM计算原语平台",
+ *               itsolotime.com, 1.1 and 5.3) in the OCP microscaling formats: x and W_r are
+ *               bf16; the library quantises x to MXFP8 (e4m3 codes, one E8M0 scale per 32
+ *               channels, see moe_quantize_mx) for the experts; expert weights are MXFP4 (e2m1
+ *               codes, two per byte, element 2j in the low nibble, one E8M0 scale per 32
+ *               channels); the SwiGLU output is re-quantised to MXFP8; fp32 accumulation (the
+ *               MFMA applies the block scales); y_perm, y_shared and out are bf16.
+ *
+ * MX scale arrays. An operand of R rows and C channels (C a multiple of 128) has its E8M0 scale
+ * codes (value 2^(code-127)) stored as [C/128][R][4] bytes: the 4-byte word at (g, r) holds the
+ * scales of channels [128g + 32b, 128g + 32b + 32) of row r in byte b. Weights: one such array
+ * per expert, R = the expert's output rows (2*inter for w13, H for w2), C = its input channels. */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 };
 /* Score function ("MoE 路由入门", section 3). */
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
 /* Group score for grouped top-K ("MoE 路由入门", section 7 uses the group maximum). */
@@ -68,13 +80,13 @@ typedef struct moe_config {
   int32_t n_group;         /* expert groups; 1 = plain top-K. Group g = experts [g*E/n, (g+1)*E/n) */
   int32_t topk_group;      /* groups kept per token (ignored when n_group == 1) */
   int32_t group_score;     /* MOE_GROUP_MAX | MOE_GROUP_TOP2_SUM */
-  int32_t dtype;           /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 */
+  int32_t dtype;           /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 | MOE_MXFP4 */
   int32_t I_shared;        /* intermediate size of the one shared expert; 0 = none */
 } moe_config;
 
-/* Validates a config (no device access). Limits: T >= 1, 1 <= K <= E <= 256, H and I
- * multiples of 128 for bf16/fp8 and of 4 for fp32, E % n_group == 0, K <= topk_group*E/n_group,
- * T*K < 2^31. */
+/* Validates a config (no device access). Limits: T >= 1, 1 <= K <= E <= 256, H, I and I_shared
+ * multiples of 128 for bf16/fp8, of 256 for MXFP4 and of 4 for fp32, E % n_group == 0,
+ * K <= topk_group*E/n_group, T*K < 2^31. */
 moe_status moe_check_config(const moe_config* cfg);
 
 /* Bytes of device workspace that moe_route, moe_permute and moe_expert_ffn (routed and
@@ -130,12 +142,13 @@ moe_status moe_update_bias(int32_t n_experts, const int32_t* counts, float* bias
  *   pair_pos     device [P] int32 out: inverse, pair_pos[sorted_pair[i]] = i
  *   x            device [T,H] activations (fp32 / bf16 as in moe_route), or NULL to skip the gather
  *   x_perm       device [P,H] out: row i = x[sorted_pair[i] / K]; same dtype as x, except
- *                MOE_FP8_E4M3 where it holds e4m3 codes (uint8)
- *   x_perm_scale device [P,H/128] fp32 out (MOE_FP8_E4M3 only, else NULL): row scale
- *                absmax/448 of each 128-channel block; code = e4m3_rne_sat(x / scale) */
+ *                MOE_FP8_E4M3 and MOE_MXFP4 where it holds e4m3 codes (uint8)
+ *   x_perm_scale MOE_FP8_E4M3: device [P,H/128] fp32 out, the row scale absmax/448 of each
+ *                128-channel block, code = e4m3_rne_sat(x / scale); MOE_MXFP4: device MX scale
+ *                array of P rows out (the codes as moe_quantize_mx gives them); else NULL */
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
-                       void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes, void* stream);
+                       void* x_perm, void* x_perm_scale, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_expert_ffn -- SwiGLU experts over expert-grouped rows, as two grouped GEMMs
  * ("MoE 路由入门", sections 1 and 5.2; Linear-1 = gate and up together, "SwiGLU / FP8 Cast",
@@ -144,19 +157,24 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
  *   n_rows     rows of x_rows and y_rows (P for routed, T for shared); offsets[n_experts] = n_rows
  *   inter      intermediate size of these experts (cfg->I or cfg->I_shared)
  *   offsets    device [n_experts+1] int32: rows [offsets[e], offsets[e+1]) belong to expert e
- *   x_rows     device [n_rows,H]: fp32 / bf16, or e4m3 codes (MOE_FP8_E4M3)
- *   x_scale    device [n_rows,H/128] fp32 row-block scales (MOE_FP8_E4M3), else NULL
- *   w13        device [n_experts, 2*inter, H]: gate rows [0,inter), up rows [inter,2*inter)
- *   w13_scale  device [n_experts, 2*inter/128, H/128] fp32 (MOE_FP8_E4M3), else NULL
- *   w2         device [n_experts, H, inter]
- *   w2_scale   device [n_experts, H/128, inter/128] fp32 (MOE_FP8_E4M3), else NULL
+ *   x_rows     device [n_rows,H]: fp32 / bf16, or e4m3 codes (MOE_FP8_E4M3, MOE_MXFP4)
+ *   x_scale    MOE_FP8_E4M3: device [n_rows,H/128] fp32 row-block scales; MOE_MXFP4: device MX
+ *              scale array of n_rows rows; else NULL
+ *   w13        device [n_experts, 2*inter, H]: gate rows [0,inter), up rows [inter,2*inter);
+ *              MOE_MXFP4: [n_experts, 2*inter, H/2] bytes of packed e2m1 codes
+ *   w13_scale  MOE_FP8_E4M3: device [n_experts, 2*inter/128, H/128] fp32; MOE_MXFP4: device
+ *              [n_experts] MX scale arrays of 2*inter rows and H channels; else NULL
+ *   w2         device [n_experts, H, inter] (MOE_MXFP4: [n_experts, H, inter/2] packed e2m1)
+ *   w2_scale   MOE_FP8_E4M3: device [n_experts, H/128, inter/128] fp32; MOE_MXFP4: device
+ *              [n_experts] MX scale arrays of H rows and inter channels; else NULL
  *   y_rows     device [n_rows,H] out: fp32 (MOE_F32 and MOE_BF16: the fp32 accumulators, so
- *              the combine rounds only once) or bf16 (MOE_FP8_E4M3)
- * The SwiGLU output is kept in the workspace (bf16, fp32 for MOE_F32, e4m3 + scales for fp8). */
+ *              the combine rounds only once) or bf16 (MOE_FP8_E4M3, MOE_MXFP4)
+ * The SwiGLU output is kept in the workspace (bf16, fp32 for MOE_F32, e4m3 + scales for fp8 and
+ * MX). */
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_rows, int32_t inter,
-                          const int32_t* offsets, const void* x_rows, const float* x_scale,
-                          const void* w13, const float* w13_scale, const void* w2,
-                          const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                          const int32_t* offsets, const void* x_rows, const void* x_scale,
+                          const void* w13, const void* w13_scale, const void* w2,
+                          const void* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
                           void* stream);
 
 /* moe_expert_ffn_gather -- moe_expert_ffn whose Linear-1 reads the activations in place:
@@ -166,15 +184,17 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_ro
  * section 3.6.2; the arithmetic is that of moe_expert_ffn, row for row.
  *   sorted_pair device [n_rows] int32: moe_permute's sorted_pair (values in [0, T*K); a value
  *               outside is clamped to the last token, so no read leaves x)
- *   x           device [T,H]: fp32 / bf16, or e4m3 codes (MOE_FP8_E4M3, e.g. moe_quantize_fp8 of
- *               the layer input, the same codes the shared expert reads)
- *   x_scale     device [T,H/128] fp32 (MOE_FP8_E4M3), else NULL
+ *   x           device [T,H]: fp32 / bf16, or e4m3 codes (MOE_FP8_E4M3 / MOE_MXFP4, e.g.
+ *               moe_quantize_fp8 / moe_quantize_mx of the layer input, the same codes the shared
+ *               expert reads)
+ *   x_scale     MOE_FP8_E4M3: device [T,H/128] fp32; MOE_MXFP4: device MX scale array of T
+ *               rows; else NULL
  * Other arguments, outputs and errors as moe_expert_ffn; MOE_ERR_UNSUPPORTED if x is 4 GiB or
  * more (the per-row offsets are 32-bit). */
 moe_status moe_expert_ffn_gather(const moe_config* cfg, int32_t n_experts, int32_t n_rows,
                                  int32_t inter, const int32_t* offsets, const int32_t* sorted_pair,
-                                 const void* x, const float* x_scale, const void* w13,
-                                 const float* w13_scale, const void* w2, const float* w2_scale,
+                                 const void* x, const void* x_scale, const void* w13,
+                                 const void* w13_scale, const void* w2, const void* w2_scale,
                                  void* y_rows, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_combine -- weighted combine back to [T,H] ("MoE 路由入门", section 5.3; shared expert
@@ -196,6 +216,16 @@ moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const flo
  *   fp32 out. cols must be a multiple of 128. */
 moe_status moe_quantize_fp8(int32_t rows, int32_t cols, const void* in, uint8_t* codes,
                             float* scales, void* stream);
+
+/* moe_quantize_mx -- MXFP8 row quantisation of bf16 rows (the experts' input in the MX layer;
+ * OCP microscaling, the FP8 side of "DeepGEMM质变", 1.1 and 5.3): per row per 32 columns the
+ * E8M0 scale code is c = floor(log2 absmax) - 8 + 127, clamped to [0, 254] (8 = the exponent of
+ * e4m3's largest power of two; an all-zero block gets c = 0); code = e4m3(v * 2^(127 - c)), round
+ * to nearest even, saturating at +-448.
+ *   in device [rows,cols] bf16; codes device [rows,cols] uint8 out; scales device MX scale array
+ *   of `rows` rows out ([cols/128][rows][4] bytes). cols must be a positive multiple of 128. */
+moe_status moe_quantize_mx(int32_t rows, int32_t cols, const void* in, uint8_t* codes,
+                           uint8_t* scales, void* stream);
 
 /* Reads (and clears) the device error word kept at the start of `ws`, waiting for `stream`.
  * *code = 0 when no kernel flagged bad data since the last read; otherwise the returned

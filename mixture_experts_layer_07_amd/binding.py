@@ -16,7 +16,7 @@ from .configs import LayerConfig
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GROUP_MAX, MOE_GROUP_TOP2_SUM = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
@@ -52,6 +52,7 @@ _SIGS = {
                                    _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_fp8": (_I, [_I, _I, _P, _P, _P, _P]),
+    "moe_quantize_mx": (_I, [_I, _I, _P, _P, _P, _P]),
     "moe_get_device_error": (_I, [_P, ctypes.POINTER(_I), _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -87,7 +88,7 @@ def header_functions():
 
 
 def make_config(cfg: LayerConfig) -> MoeConfig:
-    dt = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}[cfg.dtype]
+    dt = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}[cfg.dtype]
     return MoeConfig(cfg.T, cfg.H, cfg.I, cfg.E, cfg.K,
                      MOE_SOFTMAX if cfg.score == "softmax" else MOE_SIGMOID,
                      1 if cfg.renorm else 0, float(cfg.route_scale), cfg.n_group,
@@ -181,6 +182,11 @@ def moe_combine(cfg, pair_pos, topk_weights, y_perm, y_shared, out, stream=None)
 def moe_quantize_fp8(rows, cols, inp, codes, scales, stream=None):
     _check(lib().moe_quantize_fp8(rows, cols, _p(inp), _p(codes), _p(scales), _stream(stream)),
            "moe_quantize_fp8")
+
+
+def moe_quantize_mx(rows, cols, inp, codes, scales, stream=None):
+    _check(lib().moe_quantize_mx(rows, cols, _p(inp), _p(codes), _p(scales), _stream(stream)),
+           "moe_quantize_mx")
 
 
 def moe_get_device_error(ws, stream=None) -> int:

@@ -5,6 +5,8 @@ section 3: a Mixtral-shaped coarse layer (H=4096, E=8, top-2, I=14336) and a
 DeepSeek-V3-shaped fine-grained layer (H=7168, E=256, top-8, one shared expert).
 Grouped routing (8 groups of 32, keep 4 groups) follows section 7 of
 "MoE 路由入门：从 Dense FFN 到 GroupedTopK" and its section 10 default shape.
+The MXFP4 layers run both expert GEMMs as FP8 activations times FP4 weights ("DeepGEMM质变：
+从GEMM库到统一LLM计算原语平台", sections 1.1 and 5.3) on the fine-grained shapes.
 """
 from dataclasses import dataclass, replace
 from typing import Optional
@@ -25,7 +27,7 @@ class LayerConfig:
     topk_group: int      # groups kept per token
     group_rule: str      # "top2_sum" | "max"
     bias: Optional[str]  # None | "normal" (std 0.1) | "zipf" (skew calibrated to Zipf s=1.2)
-    dtype: str           # "f32" | "bf16" | "fp8"
+    dtype: str           # "f32" | "bf16" | "fp8" | "mxfp4" (MXFP8 activations x MXFP4 weights)
     I_shared: int        # shared expert intermediate size (0 = none)
     seed: int
 
@@ -53,6 +55,12 @@ CONFIGS = {
     5: LayerConfig("dsv3-fp8", T=8192, H=7168, I=2048, E=256, K=8, score="sigmoid",
                    renorm=True, route_scale=2.5, n_group=8, topk_group=4, group_rule="top2_sum",
                    bias="normal", dtype="fp8", I_shared=2048, seed=4),
+    7: LayerConfig("dsv3-mxfp4", T=8192, H=7168, I=2048, E=256, K=8, score="sigmoid",
+                   renorm=True, route_scale=2.5, n_group=8, topk_group=4, group_rule="top2_sum",
+                   bias="normal", dtype="mxfp4", I_shared=2048, seed=6),
+    8: LayerConfig("decode-zipf-mxfp4", T=128, H=7168, I=2048, E=256, K=8, score="sigmoid",
+                   renorm=True, route_scale=2.5, n_group=8, topk_group=4, group_rule="top2_sum",
+                   bias="zipf", dtype="mxfp4", I_shared=2048, seed=7),
 }
 
 

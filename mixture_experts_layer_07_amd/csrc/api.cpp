@@ -168,7 +168,7 @@ moe_status moe_update_bias(int32_t n_experts, const int32_t* counts, float* bias
 
 moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
-                       void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
+                       void* x_perm, void* x_perm_scale, void* ws, size_t ws_bytes,
                        void* stream) {
   MOE_TRY(checked_config(cfg));
   const moe_config& c = *cfg;
@@ -176,10 +176,11 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
     return fail(MOE_ERR_INVALID_ARG, "moe_permute: NULL buffer");
   if ((x == nullptr) != (x_perm == nullptr))
     return fail(MOE_ERR_INVALID_ARG, "moe_permute: x and x_perm must both be given or both NULL");
-  if (x && c.dtype == MOE_FP8_E4M3 && !x_perm_scale)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: fp8 layers need x_perm_scale");
-  if (c.dtype != MOE_FP8_E4M3 && x_perm_scale)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: x_perm_scale is only for fp8 layers");
+  const bool quant = c.dtype == MOE_FP8_E4M3 || c.dtype == MOE_MXFP4;
+  if (x && quant && !x_perm_scale)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: fp8 and MX layers need x_perm_scale");
+  if (!quant && x_perm_scale)
+    return fail(MOE_ERR_INVALID_ARG, "moe_permute: x_perm_scale is only for fp8 and MX layers");
   WsLayout L;
   MOE_TRY(check_ws(c, ws, ws_bytes, &L));
   MOE_TRY(ensure_device());
@@ -202,9 +203,9 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
 // gather[i] / cfg->K, x holding T rows).
 static moe_status expert_ffn(const char* where, const moe_config* cfg, int32_t n_experts,
                              int32_t n_rows, int32_t inter, const int32_t* offsets,
-                             const int32_t* gather, const void* x, const float* x_scale,
-                             const void* w13, const float* w13_scale, const void* w2,
-                             const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                             const int32_t* gather, const void* x, const void* x_scale,
+                             const void* w13, const void* w13_scale, const void* w2,
+                             const void* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
                              void* stream) {
   MOE_TRY(checked_config(cfg));
   const moe_config& c = *cfg;
@@ -214,18 +215,18 @@ static moe_status expert_ffn(const char* where, const moe_config* cfg, int32_t n
   const int64_t P = (int64_t)c.T * c.K;
   if (n_rows < 0 || n_rows > P) return fail(MOE_ERR_INVALID_ARG, w + ": n_rows must be in [0, T*K]");
   const int maxI = c.I > c.I_shared ? c.I : c.I_shared;
-  const int q = c.dtype == MOE_F32 ? 4 : 128;
+  const int q = channel_multiple(c.dtype);
   if (inter < 1 || inter > maxI || inter % q)
-    return fail(MOE_ERR_INVALID_ARG,
-                w + ": inter must be in [1, max(I, I_shared)] and a multiple of 128 (4 for fp32)");
+    return fail(MOE_ERR_INVALID_ARG, w + ": inter must be in [1, max(I, I_shared)] and a multiple of " +
+                                         std::to_string(q));
   if (!offsets || !x || !w13 || !w2 || !y_rows) return fail(MOE_ERR_INVALID_ARG, w + ": NULL buffer");
-  const bool fp8 = c.dtype == MOE_FP8_E4M3;
-  if (fp8 && (!x_scale || !w13_scale || !w2_scale))
-    return fail(MOE_ERR_INVALID_ARG, w + ": fp8 layers need x_scale, w13_scale, w2_scale");
-  if (!fp8 && (x_scale || w13_scale || w2_scale))
-    return fail(MOE_ERR_INVALID_ARG, w + ": scales are only for fp8 layers");
+  const bool quant = c.dtype == MOE_FP8_E4M3 || c.dtype == MOE_MXFP4;
+  if (quant && (!x_scale || !w13_scale || !w2_scale))
+    return fail(MOE_ERR_INVALID_ARG, w + ": fp8 and MX layers need x_scale, w13_scale, w2_scale");
+  if (!quant && (x_scale || w13_scale || w2_scale))
+    return fail(MOE_ERR_INVALID_ARG, w + ": scales are only for fp8 and MX layers");
   if (gather) {
-    const int64_t xb = c.dtype == MOE_F32 ? 4 : (fp8 ? 1 : 2);
+    const int64_t xb = c.dtype == MOE_F32 ? 4 : (quant ? 1 : 2);
     if ((int64_t)c.T * c.H * xb >= (int64_t(1) << 32))
       return fail(MOE_ERR_UNSUPPORTED, w + ": x above 4 GiB cannot be gathered (use moe_permute's x_perm)");
   }
@@ -251,7 +252,7 @@ static moe_status expert_ffn(const char* where, const moe_config* cfg, int32_t n
   a.w2_scale = w2_scale;
   a.y = y_rows;
   a.h = at<void>(ws, L.h);
-  a.h_scale = fp8 ? at<float>(ws, L.hscale) : nullptr;
+  a.h_scale = quant ? at<void>(ws, L.hscale) : nullptr;
   a.tiles = at<int32_t>(ws, L.tiles);
   a.part = at<float>(ws, L.part);
   MOE_HIP(launch_expert_ffn(a, static_cast<hipStream_t>(stream)), "expert_ffn");
@@ -261,9 +262,9 @@ static moe_status expert_ffn(const char* where, const moe_config* cfg, int32_t n
 extern "C" {
 
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_rows, int32_t inter,
-                          const int32_t* offsets, const void* x_rows, const float* x_scale,
-                          const void* w13, const float* w13_scale, const void* w2,
-                          const float* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
+                          const int32_t* offsets, const void* x_rows, const void* x_scale,
+                          const void* w13, const void* w13_scale, const void* w2,
+                          const void* w2_scale, void* y_rows, void* ws, size_t ws_bytes,
                           void* stream) {
   return expert_ffn("moe_expert_ffn", cfg, n_experts, n_rows, inter, offsets, nullptr, x_rows, x_scale,
                     w13, w13_scale, w2, w2_scale, y_rows, ws, ws_bytes, stream);
@@ -271,8 +272,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_ro
 
 moe_status moe_expert_ffn_gather(const moe_config* cfg, int32_t n_experts, int32_t n_rows,
                                  int32_t inter, const int32_t* offsets, const int32_t* sorted_pair,
-                                 const void* x, const float* x_scale, const void* w13,
-                                 const float* w13_scale, const void* w2, const float* w2_scale,
+                                 const void* x, const void* x_scale, const void* w13,
+                                 const void* w13_scale, const void* w2, const void* w2_scale,
                                  void* y_rows, void* ws, size_t ws_bytes, void* stream) {
   if (!sorted_pair) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn_gather: NULL buffer");
   return expert_ffn("moe_expert_ffn_gather", cfg, n_experts, n_rows, inter, offsets, sorted_pair, x,
@@ -302,6 +303,20 @@ moe_status moe_quantize_fp8(int32_t rows, int32_t cols, const void* in, uint8_t*
   MOE_TRY(ensure_device());
   MOE_HIP(launch_quantize_fp8(rows, cols, in, codes, scales, static_cast<hipStream_t>(stream)),
           "quantize_fp8");
+  return MOE_OK;
+}
+
+moe_status moe_quantize_mx(int32_t rows, int32_t cols, const void* in, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 128 || cols % 128)
+    return fail(MOE_ERR_INVALID_ARG, "moe_quantize_mx: rows >= 0, cols a positive multiple of 128");
+  if ((int64_t)rows * cols >= (int64_t(1) << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_quantize_mx: too large");
+  if (!in || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "moe_quantize_mx: NULL buffer");
+  if (rows == 0) return MOE_OK;
+  MOE_TRY(ensure_device());
+  MOE_HIP(launch_quantize_mx(rows, cols, in, codes, scales, static_cast<hipStream_t>(stream)),
+          "quantize_mx");
   return MOE_OK;
 }
 

@@ -14,18 +14,18 @@ namespace moe {
 struct GemmArgs {
   const uint8_t* A;
   size_t lda;           // bytes per A row
-  const float* a_scale; // fp8: [rows][K/128]
-  int a_scale_ld;
+  const float* a_scale; // fp8: [rows][K/128] fp32; MX: [K/128][a_scale_ld] words of four E8M0 codes
+  int a_scale_ld;       // fp8: K/128; MX: rows of the scale array
   const uint8_t* B;
   size_t ldb;           // bytes per B row
   size_t b_exp;         // bytes per expert
-  const float* b_scale; // fp8: [n_exp][Nb/128][K/128]
-  int b_scale_ld;       // K/128
-  size_t b_scale_exp;   // floats per expert
+  const float* b_scale; // fp8: [n_exp][Nb/128][K/128] fp32; MX: [n_exp][K/128][Nb] words
+  int b_scale_ld;       // fp8: K/128; MX: Nb
+  size_t b_scale_exp;   // fp8: floats per expert; MX: words per expert
   uint8_t* C;
   size_t ldc;           // bytes per C row
-  float* c_scale;       // fp8 GLU output: [rows][N_out/128]
-  int c_scale_ld;
+  float* c_scale;       // fp8 GLU output: [rows][N_out/128] fp32; MX: [N_out/128][c_scale_ld] words
+  int c_scale_ld;       // fp8: N_out/128; MX: rows
   const int32_t* offsets;
   const int32_t* a_rows;  // gathered A rows (Linear-1 on the activations in place), or nullptr
   int a_div, a_limit;     // grouped row i reads A row min(a_rows[i] / a_div, a_limit - 1)
@@ -288,8 +288,14 @@ __device__ __forceinline__ void dma_wait_and_barrier() {
   __syncthreads();
 }
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) for "all
+// LDS operations done and at most n vector memory operations outstanding"; as the builtin, the
+// compiler's own wait insertion accounts for it.
+__host__ __device__ constexpr int f8_wait_lgkm0_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
 // Declared launchers (kernels_gemm_*.hip)
 hipError_t launch_gemm_bf16(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s);
+hipError_t launch_gemm_mx(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s);
 
 }  // namespace moe

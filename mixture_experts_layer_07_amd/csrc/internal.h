@@ -21,7 +21,7 @@ namespace moe {
 //   base     [perm_blocks][E] int32 per-block starting rank inside each expert
 //   tiles    [2][257] int32 m-tile prefix sums of the grouped GEMMs
 //   h        [max_rows][max_I] SwiGLU output (fp32 / bf16 / e4m3 codes)
-//   hscale   [max_rows][max_I/128] fp32 (fp8 layer)
+//   hscale   [max_rows][max_I/128] fp32 (fp8 layer) / [max_I/128][rows] E8M0 words (MX layer)
 struct WsLayout {
   size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, part = 0, h = 0, hscale = 0, total = 0;
   int route_splits = 1;
@@ -35,6 +35,8 @@ constexpr int kTileMetaInts = 1024;  // tile metadata of the expert GEMMs (prefi
 // Validation; returns MOE_OK or the failure status with a reason in *why.
 moe_status check_routing(const moe_config* c, std::string* why);
 moe_status check_config(const moe_config* c, std::string* why);
+// H, I and I_shared (and the inter of an expert call) must be multiples of this.
+int channel_multiple(int dtype);
 // Workspace layout of a valid config.
 WsLayout layout(const moe_config& c);
 // Router split-K factor chosen from the shape (deterministic, host-side).
@@ -88,25 +90,27 @@ hipError_t launch_perm_scatter(const int32_t* ids, int P, int E, const int32_t* 
                                const int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                                int32_t* pair_pos, hipStream_t s);
 hipError_t launch_gather(const moe_config& c, const int32_t* sorted_pair, const void* x,
-                         void* x_perm, float* x_scale, hipStream_t s);
+                         void* x_perm, void* x_scale, hipStream_t s);
 hipError_t launch_quantize_fp8(int rows, int cols, const void* in, uint8_t* codes, float* scales,
                                hipStream_t s);
+hipError_t launch_quantize_mx(int rows, int cols, const void* in, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
 // expert FFN
 struct FfnArgs {
   int dtype = MOE_BF16;
   int n_exp = 0, n_rows = 0, H = 0, I = 0;
   const int32_t* offsets = nullptr;
   const void* x = nullptr;
-  const float* x_scale = nullptr;
+  const void* x_scale = nullptr;   // fp32 (fp8) or E8M0 words (MX)
   const int32_t* x_rows_index = nullptr;  // Linear-1 gathers row i from x row x_rows_index[i] / x_rows_div
   int x_rows_div = 1, x_rows_limit = 0;
   const void* w13 = nullptr;
-  const float* w13_scale = nullptr;
+  const void* w13_scale = nullptr;
   const void* w2 = nullptr;
-  const float* w2_scale = nullptr;
+  const void* w2_scale = nullptr;
   void* y = nullptr;
   void* h = nullptr;          // workspace
-  float* h_scale = nullptr;   // workspace (fp8)
+  void* h_scale = nullptr;    // workspace (fp8, MX)
   int32_t* tiles = nullptr;   // workspace, kTileMetaInts
   float* part = nullptr;      // workspace, partial tiles of K-split GEMM tiles
 };

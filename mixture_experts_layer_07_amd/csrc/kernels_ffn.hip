@@ -186,43 +186,60 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid), dim3(256), 0, s, g2);
     });
   }
-  const bool fp8 = a.dtype == MOE_FP8_E4M3;
-  const size_t es = fp8 ? 1 : 2;
+  const bool fp8 = a.dtype == MOE_FP8_E4M3, mx = a.dtype == MOE_MXFP4;
+  const size_t es = fp8 || mx ? 1 : 2;  // bytes per activation element
+  const size_t ws_ = mx ? 1 : es * 2;   // bytes per two weight elements
   g1.A = static_cast<const uint8_t*>(a.x);
   g1.lda = (size_t)H * es;
   g1.B = static_cast<const uint8_t*>(a.w13);
-  g1.ldb = (size_t)H * es;
-  g1.b_exp = (size_t)2 * I * H * es;
+  g1.ldb = (size_t)H * ws_ / 2;
+  g1.b_exp = (size_t)2 * I * H * ws_ / 2;
   g1.C = static_cast<uint8_t*>(a.h);
   g1.ldc = (size_t)I * es;
   g1.n_tiles_n = I / 128;
   g2.A = static_cast<const uint8_t*>(a.h);
   g2.lda = (size_t)I * es;
   g2.B = static_cast<const uint8_t*>(a.w2);
-  g2.ldb = (size_t)I * es;
-  g2.b_exp = (size_t)H * I * es;
+  g2.ldb = (size_t)I * ws_ / 2;
+  g2.b_exp = (size_t)H * I * ws_ / 2;
   g2.C = static_cast<uint8_t*>(a.y);
-  g2.ldc = (size_t)H * (fp8 ? 2 : 4);  // y rows: fp32 for bf16 layers, bf16 for fp8 layers
+  g2.ldc = (size_t)H * (fp8 || mx ? 2 : 4);  // y rows: fp32 for bf16 layers, bf16 for fp8 / MX layers
   g2.n_tiles_n = (H + 255) / 256;
+  g1.a_scale = static_cast<const float*>(a.x_scale);
+  g1.b_scale = static_cast<const float*>(a.w13_scale);
+  g1.c_scale = static_cast<float*>(a.h_scale);
+  g2.a_scale = static_cast<const float*>(a.h_scale);
+  g2.b_scale = static_cast<const float*>(a.w2_scale);
   if (fp8) {
-    g1.a_scale = a.x_scale;
     g1.a_scale_ld = H / 128;
-    g1.b_scale = a.w13_scale;
     g1.b_scale_ld = H / 128;
     g1.b_scale_exp = (size_t)(2 * I / 128) * (H / 128);
-    g1.c_scale = a.h_scale;
     g1.c_scale_ld = I / 128;
-    g2.a_scale = a.h_scale;
     g2.a_scale_ld = I / 128;
-    g2.b_scale = a.w2_scale;
     g2.b_scale_ld = I / 128;
     g2.b_scale_exp = (size_t)(H / 128) * (I / 128);
+  }
+  if (mx) {
+    // [K/128][rows] words: the scale arrays' row counts; Linear-1 gathers x rows (T of them) or
+    // reads the n_rows grouped rows
+    g1.a_scale_ld = a.x_rows_index ? a.x_rows_limit : a.n_rows;
+    g1.b_scale_ld = 2 * I;
+    g1.b_scale_exp = (size_t)(H / 128) * 2 * I;
+    g1.c_scale_ld = a.n_rows;
+    g2.a_scale_ld = a.n_rows;
+    g2.b_scale_ld = H;
+    g2.b_scale_exp = (size_t)(I / 128) * H;
   }
   // Tile shape from the mean rows per expert (a host-side choice; the API has no knob): large M
   // tiles when experts are well filled (weights then stream once per n-tile) and the large tiles
   // still cover every CU, 32-row tiles for decode-sized row groups.
   const int avg = a.n_rows / a.n_exp;
   auto enough = [&](int bm) { return (long)((a.n_rows + bm - 1) / bm) * g1.n_tiles_n >= cus; };
+  if (mx) {
+    const int variant = avg >= 64 && enough(128) ? 2 : 1;
+    if ((e = build_tiles(a, variant == 2 ? 128 : 32, a.tiles, s)) != hipSuccess) return e;
+    return launch_gemm_mx(g1, g2, variant, cus, s);
+  }
   if (!fp8) {
     const int variant = avg >= 128 && enough(256) ? 0 : 1;
     if ((e = build_tiles(a, variant == 0 ? 256 : 32, a.tiles, s)) != hipSuccess) return e;

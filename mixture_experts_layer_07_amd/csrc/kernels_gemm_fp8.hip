@@ -58,11 +58,6 @@ __device__ __forceinline__ void mma_step_fp8(const u32x4* sta, const u32x4* stb,
   }
 }
 
-// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8) for "all
-// LDS operations done and at most n vector memory operations outstanding"; as the builtin, the
-// compiler's own wait insertion accounts for it.
-__host__ __device__ constexpr int f8_wait_lgkm0_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
-
 // 128- or 32-row tiles, NWM x NWN waves. One K step is 128 channels (one scale block) through two
 // LDS stages, each an A array, a B array and the step's row scales. A and the row scales are
 // filled by direct-to-LDS loads one step ahead; the weights stream through registers two steps

@@ -138,15 +138,19 @@ hipError_t launch_perm_scatter(const int32_t* ids, int P, int E, const int32_t* 
   });
 }
 
-// ------------------------------------------------------------------ gather / fp8 quantise
+// ------------------------------------------------------------------ gather / fp8 and MX quantise
 // One wave per destination row. bf16 / fp32: 16-byte copies. fp8: the bf16 row is read in
 // 128-channel blocks (16 lanes x 8 channels), the block absmax is reduced over its 16 lanes,
 // scale = absmax / 448 and each value is encoded as e4m3(v / scale) (IEEE fp32 divisions).
-template <int MODE>  // 0: copy 16-byte chunks, 1: bf16 -> e4m3 + scales
+// MX (OCP microscaling, MXFP8): the same 128-channel groups, each 4 x 32-channel blocks of 4
+// lanes; a block's E8M0 code is the binary exponent of its absmax minus 8, clamped at 0
+// (= floor(log2 absmax) - 8 + 127), its values e4m3(v * 2^(127 - code)) (an exact power-of-two
+// scaling); the four codes of a group are one word of the [cols/128][rows] scale array.
+template <int MODE>  // 0: copy 16-byte chunks, 1: bf16 -> e4m3 + fp32 scales, 2: bf16 -> MXFP8
 __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ sorted_pair, int K,
                                                 int rows, int nsrc, const uint8_t* __restrict__ x,
                                                 size_t row_bytes, uint8_t* __restrict__ out,
-                                                float* __restrict__ scales, int cols) {
+                                                void* __restrict__ scales, int cols) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= rows) return;
@@ -175,26 +179,47 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ sort
       float m = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+      if (MODE == 1) {
 #pragma unroll
-      for (int o2 = 1; o2 < 16; o2 <<= 1) m = fmaxf(m, __shfl_xor(m, o2, 64));
-      const float scale = m / 448.0f;
-      uint32_t lo = 0, hi = 0;
-      if (m > 0.f) {
+        for (int o2 = 1; o2 < 16; o2 <<= 1) m = fmaxf(m, __shfl_xor(m, o2, 64));
+        const float scale = m / 448.0f;
+        uint32_t lo = 0, hi = 0;
+        if (m > 0.f) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] / scale) << (8 * j);
+          for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] / scale) << (8 * j);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[4 + j] / scale) << (8 * j);
-      }
-      if (act) {
-        reinterpret_cast<uint2*>(o)[(size_t)b * 16 + (lane & 15)] = make_uint2(lo, hi);
-        if ((lane & 15) == 0) scales[(size_t)i * nblk + b] = scale;
+          for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[4 + j] / scale) << (8 * j);
+        }
+        if (act) {
+          reinterpret_cast<uint2*>(o)[(size_t)b * 16 + (lane & 15)] = make_uint2(lo, hi);
+          if ((lane & 15) == 0) static_cast<float*>(scales)[(size_t)i * nblk + b] = scale;
+        }
+      } else {
+        // 32-channel block = 4 lanes
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        const int ex = (int)(__float_as_uint(m) >> 23);
+        const int code = ex > 8 ? ex - 8 : 0;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(v[j], 127 - code)) << (8 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(v[4 + j], 127 - code)) << (8 * j);
+        const int base = lane & ~15;
+        uint32_t word = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) word |= (uint32_t)__shfl(code, base + 4 * q, 64) << (8 * q);
+        if (act) {
+          reinterpret_cast<uint2*>(o)[(size_t)b * 16 + (lane & 15)] = make_uint2(lo, hi);
+          if ((lane & 15) == 0) static_cast<uint32_t*>(scales)[(size_t)b * rows + i] = word;
+        }
       }
     }
   }
 }
 
 hipError_t launch_gather(const moe_config& c, const int32_t* sorted_pair, const void* x,
-                         void* x_perm, float* x_scale, hipStream_t s) {
+                         void* x_perm, void* x_scale, hipStream_t s) {
   const int P = c.T * c.K;
   const dim3 grid((P + 3) / 4);
   const uint8_t* xi = static_cast<const uint8_t*>(x);
@@ -202,6 +227,11 @@ hipError_t launch_gather(const moe_config& c, const int32_t* sorted_pair, const 
   if (c.dtype == MOE_FP8_E4M3)
     return timed_launch("gather_quant_fp8", s, [&] {
       hipLaunchKernelGGL(k_gather<1>, grid, dim3(256), 0, s, sorted_pair, c.K, P, c.T, xi,
+                         (size_t)c.H * 2, xo, x_scale, c.H);
+    });
+  if (c.dtype == MOE_MXFP4)
+    return timed_launch("gather_quant_mx", s, [&] {
+      hipLaunchKernelGGL(k_gather<2>, grid, dim3(256), 0, s, sorted_pair, c.K, P, c.T, xi,
                          (size_t)c.H * 2, xo, x_scale, c.H);
     });
   const size_t rb = (size_t)c.H * (c.dtype == MOE_F32 ? 4 : 2);
@@ -215,6 +245,14 @@ hipError_t launch_quantize_fp8(int rows, int cols, const void* in, uint8_t* code
                                hipStream_t s) {
   return timed_launch("quantize_fp8", s, [&] {
     hipLaunchKernelGGL(k_gather<1>, dim3((rows + 3) / 4), dim3(256), 0, s, nullptr, 1, rows, rows,
+                       static_cast<const uint8_t*>(in), (size_t)cols * 2, codes, scales, cols);
+  });
+}
+
+hipError_t launch_quantize_mx(int rows, int cols, const void* in, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s) {
+  return timed_launch("quantize_mx", s, [&] {
+    hipLaunchKernelGGL(k_gather<2>, dim3((rows + 3) / 4), dim3(256), 0, s, nullptr, 1, rows, rows,
                        static_cast<const uint8_t*>(in), (size_t)cols * 2, codes, scales, cols);
   });
 }

@@ -10,6 +10,8 @@ namespace moe {
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+int channel_multiple(int dtype) { return dtype == MOE_F32 ? 4 : (dtype == MOE_MXFP4 ? 256 : 128); }
+
 // The fields scoring and selection read: T, E, K, the score function, renorm, route_scale and
 // the group rule.
 moe_status check_routing(const moe_config* c, std::string* why) {
@@ -50,14 +52,15 @@ moe_status check_config(const moe_config* c, std::string* why) {
   const moe_status r = check_routing(c, why);
   if (r != MOE_OK) return r;
   if (c->H < 1 || c->I < 1) return bad(MOE_ERR_INVALID_ARG, "T, H, I, E and K must be positive");
-  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8_E4M3)
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8_E4M3 && c->dtype != MOE_MXFP4)
     return bad(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (c->I_shared < 0) return bad(MOE_ERR_INVALID_ARG, "I_shared must be >= 0");
-  const int q = (c->dtype == MOE_F32) ? 4 : 128;
+  const int q = channel_multiple(c->dtype);
   if (c->H % q || c->I % q || c->I_shared % q)
     return bad(MOE_ERR_UNSUPPORTED,
-               c->dtype == MOE_F32 ? "fp32 layers need H, I, I_shared multiples of 4"
-                                   : "bf16/fp8 layers need H, I, I_shared multiples of 128");
+               c->dtype == MOE_F32     ? "fp32 layers need H, I, I_shared multiples of 4"
+               : c->dtype == MOE_MXFP4 ? "MXFP4 layers need H, I, I_shared multiples of 256"
+                                       : "bf16/fp8 layers need H, I, I_shared multiples of 128");
   const int64_t P = (int64_t)c->T * c->K;
   if (P >= (int64_t(1) << 31)) return bad(MOE_ERR_INVALID_ARG, "T*K must be below 2^31");
   const int64_t maxI = c->I > c->I_shared ? c->I : c->I_shared;
@@ -102,8 +105,8 @@ WsLayout layout(const moe_config& c) {
   const size_t elem = c.dtype == MOE_F32 ? 4 : (c.dtype == MOE_BF16 ? 2 : 1);
   L.h = off;
   off = align256(off + P * maxI * elem);
-  L.hscale = off;
-  off = align256(off + (c.dtype == MOE_FP8_E4M3 ? P * (maxI / 128) * 4 : 0));
+  L.hscale = off;  // fp8: one fp32 per row per 128 channels; MX: one word of four E8M0 codes
+  off = align256(off + (c.dtype == MOE_FP8_E4M3 || c.dtype == MOE_MXFP4 ? P * (maxI / 128) * 4 : 0));
   L.total = off;
   return L;
 }

@@ -15,11 +15,17 @@ Recipe (weights drawn N(0, 1/fan_in), i.e. variance 1/fan_in):
   logits   (routing-only workloads) N(0,1) [T,E] fp32, the unit logit spread of the layers
   fp8      weights drawn in fp32 as above, then per 128x128 block scale = absmax/448
            and codes = e4m3(w / scale) via torch's float8_e4m3fn cast.
+  mxfp4    weights drawn directly as codes: packed e2m1 bytes uniform over 0..255 (each nibble
+           uniform over the 16 codes, rms value 2.93) and one E8M0 code per 32 channels,
+           b + U{-1,0,1} (rms factor 1.32) with b = 127 + round(log2(fan_in^-1/2 / (2.93 * 1.32))),
+           so that the weights have about the N(0,1/fan_in) spread of the other layers (119 for
+           H = 7168, 120 for I = 2048); scale codes in the library's [in/128][out rows][4] layout.
 Generator seed: (seed << 24) | (tensor_id << 16) | expert.
 x, W_r and the bias are drawn on the CPU (so every machine sees the same
 values); the expert weights are drawn on `device` with one generator per
 (tensor, expert), so any single expert can be regenerated on its own.
 """
+import math
 import os
 
 import torch
@@ -92,13 +98,30 @@ def fp8_block_quantise(w):
     return codes, s.contiguous()
 
 
+E2M1_RMS = 2.93 * 1.32  # rms of a uniform e2m1 code times that of 2^j, j uniform in {-1, 0, 1}
+
+
+def mx_weight(rows, cols, seed, tensor, expert, device):
+    """Random MXFP4 weight [rows, cols]: (packed codes [rows, cols/2] uint8, E8M0 scale codes
+    [cols/128, rows, 4] uint8)."""
+    g = _gen(seed, tensor, expert, device)
+    codes = torch.randint(0, 256, (rows, cols // 2), generator=g, device=device, dtype=torch.uint8)
+    base = 127 + round(math.log2(cols ** -0.5 / E2M1_RMS))
+    jit = torch.randint(-1, 2, (cols // 128, rows, 4), generator=g, device=device, dtype=torch.int32)
+    return codes, (base + jit).to(torch.uint8)
+
+
 def expert_weights(cfg: LayerConfig, e, device="cpu", shared=False):
     """(w13 [2I,H], w2 [H,I]) of routed expert e (or the shared expert) in the layer dtype.
 
-    For fp8 returns (w13_codes, w13_scale, w2_codes, w2_scale).
+    For fp8 and mxfp4 returns (w13_codes, w13_scale, w2_codes, w2_scale).
     """
     I = cfg.I_shared if shared else cfg.I
     t13, t2 = ("w13s", "w2s") if shared else ("w13", "w2")
+    if cfg.dtype == "mxfp4":
+        c13, s13 = mx_weight(2 * I, cfg.H, cfg.seed, t13, e, device)
+        c2, s2 = mx_weight(cfg.H, I, cfg.seed, t2, e, device)
+        return c13, s13, c2, s2
     w13 = _randn((2 * I, cfg.H), cfg.H ** -0.5, cfg.seed, t13, e, device)
     w2 = _randn((cfg.H, I), I ** -0.5, cfg.seed, t2, e, device)
     if cfg.dtype == "f32":
@@ -114,6 +137,15 @@ def make_expert_weights(cfg: LayerConfig, device="cpu", shared=False):
     """Stacked expert weights on `device`: dict with w13 [n,2I,H], w2 [n,H,I] (+ scales for fp8)."""
     n = 1 if shared else cfg.E
     I = cfg.I_shared if shared else cfg.I
+    if cfg.dtype == "mxfp4":
+        u8 = dict(dtype=torch.uint8, device=device)
+        w13 = torch.empty((n, 2 * I, cfg.H // 2), **u8)
+        w2 = torch.empty((n, cfg.H, I // 2), **u8)
+        s13 = torch.empty((n, cfg.H // 128, 2 * I, 4), **u8)
+        s2 = torch.empty((n, I // 128, cfg.H, 4), **u8)
+        for e in range(n):
+            w13[e], s13[e], w2[e], s2[e] = expert_weights(cfg, e, device, shared)
+        return {"w13": w13, "w2": w2, "w13_scale": s13, "w2_scale": s2}
     if cfg.dtype == "fp8":
         w13 = torch.empty((n, 2 * I, cfg.H), dtype=torch.uint8, device=device)
         w2 = torch.empty((n, cfg.H, I), dtype=torch.uint8, device=device)

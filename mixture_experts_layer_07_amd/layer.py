@@ -1,8 +1,8 @@
 """One MoE layer forward on torch device buffers: the C-ABI calls in order.
 
 route -> permute -> expert FFN (routed experts, then the shared expert if any) -> combine.
-With gather=True (the default) the permute stage only builds the pair order (and, for fp8,
-quantises the T input rows once) and Linear-1 of the routed experts reads the token rows in
+With gather=True (the default) the permute stage only builds the pair order (and, for fp8 and
+MX layers, quantises the T input rows once) and Linear-1 of the routed experts reads the token rows in
 place (moe_expert_ffn_gather); with gather=False the permute stage also writes the permuted
 copy x_perm that moe_expert_ffn reads. Buffers are allocated once at construction and reused by
 every forward; the calls are enqueued on the current stream and none of them waits.
@@ -16,7 +16,7 @@ from .configs import LayerConfig
 class MoELayer:
     def __init__(self, cfg: LayerConfig, w_router, bias, experts, shared=None, device="cuda",
                  gather=True):
-        """experts / shared: dicts with w13, w2 (+ w13_scale, w2_scale for fp8) on `device`."""
+        """experts / shared: dicts with w13, w2 (+ w13_scale, w2_scale for fp8 / mxfp4) on `device`."""
         self.cfg = cfg
         self.gather = gather
         self.c = B.make_config(cfg)
@@ -24,6 +24,8 @@ class MoELayer:
         T, H, E, K, P = cfg.T, cfg.H, cfg.E, cfg.K, cfg.P
         act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
         self.fp8 = cfg.dtype == "fp8"
+        self.mx = cfg.dtype == "mxfp4"
+        self.quant = self.fp8 or self.mx   # experts read e4m3 codes plus scales
         dev = torch.device(device)
         self.w_router = w_router
         self.bias = bias
@@ -40,16 +42,16 @@ class MoELayer:
         self.pair_pos = torch.empty(P, **i32)
         self.x_perm = self.x_perm_scale = None
         if not gather:
-            self.x_perm = torch.empty((P, H), dtype=torch.uint8 if self.fp8 else act, device=dev)
-            if self.fp8:
-                self.x_perm_scale = torch.empty((P, H // 128), dtype=torch.float32, device=dev)
+            self.x_perm = torch.empty((P, H), dtype=torch.uint8 if self.quant else act, device=dev)
+            if self.quant:
+                self.x_perm_scale = self._scales(P, H, dev)
         self.xq = self.xq_scale = None
-        if self.fp8 and (gather or self.shared is not None):
+        if self.quant and (gather or self.shared is not None):
             # the e4m3 codes of the T input rows, read by the gathered Linear-1 and the shared expert
             self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
-            self.xq_scale = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
-        # expert outputs: fp32 accumulators for fp32 / bf16 layers, bf16 for the fp8 layer
-        ydt = torch.bfloat16 if self.fp8 else torch.float32
+            self.xq_scale = self._scales(T, H, dev)
+        # expert outputs: fp32 accumulators for fp32 / bf16 layers, bf16 for the fp8 / MX layers
+        ydt = torch.bfloat16 if self.quant else torch.float32
         self.y_perm = torch.empty((P, H), dtype=ydt, device=dev)
         self.out = torch.empty((T, H), dtype=act, device=dev)
         if self.shared is not None:
@@ -58,6 +60,16 @@ class MoELayer:
         else:
             self.y_shared = None
 
+    def _scales(self, rows, cols, dev):
+        """fp8: [rows, cols/128] fp32; MX: the [cols/128][rows][4] E8M0 code array."""
+        if self.mx:
+            return torch.empty((cols // 128, rows, 4), dtype=torch.uint8, device=dev)
+        return torch.empty((rows, cols // 128), dtype=torch.float32, device=dev)
+
+    def _quantize(self, x):
+        q = B.moe_quantize_mx if self.mx else B.moe_quantize_fp8
+        q(self.cfg.T, self.cfg.H, x, self.xq, self.xq_scale)
+
     def route(self, x):
         B.moe_route(self.c, x, self.w_router, self.bias, self.topk_ids, self.topk_weights, self.ws)
 
@@ -65,8 +77,8 @@ class MoELayer:
         if self.gather:
             B.moe_permute(self.c, self.topk_ids, self.counts, self.offsets, self.sorted_pair,
                           self.pair_pos, None, None, None, self.ws)
-            if self.fp8:
-                B.moe_quantize_fp8(self.cfg.T, self.cfg.H, x, self.xq, self.xq_scale)
+            if self.quant:
+                self._quantize(x)
         else:
             B.moe_permute(self.c, self.topk_ids, self.counts, self.offsets, self.sorted_pair,
                           self.pair_pos, x, self.x_perm, self.x_perm_scale, self.ws)
@@ -74,7 +86,7 @@ class MoELayer:
     def expert_ffn(self, x):
         ex = self.experts
         if self.gather:
-            xs, xs_scale = (self.xq, self.xq_scale) if self.fp8 else (x, None)
+            xs, xs_scale = (self.xq, self.xq_scale) if self.quant else (x, None)
             B.moe_expert_ffn_gather(self.c, self.cfg.E, self.cfg.P, self.cfg.I, self.offsets,
                                     self.sorted_pair, xs, xs_scale, ex["w13"], ex.get("w13_scale"),
                                     ex["w2"], ex.get("w2_scale"), self.y_perm, self.ws)
@@ -88,9 +100,9 @@ class MoELayer:
             return
         sh = self.shared
         xs, xs_scale = x, None
-        if self.fp8:
+        if self.quant:
             if not self.gather:  # (with gather the permute stage has quantised x already)
-                B.moe_quantize_fp8(self.cfg.T, self.cfg.H, x, self.xq, self.xq_scale)
+                self._quantize(x)
             xs, xs_scale = self.xq, self.xq_scale
         B.moe_expert_ffn(self.c, 1, self.cfg.T, self.cfg.I_shared, self.shared_offsets, xs, xs_scale,
                          sh["w13"], sh.get("w13_scale"), sh["w2"], sh.get("w2_scale"),

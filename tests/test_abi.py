@@ -59,6 +59,9 @@ def test_check_config(lib):
     c = cfg(1)
     c.H = 130          # fp32 needs multiples of 4
     assert lib.moe_check_config(ctypes.byref(c)) == UNSUPPORTED
+    for kw in (dict(H=7168 + 128), dict(I=2048 + 128), dict(I_shared=384)):  # MX: multiples of 256
+        assert lib.moe_check_config(ctypes.byref(cfg(7, **kw))) == UNSUPPORTED, kw
+    assert lib.moe_check_config(ctypes.byref(cfg(7, H=512, I=256, I_shared=256))) == OK
     assert lib.moe_check_config(None) == INVALID
 
 
@@ -67,7 +70,7 @@ def test_workspace_size(lib):
         c = B.make_config(CONFIGS[i])
         n = lib.moe_workspace_size(ctypes.byref(c))
         cf = CONFIGS[i]
-        elem = {"f32": 4, "bf16": 2, "fp8": 1}[cf.dtype]
+        elem = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 1}[cf.dtype]
         assert n >= cf.P * max(cf.I, cf.I_shared) * elem
         assert n % 256 == 0
     c = cfg(3, E=257)
@@ -103,6 +106,18 @@ def test_entry_points_validate_before_device(lib):
     assert lib.moe_combine(pc, None, FAKE, FAKE, None, FAKE, None) == INVALID
     assert lib.moe_quantize_fp8(4, 100, FAKE, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_fp8(4, 256, None, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_mx(4, 100, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_mx(-1, 256, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_quantize_mx(4, 256, FAKE, FAKE, None, None) == INVALID
+    cm = cfg(7, T=64, H=256, I=256, E=16, K=4, n_group=4, topk_group=2, I_shared=256)
+    pm = ctypes.byref(cm)
+    nm = lib.moe_workspace_size(pm)
+    assert lib.moe_expert_ffn(pm, 16, 256, 256, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                              nm, None) == INVALID                           # MX without w13_scale
+    assert lib.moe_expert_ffn(pm, 16, 256, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              nm, None) == INVALID                           # MX inter not a multiple of 256
+    assert lib.moe_permute(pm, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, nm,
+                           None) == INVALID                                  # MX without x_perm_scale
     assert lib.moe_get_device_error(None, ctypes.byref(ctypes.c_int32()), None) == INVALID
     # logits-only routing reads only the routing fields: H, I and dtype are not checked
     cr = cfg(3, T=83, E=256, K=8, n_group=8, topk_group=4)

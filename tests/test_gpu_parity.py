@@ -34,6 +34,10 @@ SMALL = {
     "decode-fp8": (CONFIGS[5].scaled(T=24, H=256, I=2048, E=64, K=8, I_shared=2048), None),
     "fp32-grouped": (CONFIGS[3].scaled(T=100, H=64, I=96, E=16, K=4, n_group=4, topk_group=2,
                                        dtype="f32", I_shared=32), None),
+    # MX: 128-row tiles with an odd K-step count in Linear-1 (H = 768: 3 steps of 256 channels),
+    # and 32-row tiles with an even one
+    "dsv3-mxfp4": (CONFIGS[7].scaled(T=260, H=768, I=2048, E=32, K=8, I_shared=2048), None),
+    "decode-mxfp4": (CONFIGS[7].scaled(T=24, H=512, I=2048, E=64, K=8, I_shared=2048), None),
 }
 
 
@@ -98,12 +102,13 @@ def _skewed_ids(T, counts):
 
 
 @pytest.mark.parametrize("gather", [True, False], ids=["gather", "x_perm"])
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "mxfp4"])
 def test_large_tile_paths(dtype, gather):
     """Row groups that select the large-tile kernels (bf16: 256 rows, with every valid-row height
-    of the last m-tile: full, <= 128, <= 64, <= 32 rows; fp8: 128 rows) with caller-supplied ids;
-    sampled rows of every expert, the last m-tile's among them, against the oracle."""
-    base = CONFIGS[2] if dtype == "bf16" else CONFIGS[5]
+    of the last m-tile: full, <= 128, <= 64, <= 32 rows; fp8 and MX: 128 rows; MX with a single
+    K step in Linear-1) with caller-supplied ids; sampled rows of every expert, the last m-tile's
+    among them, against the oracle."""
+    base = {"bf16": CONFIGS[2], "fp8": CONFIGS[5], "mxfp4": CONFIGS[7]}[dtype]
     cfg = base.scaled(T=2048, H=256, I=2048, E=8, K=2, score="softmax", renorm=True, route_scale=1.0,
                       n_group=1, topk_group=1, bias=None, I_shared=0)
     counts = [2000, 800, 500, 300, 220, 150, 90, 36]   # last m-tiles: 208, 32, 244, 44, 220, 150, 90, 36
@@ -162,11 +167,34 @@ def test_quantize_fp8_bit_exact():
     assert (codes.cpu().numpy() == want_c).all()
 
 
-FULL = [1, 2, 3, 4, 5]
+def test_quantize_mx_bit_exact():
+    rng = np.random.default_rng(1)
+    rows = rng.normal(size=(37, 512)).astype(np.float32)
+    rows[3] = 0.0                                        # all-zero blocks
+    rows[4, :128] = 1e-30                                # tiny values
+    rows[5, 128:256] = np.linspace(-448, 448, 128)       # block maxima at and near 448
+    rows[6] *= 1e4
+    rows[7, :32] = 500.0 * np.sign(rows[7, :32])         # scaled maxima in (448, 512): saturation
+    rows[8, 64:96] = -0.0                                # negative zeros
+    rows[9, 256:288] = 1e-39                             # bf16 subnormals (block exponent below range)
+    rows[10] *= np.exp(rng.normal(size=512) * 4).astype(np.float32)
+    x = torch.from_numpy(rows).to(torch.bfloat16)
+    codes = torch.empty((37, 512), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((4, 37, 4), dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mx(37, 512, x.cuda(), codes, scales)
+    torch.cuda.synchronize()
+    want_c, want_s = orc.quantize_rows_mx(x.float().numpy())
+    got_s = scales.cpu().numpy().transpose(1, 0, 2).reshape(37, 16)
+    assert (got_s == want_s).all(), np.argwhere(got_s != want_s)[:5]
+    got_c = codes.cpu().numpy()
+    assert (got_c == want_c).all(), np.argwhere(got_c != want_c)[:5]
 
 
-@pytest.mark.parametrize("cid,gather", [(c, True) for c in FULL] + [(3, False), (5, False)],
-                         ids=[f"{c}-gather" for c in FULL] + ["3-x_perm", "5-x_perm"])
+FULL = [1, 2, 3, 4, 5, 7, 8]
+
+
+@pytest.mark.parametrize("cid,gather", [(c, True) for c in FULL] + [(3, False), (5, False), (7, False)],
+                         ids=[f"{c}-gather" for c in FULL] + ["3-x_perm", "5-x_perm", "7-x_perm"])
 def test_full_size_parity(cid, gather):
     """Real workload sizes: exact routing / permutation; sampled expert rows and tokens. The
     gathered path is the one the benchmark times."""
