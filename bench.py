@@ -90,6 +90,8 @@ def kernel_work(cfg, active, gather=True):
         add(f"permute/gather_quant_{qn}" if q else "permute/gather", 0.0,
             P * 4 + P * H * xb + P * H * (ab + sc))
     add("ffn/build_tiles", 0.0, E * 8)
+    if gather and mx:  # the gathered rows' activation scales, written in grouped row order
+        add("ffn/gather_scales_mx", 0.0, P * 4 + 2 * P * H * sc)
     ffn("ffn/", P, active, I, T if gather else P)
     if Is:
         if q and not gather:

@@ -22,8 +22,11 @@ namespace moe {
 //   tiles    [2][257] int32 m-tile prefix sums of the grouped GEMMs
 //   h        [max_rows][max_I] SwiGLU output (fp32 / bf16 / e4m3 codes)
 //   hscale   [max_rows][max_I/128] fp32 (fp8 layer) / [max_I/128][rows] E8M0 words (MX layer)
+//   xscale   [H/128][T*K] E8M0 words (MX layer): the activation scales of a gathered Linear-1 in
+//            grouped row order
 struct WsLayout {
-  size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, part = 0, h = 0, hscale = 0, total = 0;
+  size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, part = 0, h = 0, hscale = 0, xscale = 0,
+         total = 0;
   int route_splits = 1;
   int perm_blocks = 0;
 };
@@ -111,6 +114,7 @@ struct FfnArgs {
   void* y = nullptr;
   void* h = nullptr;          // workspace
   void* h_scale = nullptr;    // workspace (fp8, MX)
+  void* x_scale_grouped = nullptr;  // workspace (MX): x_scale gathered into grouped row order
   int32_t* tiles = nullptr;   // workspace, kTileMetaInts
   float* part = nullptr;      // workspace, partial tiles of K-split GEMM tiles
 };

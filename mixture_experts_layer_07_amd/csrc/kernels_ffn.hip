@@ -32,6 +32,20 @@ __global__ __launch_bounds__(256) void k_build_tiles(const int32_t* __restrict__
   for (int i = tid; i < 2 * kQueues + 2 * kMaxSplitItems; i += 256) tp[kTileQueueOffset + i] = 0;
 }
 
+// MX activation scales of a gathered Linear-1 in grouped row order: word (g, i) = x_scale word
+// (g, token of row i) (token clamped into x, as the row itself). The GEMM then reads the scales of
+// consecutive tile rows as consecutive words instead of one scattered word per row per 128
+// channels in every n-tile.
+__global__ __launch_bounds__(256) void k_gather_scale_words(const int32_t* __restrict__ rows_index, int div,
+                                                            int limit, const uint32_t* __restrict__ in,
+                                                            uint32_t* __restrict__ out, int n_rows, int groups) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_rows) return;
+  unsigned tok = (unsigned)rows_index[i] / (unsigned)div;
+  tok = tok < (unsigned)limit ? tok : (unsigned)(limit - 1);
+  for (int g = blockIdx.y; g < groups; g += gridDim.y) out[(size_t)g * n_rows + i] = in[(size_t)g * limit + tok];
+}
+
 // ============================================================================ fp32 (VALU)
 // 64 x 64 output tiles, 16-channel K steps through LDS, 4 x 4 outputs per thread, fp32 FMA in
 // channel order. GLU tiles compute the gate and up tiles together.
@@ -220,9 +234,20 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
     g2.b_scale_exp = (size_t)(H / 128) * (I / 128);
   }
   if (mx) {
-    // [K/128][rows] words: the scale arrays' row counts; Linear-1 gathers x rows (T of them) or
-    // reads the n_rows grouped rows
-    g1.a_scale_ld = a.x_rows_index ? a.x_rows_limit : a.n_rows;
+    // [K/128][rows] words: the scale arrays' row counts. The MX kernels read activation scales in
+    // grouped row order; a gathered Linear-1 gets its rows' scales gathered first.
+    if (a.x_rows_index) {
+      const int groups = H / 128;
+      const dim3 grid((a.n_rows + 255) / 256, groups < 8 ? groups : 8);
+      if ((e = timed_launch("gather_scales_mx", s, [&] {
+             hipLaunchKernelGGL(k_gather_scale_words, grid, dim3(256), 0, s, a.x_rows_index, a.x_rows_div,
+                                a.x_rows_limit, static_cast<const uint32_t*>(a.x_scale),
+                                static_cast<uint32_t*>(a.x_scale_grouped), a.n_rows, groups);
+           })) != hipSuccess)
+        return e;
+      g1.a_scale = static_cast<const float*>(a.x_scale_grouped);
+    }
+    g1.a_scale_ld = a.n_rows;
     g1.b_scale_ld = 2 * I;
     g1.b_scale_exp = (size_t)(H / 128) * 2 * I;
     g1.c_scale_ld = a.n_rows;

@@ -10,6 +10,8 @@
 // Scale storage of an operand with R rows and K channels: one 32-bit word per row per 128
 // channels, word (k/128) * R + row, whose byte b is the scale of channels [k0 + 32b, k0 + 32b + 32)
 // of that 128-channel group. A K step's scales of consecutive rows are then consecutive words.
+// Activation scales are read in grouped row order (word row = the tile's grouped row), also when
+// the rows themselves are gathered: the launcher gathers those scales beforehand.
 //
 // Operand layout of the scaled MFMA 32x32x64 with an e4m3 A and an e2m1 B (measured on gfx950):
 // of the 64 channels of one MFMA, lane r + 32h holds, for A, channels [16h, 16h+16) in bytes
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
     for (int mb = 0; mb < MB; ++mb) {
       const int r = wm * WM + mb * 32 + lrow;
       const int rc = r < ti.mvalid ? r : ti.mvalid - 1;
-      srow[mb] = (uint32_t)(g.a_rows ? a_row(g, ti, rc) : ti.row0 + rc);
+      srow[mb] = (uint32_t)(ti.row0 + rc);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) scol[nb] = (uint32_t)weight_row<GLU, BN>(wn * WN + nb * 32 + lrow, ti.nt, g);

@@ -107,6 +107,8 @@ WsLayout layout(const moe_config& c) {
   off = align256(off + P * maxI * elem);
   L.hscale = off;  // fp8: one fp32 per row per 128 channels; MX: one word of four E8M0 codes
   off = align256(off + (c.dtype == MOE_FP8_E4M3 || c.dtype == MOE_MXFP4 ? P * (maxI / 128) * 4 : 0));
+  L.xscale = off;
+  off = align256(off + (c.dtype == MOE_MXFP4 ? P * (H / 128) * 4 : 0));
   L.total = off;
   return L;
 }
