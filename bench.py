@@ -106,7 +106,7 @@ def kernel_work(cfg, active, gather=True):
 
 def variant_free(name):
     """Kernel name without its tile-variant suffix (the work model does not depend on it)."""
-    for suf in ("_m32", "_m128"):
+    for suf in ("_m32", "_m128", "_m256"):
         if name.endswith(suf):
             return name[:-len(suf)]
     return name

@@ -261,8 +261,8 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
   const int avg = a.n_rows / a.n_exp;
   auto enough = [&](int bm) { return (long)((a.n_rows + bm - 1) / bm) * g1.n_tiles_n >= cus; };
   if (mx) {
-    const int variant = avg >= 64 && enough(128) ? 2 : 1;
-    if ((e = build_tiles(a, variant == 2 ? 128 : 32, a.tiles, s)) != hipSuccess) return e;
+    const int variant = avg >= 128 && enough(256) ? 0 : (avg >= 64 && enough(128) ? 2 : 1);
+    if ((e = build_tiles(a, variant == 0 ? 256 : (variant == 2 ? 128 : 32), a.tiles, s)) != hipSuccess) return e;
     return launch_gemm_mx(g1, g2, variant, cus, s);
   }
   if (!fp8) {

@@ -278,6 +278,286 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
   }
 }
 
+// ============================================================================ 256 x 256 tiles
+// Eight waves (4 x 2) of 64 rows x 128 weight rows. Per MFMA a wave reads 1 KB of fragments from
+// LDS (a 64 x 64 wave tile reads 1.5 KB), which keeps the LDS (fragment reads plus stage fills)
+// below its bandwidth at the MFMA rate; two waves per SIMD hide each other's barriers and
+// epilogues. K steps of 128 channels go through a ring of three LDS stages, each an A tile (256 rows
+// x 128 bytes) and a weight tile (256 rows x 64 bytes), filled by direct-to-LDS loads: the step's
+// barrier sits between its two 64-channel sub-steps, after which the step's stage is free and
+// receives step k+3, two steps ahead of its first read. Fragments are double-buffered in
+// registers, their LDS reads interleaved with the MFMAs of the other buffer; scale words run two
+// steps ahead. Every step has one shape (loads past the last step are clamped and never read), so
+// no branch splits the scheduling; the K loop is specialised on the wave's number of valid 32-row
+// blocks (2, 1 or 0).
+namespace mx8 {
+constexpr int BM = 256, BN = 256, NWN = 2, NT = 512, NW = 8;
+constexpr int WM = 64, WN = 128, MB = 2, NB = 4;
+constexpr int ACH = BM * 8;  // A stage: 256 rows x 128 bytes
+constexpr int BCH = BN * 4;  // weight stage: 256 rows x 64 bytes (128 e2m1 codes)
+constexpr int AJ = ACH / NT, BJ = BCH / NT;
+}  // namespace mx8
+
+// Weight stage rows are 64 bytes (4 chunks, a quarter of the banks): chunk c of row r sits at
+// c ^ ((r >> 2) & 3), so 16 consecutive rows put one logical chunk in 16 different bank groups.
+// Instance j of wave w of a 1 KB transfer covers rows (j*NW + w)*16 .. +16, lane i slot i.
+__device__ __forceinline__ int mx_swz4(int row) { return (row >> 2) & 3; }
+template <int NW>
+__device__ __forceinline__ int mx_b64_row(int j, int wave, int lane) { return (j * NW + wave) * 16 + (lane >> 2); }
+__device__ __forceinline__ int mx_b64_chunk(int row, int lane) { return (lane & 3) ^ mx_swz4(row); }
+
+struct MxFrag {
+  i32x8 a[mx8::MB];
+  u32x4 b[mx8::NB];
+};
+
+// Fragments of sub-step J (channels [64J, 64J+64) of the step) of the wave's first NMB row blocks.
+template <int NMB, int J>
+__device__ __forceinline__ void mx8_frags(const u32x4* sta, const u32x4* stb, int wm, int wn, int lane, MxFrag& f) {
+  if constexpr (NMB > 0) {
+    const int lrow = lane & 31, h = lane >> 5;
+    const int sA = lds_swz(lrow), sB = mx_swz4(lrow);  // block rows start at multiples of 32
+    const u32x4* la = sta + (wm * mx8::WM + lrow) * 8;
+    const u32x4* lb = stb + (wn * mx8::WN + lrow) * 4;
+#pragma unroll
+    for (int nb = 0; nb < mx8::NB; ++nb) f.b[nb] = lb[nb * 128 + ((2 * J + h) ^ sB)];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) f.a[mb] = mx_fragA(la + mb * 256, (4 * J + h) ^ sA, (4 * J + 2 + h) ^ sA);
+  }
+}
+
+// MFMAs of sub-step J; sa / sb: the step's scale words shifted by 8h, so op_sel 2J picks the byte
+// of channels [32h, 32h+32) of the sub-step.
+template <int NMB, int J>
+__device__ __forceinline__ void mx8_mfmas(const MxFrag& f, const uint32_t (&sa)[mx8::MB],
+                                          const uint32_t (&sb)[mx8::NB], f32x16 (&acc)[mx8::MB][mx8::NB]) {
+  constexpr int OPS = 2 * J;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < mx8::NB; ++nb) {
+      const u32x4 b = f.b[nb];
+      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          f.a[mb], i32x8{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0}, acc[mb][nb], 0, 4, OPS, (int)sa[mb], OPS,
+          (int)sb[nb]);
+    }
+}
+
+// Scheduling groups of one half step: MFMA I carries one LDS read (while NR remain) and its even
+// share of NV vector memory operations (0x008 MFMA, 0x100 LDS read, 0x010 vector memory).
+template <int I, int NM, int NR, int NV>
+__device__ __forceinline__ void mx8_sched() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (I < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    constexpr int nv = NV * (I + 1) / NM - NV * I / NM;
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x010, nv, 0);
+    if constexpr (I + 1 == NM && NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+    mx8_sched<I + 1, NM, NR, NV>();
+  }
+}
+
+template <bool GLU>
+__global__ __launch_bounds__(512, 1) void k_gemm_mx_m256(GemmArgs g) {
+  using namespace mx8;
+  __shared__ u32x4 sA0[ACH];
+  __shared__ u32x4 sA1[ACH];
+  __shared__ u32x4 sA2[ACH];
+  __shared__ u32x4 sB0[BCH];
+  __shared__ u32x4 sB1[BCH];
+  __shared__ u32x4 sB2[BCH];
+  __shared__ int tp[kMaxExperts + 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / NWN, wn = wave % NWN;
+  for (int i = tid; i <= g.n_exp; i += NT) tp[i] = g.tp[i];
+  __syncthreads();
+  const int total = tp[g.n_exp] * g.n_tiles_n;
+  const int KT = g.K / 128;
+  const int lrow = lane & 31, h = lane >> 5;
+  __shared__ int s_slot[1];
+  const TileQueue tq = tile_queue(total);
+  const uint32_t* a_sc = reinterpret_cast<const uint32_t*>(g.a_scale);
+  const uint32_t* b_sc = reinterpret_cast<const uint32_t*>(g.b_scale);
+  const size_t a_sld = (size_t)g.a_scale_ld;
+  const size_t b_sld = (size_t)g.b_scale_ld;
+
+  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
+    TileInfo ti = decode_tile(t, tp, g, BM);
+    ti.e = __builtin_amdgcn_readfirstlane(ti.e);
+    ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
+    ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
+    ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
+    // valid 32-row blocks of this wave (0..MB)
+    int nmb = (ti.mvalid - wm * WM + 31) / 32;
+    nmb = __builtin_amdgcn_readfirstlane(nmb < 0 ? 0 : (nmb > MB ? MB : nmb));
+    const uint8_t* Ab = a_base(g, ti);
+    const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
+    TileDma<AJ> da;
+    TileDma<BJ> db;
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) {
+      const int r = dma_row<NW>(j, wave, lane);
+      const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
+      da.off[j] = (uint32_t)rr * (uint32_t)g.lda + (uint32_t)dma_chunk(r, lane) * 16u;
+    }
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) {
+      const int r = mx_b64_row<NW>(j, wave, lane);
+      db.off[j] = (uint32_t)weight_row<GLU, BN>(r, ti.nt, g) * (uint32_t)g.ldb + (uint32_t)mx_b64_chunk(r, lane) * 16u;
+    }
+    uint32_t srow[MB], scol[NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = wm * WM + mb * 32 + lrow;
+      srow[mb] = (uint32_t)(ti.row0 + (r < ti.mvalid ? r : ti.mvalid - 1));
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) scol[nb] = (uint32_t)weight_row<GLU, BN>(wn * WN + nb * 32 + lrow, ti.nt, g);
+    // formed once per tile: the empty asm keeps the compiler from recomputing them (with the row
+    // lookups of a gathered A) inside the K loop
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) asm volatile("" : "+v"(da.off[j]));
+#pragma unroll
+    for (int j = 0; j < BJ; ++j) asm volatile("" : "+v"(db.off[j]));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(srow[mb]));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(scol[nb]));
+    const uint32_t* bsc_e = b_sc + (size_t)ti.e * g.b_scale_exp;
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+    MxFrag F0, F1;
+    uint32_t S0a[MB], S0b[NB], S1a[MB], S1b[NB], S2a[MB], S2b[NB];
+
+#define MX8_SLOAD(SA, SB, kt)                                                                       \
+  do {                                                                                              \
+    const size_t k_ = (size_t)((kt) < KT ? (kt) : KT - 1);                                          \
+    const uint32_t* pa_ = a_sc + k_ * a_sld;                                                        \
+    const uint32_t* pb_ = bsc_e + k_ * b_sld;                                                       \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) SA[mb] = pa_[srow[mb]];                       \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) SB[nb] = pb_[scol[nb]];                       \
+  } while (0)
+#define MX8_SSHIFT(SA, SB)                                                                          \
+  do {                                                                                              \
+    _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) SA[mb] >>= 8 * h;                             \
+    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) SB[nb] >>= 8 * h;                             \
+  } while (0)
+// A and weights of step kt into stage (sa_, sb_)
+#define MX8_DMA(kt, sa_, sb_)                                                                       \
+  do {                                                                                              \
+    _Pragma("unroll") for (int j_ = 0; j_ < AJ; ++j_)                                               \
+        dma_to_lds<16>(Ab + (da.off[j_] + (uint32_t)(kt) * 128u), (sa_) + (j_ * NW + wave) * 64);   \
+    _Pragma("unroll") for (int j_ = 0; j_ < BJ; ++j_)                                               \
+        dma_to_lds<16>(Be + (db.off[j_] + (uint32_t)(kt) * 64u), (sb_) + (j_ * NW + wave) * 64);    \
+  } while (0)
+// Step kt on stage (ca, cb) with scales (SA, SB); F0 holds its sub-step 0 fragments. Part 1:
+// sub-step 0 MFMAs carrying the reads of sub-step 1 into F1. Barrier (this wave's reads done, the
+// loads of step kt+1 landed in every wave). Part 2: sub-step 1 MFMAs carrying the reads of step
+// kt+1's sub-step 0 into F0 (stage (na, nb_)), the scale words of step kt+2 (into SL*) and the
+// loads of step kt+3 into the now free stage (ca, cb).
+#define MX8_STEP(NMB_, kt, ca, cb, na, nb_, SA, SB, SNA, SNB, SLA, SLB)                             \
+  {                                                                                                 \
+    constexpr int nm_ = (NMB_) * NB, nr_ = (NMB_) > 0 ? (NMB_) * 2 + NB : 0;                        \
+    mx8_frags<NMB_, 1>(ca, cb, wm, wn, lane, F1);                                                   \
+    mx8_mfmas<NMB_, 0>(F0, SA, SB, acc);                                                            \
+    mx8_sched<0, nm_, nr_, 0>();                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                              \
+    __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(AJ + BJ));                                          \
+    __builtin_amdgcn_s_barrier();                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                              \
+    mx8_frags<NMB_, 0>(na, nb_, wm, wn, lane, F0);                                                  \
+    MX8_SSHIFT(SNA, SNB);                                                                           \
+    MX8_SLOAD(SLA, SLB, (kt) + 2);                                                                  \
+    MX8_DMA((kt) + 3 < KT ? (kt) + 3 : KT - 1, ca, cb);                                             \
+    mx8_mfmas<NMB_, 1>(F1, SA, SB, acc);                                                            \
+    mx8_sched<0, nm_, nr_, MB + NB + AJ + BJ>();                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                              \
+  }
+#define MX8_KLOOP(NMB_)                                                                             \
+  {                                                                                                 \
+    mx8_frags<NMB_, 0>(sA0, sB0, wm, wn, lane, F0);                                                 \
+    int kt = 0;                                                                                     \
+    for (; kt + 3 <= KT; kt += 3) {                                                                 \
+      MX8_STEP(NMB_, kt, sA0, sB0, sA1, sB1, S0a, S0b, S1a, S1b, S2a, S2b)                          \
+      MX8_STEP(NMB_, kt + 1, sA1, sB1, sA2, sB2, S1a, S1b, S2a, S2b, S0a, S0b)                      \
+      MX8_STEP(NMB_, kt + 2, sA2, sB2, sA0, sB0, S2a, S2b, S0a, S0b, S1a, S1b)                      \
+    }                                                                                               \
+    if (kt < KT) MX8_STEP(NMB_, kt, sA0, sB0, sA1, sB1, S0a, S0b, S1a, S1b, S2a, S2b)               \
+    if (kt + 1 < KT) MX8_STEP(NMB_, kt + 1, sA1, sB1, sA2, sB2, S1a, S1b, S2a, S2b, S0a, S0b)       \
+  }
+    // prologue: scale words of steps 0 and 1, loads of steps 0, 1 and 2 (clamped); wait for the
+    // scales and step 0 (steps 1 and 2 may still be in flight)
+    MX8_SLOAD(S0a, S0b, 0);
+    MX8_SLOAD(S1a, S1b, 1);
+    MX8_DMA(0, sA0, sB0);
+    MX8_DMA(KT > 1 ? 1 : KT - 1, sA1, sB1);
+    MX8_DMA(KT > 2 ? 2 : KT - 1, sA2, sB2);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(2 * (AJ + BJ)));
+    __builtin_amdgcn_s_barrier();
+    MX8_SSHIFT(S0a, S0b);
+    if (nmb == MB) {
+      MX8_KLOOP(2)
+    } else if (nmb == 1) {
+      MX8_KLOOP(1)
+    } else {
+      MX8_KLOOP(0)
+    }
+#undef MX8_SLOAD
+#undef MX8_SSHIFT
+#undef MX8_DMA
+#undef MX8_STEP
+#undef MX8_KLOOP
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (GLU) {
+      // this wave's 64 h columns: two MX blocks per row (gate / up pairs nb = 2q, 2q + 1)
+      uint8_t* csc = reinterpret_cast<uint8_t*>(g.c_scale);
+      const size_t c_sld = (size_t)g.c_scale_ld;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float hv = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
+            float m = fabsf(hv);
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            const int ex = (int)(__float_as_uint(m) >> 23);
+            const int code = ex > 8 ? ex - 8 : 0;
+            const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+            if (r < ti.mvalid) {
+              const size_t row = (size_t)(ti.row0 + r);
+              const int col = ti.nt * 128 + wn * 64 + q * 32 + lrow;
+              g.C[row * g.ldc + col] = (uint8_t)f32_to_e4m3(__builtin_amdgcn_ldexpf(hv, 127 - code));
+              if (lrow == 0) csc[((size_t)ti.nt * c_sld + row) * 4 + 2 * wn + q] = (uint8_t)code;
+            }
+          }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = ti.nt * BN + wn * WN + nb * 32 + lrow;
+          if (col < g.N_out) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+              if (r < ti.mvalid)
+                reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(acc[mb][nb][i]);
+            }
+          }
+        }
+    }
+  }
+}
+
 template <class K>
 static hipError_t launch_one(const char* name, K kernel, int grid, int threads, const GemmArgs& g,
                              hipStream_t s) {
@@ -286,11 +566,16 @@ static hipError_t launch_one(const char* name, K kernel, int grid, int threads, 
 
 static int round8(int v) { return ((v + 7) / 8) * 8; }
 
+// variant 0: 256 x 256 tiles, 8 waves of 64 x 128, 128-channel steps, one workgroup per CU;
 // variant 2: 128 x 256 tiles, 8 waves of 64 x 64, one workgroup per CU;
 // variant 1: 32 x 256, 4 waves of 32 x 64, one workgroup per CU.
 hipError_t launch_gemm_mx(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s) {
   hipError_t e;
   const int grid = round8(cus);
+  if (variant == 0) {
+    if ((e = launch_one("gemm_mx_gateup_swiglu_m256", k_gemm_mx_m256<true>, grid, 512, g1, s)) != hipSuccess) return e;
+    return launch_one("gemm_mx_down_m256", k_gemm_mx_m256<false>, grid, 512, g2, s);
+  }
   if (variant == 2) {
     if ((e = launch_one("gemm_mx_gateup_swiglu_m128", k_gemm_mx<128, 256, 2, 4, true, 1>, grid, 512, g1, s)) !=
         hipSuccess)
