@@ -261,7 +261,9 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
   const int avg = a.n_rows / a.n_exp;
   auto enough = [&](int bm) { return (long)((a.n_rows + bm - 1) / bm) * g1.n_tiles_n >= cus; };
   if (mx) {
-    const int variant = avg >= 128 && enough(256) ? 0 : (avg >= 64 && enough(128) ? 2 : 1);
+    // 32-row tiles: the three-stage kernel (two workgroups per CU, more weight bytes in flight)
+    // once the launch has a tile per CU, else the two-stage one (shorter per-tile start-up)
+    const int variant = avg >= 128 && enough(256) ? 0 : (avg >= 64 && enough(128) ? 2 : (enough(32) ? 3 : 1));
     if ((e = build_tiles(a, variant == 0 ? 256 : (variant == 2 ? 128 : 32), a.tiles, s)) != hipSuccess) return e;
     return launch_gemm_mx(g1, g2, variant, cus, s);
   }

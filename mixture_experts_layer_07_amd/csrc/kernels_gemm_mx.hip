@@ -278,25 +278,31 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
   }
 }
 
-// ============================================================================ 256 x 256 tiles
-// Eight waves (4 x 2) of 64 rows x 128 weight rows. Per MFMA a wave reads 1 KB of fragments from
-// LDS (a 64 x 64 wave tile reads 1.5 KB), which keeps the LDS (fragment reads plus stage fills)
-// below its bandwidth at the MFMA rate; two waves per SIMD hide each other's barriers and
-// epilogues. K steps of 128 channels go through a ring of three LDS stages, each an A tile (256 rows
-// x 128 bytes) and a weight tile (256 rows x 64 bytes), filled by direct-to-LDS loads: the step's
-// barrier sits between its two 64-channel sub-steps, after which the step's stage is free and
-// receives step k+3, two steps ahead of its first read. Fragments are double-buffered in
-// registers, their LDS reads interleaved with the MFMAs of the other buffer; scale words run two
-// steps ahead. Every step has one shape (loads past the last step are clamped and never read), so
-// no branch splits the scheduling; the K loop is specialised on the wave's number of valid 32-row
-// blocks (2, 1 or 0).
-namespace mx8 {
-constexpr int BM = 256, BN = 256, NWN = 2, NT = 512, NW = 8;
-constexpr int WM = 64, WN = 128, MB = 2, NB = 4;
-constexpr int ACH = BM * 8;  // A stage: 256 rows x 128 bytes
-constexpr int BCH = BN * 4;  // weight stage: 256 rows x 64 bytes (128 e2m1 codes)
-constexpr int AJ = ACH / NT, BJ = BCH / NT;
-}  // namespace mx8
+// ============================================================================ three-stage ring
+// BM x BN tiles of NWM x NWN waves, K steps of 128 channels through a ring of three LDS stages,
+// each an A tile (BM rows x 128 bytes) and a weight tile (BN rows x 64 bytes), filled by
+// direct-to-LDS loads: the step's barrier sits between its two 64-channel sub-steps, after which
+// the step's stage is free and receives step k+3, two steps ahead of its first read. Fragments
+// are double-buffered in registers, their LDS reads interleaved with the MFMAs of the other
+// buffer; scale words run two steps ahead. Every step has one shape (loads past the last step are
+// clamped and never read), so no branch splits the scheduling; the K loop is specialised on the
+// wave's number of valid 32-row blocks.
+//   256 x 256, eight waves of 64 rows x 128 weight rows: per MFMA a wave reads 1 KB of fragments
+//   from LDS (a 64 x 64 wave tile reads 1.5 KB), which keeps the LDS (fragment reads plus stage
+//   fills) below its bandwidth at the MFMA rate; two waves per SIMD hide each other's barriers
+//   and epilogues.
+//   32 x 256, four waves of 32 x 64 (decode-sized row groups): 60 KB of LDS, two workgroups per
+//   CU, so ≈ 80 KB of weight loads are in flight per CU.
+template <int BM_, int BN_, int NWM_, int NWN_>
+struct MxR3 {
+  static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_;
+  static constexpr int NW = NWM * NWN, NT = NW * 64;
+  static constexpr int WM = BM / NWM, WN = BN / NWN, MB = WM / 32, NB = WN / 32;
+  static constexpr int ACH = BM * 8;  // A stage: BM rows x 128 bytes
+  static constexpr int BCH = BN * 4;  // weight stage: BN rows x 64 bytes (128 e2m1 codes)
+  static constexpr int AJ = ACH / NT, BJ = BCH / NT;
+  static_assert(ACH % NT == 0 && BCH % NT == 0 && WM % 32 == 0 && WN % 32 == 0, "tile / wave mismatch");
+};
 
 // Weight stage rows are 64 bytes (4 chunks, a quarter of the banks): chunk c of row r sits at
 // c ^ ((r >> 2) & 3), so 16 consecutive rows put one logical chunk in 16 different bank groups.
@@ -306,21 +312,23 @@ template <int NW>
 __device__ __forceinline__ int mx_b64_row(int j, int wave, int lane) { return (j * NW + wave) * 16 + (lane >> 2); }
 __device__ __forceinline__ int mx_b64_chunk(int row, int lane) { return (lane & 3) ^ mx_swz4(row); }
 
+template <int MB, int NB>
 struct MxFrag {
-  i32x8 a[mx8::MB];
-  u32x4 b[mx8::NB];
+  i32x8 a[MB];
+  u32x4 b[NB];
 };
 
 // Fragments of sub-step J (channels [64J, 64J+64) of the step) of the wave's first NMB row blocks.
-template <int NMB, int J>
-__device__ __forceinline__ void mx8_frags(const u32x4* sta, const u32x4* stb, int wm, int wn, int lane, MxFrag& f) {
+template <class P, int NMB, int J>
+__device__ __forceinline__ void mx8_frags(const u32x4* sta, const u32x4* stb, int wm, int wn, int lane,
+                                          MxFrag<P::MB, P::NB>& f) {
   if constexpr (NMB > 0) {
     const int lrow = lane & 31, h = lane >> 5;
     const int sA = lds_swz(lrow), sB = mx_swz4(lrow);  // block rows start at multiples of 32
-    const u32x4* la = sta + (wm * mx8::WM + lrow) * 8;
-    const u32x4* lb = stb + (wn * mx8::WN + lrow) * 4;
+    const u32x4* la = sta + (wm * P::WM + lrow) * 8;
+    const u32x4* lb = stb + (wn * P::WN + lrow) * 4;
 #pragma unroll
-    for (int nb = 0; nb < mx8::NB; ++nb) f.b[nb] = lb[nb * 128 + ((2 * J + h) ^ sB)];
+    for (int nb = 0; nb < P::NB; ++nb) f.b[nb] = lb[nb * 128 + ((2 * J + h) ^ sB)];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) f.a[mb] = mx_fragA(la + mb * 256, (4 * J + h) ^ sA, (4 * J + 2 + h) ^ sA);
   }
@@ -328,14 +336,14 @@ __device__ __forceinline__ void mx8_frags(const u32x4* sta, const u32x4* stb, in
 
 // MFMAs of sub-step J; sa / sb: the step's scale words shifted by 8h, so op_sel 2J picks the byte
 // of channels [32h, 32h+32) of the sub-step.
-template <int NMB, int J>
-__device__ __forceinline__ void mx8_mfmas(const MxFrag& f, const uint32_t (&sa)[mx8::MB],
-                                          const uint32_t (&sb)[mx8::NB], f32x16 (&acc)[mx8::MB][mx8::NB]) {
+template <class P, int NMB, int J>
+__device__ __forceinline__ void mx8_mfmas(const MxFrag<P::MB, P::NB>& f, const uint32_t (&sa)[P::MB],
+                                          const uint32_t (&sb)[P::NB], f32x16 (&acc)[P::MB][P::NB]) {
   constexpr int OPS = 2 * J;
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < mx8::NB; ++nb) {
+    for (int nb = 0; nb < P::NB; ++nb) {
       const u32x4 b = f.b[nb];
       acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           f.a[mb], i32x8{(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0}, acc[mb][nb], 0, 4, OPS, (int)sa[mb], OPS,
@@ -357,9 +365,12 @@ __device__ __forceinline__ void mx8_sched() {
   }
 }
 
-template <bool GLU>
-__global__ __launch_bounds__(512, 1) void k_gemm_mx_m256(GemmArgs g) {
-  using namespace mx8;
+template <class P, bool GLU, int MINB>
+__global__ __launch_bounds__(P::NT, MINB) void k_gemm_mx_r3(GemmArgs g) {
+  constexpr int BM = P::BM, BN = P::BN, NWN = P::NWN, NT = P::NT, NW = P::NW;
+  constexpr int WM = P::WM, WN = P::WN, MB = P::MB, NB = P::NB, ACH = P::ACH, BCH = P::BCH;
+  constexpr int AJ = P::AJ, BJ = P::BJ;
+  static_assert(!GLU || (NB % 2 == 0 && BN == 256), "GLU: gate / up pairs per wave, 128 h columns per tile");
   __shared__ u32x4 sA0[ACH];
   __shared__ u32x4 sA1[ACH];
   __shared__ u32x4 sA2[ACH];
@@ -432,7 +443,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx_m256(GemmArgs g) {
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-    MxFrag F0, F1;
+    MxFrag<MB, NB> F0, F1;
     uint32_t S0a[MB], S0b[NB], S1a[MB], S1b[NB], S2a[MB], S2b[NB];
 
 #define MX8_SLOAD(SA, SB, kt)                                                                       \
@@ -464,24 +475,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx_m256(GemmArgs g) {
 #define MX8_STEP(NMB_, kt, ca, cb, na, nb_, SA, SB, SNA, SNB, SLA, SLB)                             \
   {                                                                                                 \
     constexpr int nm_ = (NMB_) * NB, nr_ = (NMB_) > 0 ? (NMB_) * 2 + NB : 0;                        \
-    mx8_frags<NMB_, 1>(ca, cb, wm, wn, lane, F1);                                                   \
-    mx8_mfmas<NMB_, 0>(F0, SA, SB, acc);                                                            \
+    mx8_frags<P, NMB_, 1>(ca, cb, wm, wn, lane, F1);                                                \
+    mx8_mfmas<P, NMB_, 0>(F0, SA, SB, acc);                                                         \
     mx8_sched<0, nm_, nr_, 0>();                                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                              \
     __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(AJ + BJ));                                          \
     __builtin_amdgcn_s_barrier();                                                                   \
     __builtin_amdgcn_sched_barrier(0);                                                              \
-    mx8_frags<NMB_, 0>(na, nb_, wm, wn, lane, F0);                                                  \
+    mx8_frags<P, NMB_, 0>(na, nb_, wm, wn, lane, F0);                                               \
     MX8_SSHIFT(SNA, SNB);                                                                           \
     MX8_SLOAD(SLA, SLB, (kt) + 2);                                                                  \
     MX8_DMA((kt) + 3 < KT ? (kt) + 3 : KT - 1, ca, cb);                                             \
-    mx8_mfmas<NMB_, 1>(F1, SA, SB, acc);                                                            \
+    mx8_mfmas<P, NMB_, 1>(F1, SA, SB, acc);                                                         \
     mx8_sched<0, nm_, nr_, MB + NB + AJ + BJ>();                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                              \
   }
 #define MX8_KLOOP(NMB_)                                                                             \
   {                                                                                                 \
-    mx8_frags<NMB_, 0>(sA0, sB0, wm, wn, lane, F0);                                                 \
+    mx8_frags<P, NMB_, 0>(sA0, sB0, wm, wn, lane, F0);                                              \
     int kt = 0;                                                                                     \
     for (; kt + 3 <= KT; kt += 3) {                                                                 \
       MX8_STEP(NMB_, kt, sA0, sB0, sA1, sB1, S0a, S0b, S1a, S1b, S2a, S2b)                          \
@@ -502,10 +513,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx_m256(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(2 * (AJ + BJ)));
     __builtin_amdgcn_s_barrier();
     MX8_SSHIFT(S0a, S0b);
-    if (nmb == MB) {
-      MX8_KLOOP(2)
-    } else if (nmb == 1) {
-      MX8_KLOOP(1)
+    constexpr int kOneBlock = MB > 1 ? 1 : MB;  // (a one-block wave tile has no partial case)
+    if (nmb >= MB) {
+      MX8_KLOOP(MB)
+    } else if (MB > 1 && nmb == 1) {
+      MX8_KLOOP(kOneBlock)
     } else {
       MX8_KLOOP(0)
     }
@@ -516,13 +528,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx_m256(GemmArgs g) {
 #undef MX8_KLOOP
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (GLU) {
-      // this wave's 64 h columns: two MX blocks per row (gate / up pairs nb = 2q, 2q + 1)
+      // this wave's WN / 2 h columns: NB / 2 MX blocks per row (gate / up pairs nb = 2q, 2q + 1)
       uint8_t* csc = reinterpret_cast<uint8_t*>(g.c_scale);
       const size_t c_sld = (size_t)g.c_scale_ld;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < NB / 2; ++q)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float hv = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
@@ -534,9 +546,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx_m256(GemmArgs g) {
             const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
             if (r < ti.mvalid) {
               const size_t row = (size_t)(ti.row0 + r);
-              const int col = ti.nt * 128 + wn * 64 + q * 32 + lrow;
+              const int col = ti.nt * 128 + wn * (WN / 2) + q * 32 + lrow;
               g.C[row * g.ldc + col] = (uint8_t)f32_to_e4m3(__builtin_amdgcn_ldexpf(hv, 127 - code));
-              if (lrow == 0) csc[((size_t)ti.nt * c_sld + row) * 4 + 2 * wn + q] = (uint8_t)code;
+              if (lrow == 0) csc[((size_t)ti.nt * c_sld + row) * 4 + wn * (NB / 2) + q] = (uint8_t)code;
             }
           }
     } else {
@@ -567,14 +579,26 @@ static hipError_t launch_one(const char* name, K kernel, int grid, int threads, 
 static int round8(int v) { return ((v + 7) / 8) * 8; }
 
 // variant 0: 256 x 256 tiles, 8 waves of 64 x 128, 128-channel steps, one workgroup per CU;
+// variant 3: 32 x 256 tiles, 4 waves of 32 x 64, 128-channel steps, two workgroups per CU;
 // variant 2: 128 x 256 tiles, 8 waves of 64 x 64, one workgroup per CU;
 // variant 1: 32 x 256, 4 waves of 32 x 64, one workgroup per CU.
 hipError_t launch_gemm_mx(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s) {
   hipError_t e;
   const int grid = round8(cus);
+  using M256 = MxR3<256, 256, 4, 2>;
+  using M32 = MxR3<32, 256, 1, 4>;
   if (variant == 0) {
-    if ((e = launch_one("gemm_mx_gateup_swiglu_m256", k_gemm_mx_m256<true>, grid, 512, g1, s)) != hipSuccess) return e;
-    return launch_one("gemm_mx_down_m256", k_gemm_mx_m256<false>, grid, 512, g2, s);
+    if ((e = launch_one("gemm_mx_gateup_swiglu_m256", k_gemm_mx_r3<M256, true, 1>, grid, M256::NT, g1, s)) !=
+        hipSuccess)
+      return e;
+    return launch_one("gemm_mx_down_m256", k_gemm_mx_r3<M256, false, 1>, grid, M256::NT, g2, s);
+  }
+  if (variant == 3) {
+    const int grid2 = round8(cus * 2);
+    if ((e = launch_one("gemm_mx_gateup_swiglu_m32", k_gemm_mx_r3<M32, true, 2>, grid2, M32::NT, g1, s)) !=
+        hipSuccess)
+      return e;
+    return launch_one("gemm_mx_down_m32", k_gemm_mx_r3<M32, false, 2>, grid2, M32::NT, g2, s);
   }
   if (variant == 2) {
     if ((e = launch_one("gemm_mx_gateup_swiglu_m128", k_gemm_mx<128, 256, 2, 4, true, 1>, grid, 512, g1, s)) !=
