@@ -6,8 +6,7 @@
 // fp32 router arithmetic; section 9 notes that softmax keeps the order of the logits, so
 // selection without a bias can run on the logits themselves. The selection-only bias is from
 // the "MoE" chapter README (llm-infra-atlas.github.io/moe), sections 0 and 2.2.
-#include "device.h"
-#include "internal.h"
+#include "gemm_common.h"
 
 namespace moe {
 
@@ -58,74 +57,118 @@ hipError_t launch_transpose_bf16(const void* in, void* out, int rows, int cols, 
   });
 }
 
-// ------------------------------------------------------------------ bf16 router (MFMA 16x16x32)
-// Workgroup: 4 waves, 32 tokens x 256 experts; wave w owns experts [64w, 64w+64) as four 16-wide
-// blocks, two 16-row token blocks. blockIdx.y splits H into `splits` chunks (multiples of 128
-// channels); each split writes its own partial logits, summed later in split order.
-// Operands are read straight from global memory (x rows and the K-major transposed W_r):
-// each lane holds 8 consecutive channels of one row for the A operand and of one expert for
-// the B operand, the same channel set for both, so the MFMA sums every channel once.
-__global__ __launch_bounds__(256) void k_router_bf16(const uint16_t* __restrict__ x,
-                                                     const uint16_t* __restrict__ wrt,
-                                                     float* __restrict__ logits, int T, int H,
-                                                     int E, int splits) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = wave * 64;
-  if (e0 >= E) return;
-  const int t0 = blockIdx.x * 32;
-  const int nk = H / 128;
-  const int s = blockIdx.y;
-  const int kc0 = (int)((long long)s * nk / splits) * 128;
-  const int kc1 = (int)((long long)(s + 1) * nk / splits) * 128;
-  const int r = lane & 15, kq = (lane >> 4) * 8;
-  const uint16_t* arow[2];
-  const uint16_t* brow[4];
+// ------------------------------------------------------------------ bf16 router (MFMA 32x32x16)
+// Tiles of 128 tokens x TE experts (all experts, padded to 32), four waves of NWT x NWE, each
+// (MB*32 tokens) x (NB*32 experts). blockIdx.y splits H into `splits` pieces of whole 128-channel
+// units; each split writes its own partial logits, summed later in split order. 64-channel K steps
+// go through a ring of three LDS stages, each the step's x rows (128 x 128 bytes) and W_r rows
+// (TE x 128 bytes, K-major transposed W_r), filled by direct-to-LDS loads two steps ahead: the
+// tile reads its token rows once and W_r once per 128 tokens, where a wave reading its operands
+// from global memory would fetch the token rows once per wave and W_r once per 32 tokens.
+template <int NWT, int NWE, int MB, int NB>
+__global__ __launch_bounds__(256, 1) void k_router_bf16(const uint8_t* __restrict__ x,
+                                                        const uint8_t* __restrict__ wrt,
+                                                        float* __restrict__ logits, int T, int H,
+                                                        int E, int splits) {
+  constexpr int NW = 4, NT = 256;
+  static_assert(NWT * NWE == NW, "four waves");
+  constexpr int TM = NWT * MB * 32, TE = NWE * NB * 32;
+  constexpr int ACH = TM * 8, BCH = TE * 8;  // 16-byte chunks of one stage (rows of 64 channels)
+  constexpr int AJ = ACH / NT, BJ = BCH / NT;
+  static_assert(TM == 128 && ACH % NT == 0 && BCH % NT == 0, "tile shape");
+  __shared__ u32x4 sA0[ACH];
+  __shared__ u32x4 sA1[ACH];
+  __shared__ u32x4 sA2[ACH];
+  __shared__ u32x4 sB0[BCH];
+  __shared__ u32x4 sB1[BCH];
+  __shared__ u32x4 sB2[BCH];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave / NWE, we = wave % NWE;
+  const int t0 = blockIdx.x * TM;
+  const int nk = H / 128, sp = blockIdx.y;
+  const int kc0 = (int)((long long)sp * nk / splits) * 128;
+  const int kc1 = (int)((long long)(sp + 1) * nk / splits) * 128;
+  const int KT = (kc1 - kc0) / 64;
+  // tile-relative byte offsets (rows clamped into x and W_r): below 4 GiB for any H < 2^24
+  const uint8_t* xb = x + ((size_t)t0 * H + kc0) * 2;
+  const uint8_t* wb = wrt + (size_t)kc0 * 2;
+  TileDma<AJ> da;
+  TileDma<BJ> db;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    int t = t0 + mb * 16 + r;
-    t = t < T ? t : T - 1;
-    arow[mb] = x + (size_t)t * H + kq;
+  for (int j = 0; j < AJ; ++j) {
+    const int r = dma_row<NW>(j, wave, lane);
+    const int t = t0 + r < T ? r : T - 1 - t0;
+    da.off[j] = (uint32_t)t * (uint32_t)H * 2u + (uint32_t)dma_chunk(r, lane) * 16u;
   }
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    int e = e0 + nb * 16 + r;
-    e = e < E ? e : E - 1;
-    brow[nb] = wrt + (size_t)e * H + kq;
+  for (int j = 0; j < BJ; ++j) {
+    const int r = dma_row<NW>(j, wave, lane);
+    const int e = r < E ? r : E - 1;
+    db.off[j] = (uint32_t)e * (uint32_t)H * 2u + (uint32_t)dma_chunk(r, lane) * 16u;
   }
-  f32x4 acc[2][4];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = kc0; k < kc1; k += 128) {
-    bf16x8 a[4][2], b[4][4];
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        a[ks][mb] = *reinterpret_cast<const bf16x8*>(arow[mb] + k + ks * 32);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        b[ks][nb] = *reinterpret_cast<const bf16x8*>(brow[nb] + k + ks * 32);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][mb], b[ks][nb], acc[mb][nb], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+  const int lrow = lane & 31, lk = lane >> 5;
+
+// x rows and W_r rows of step kt (clamped to the last step: past the end the loads are never read)
+#define RT_DMA(kt, sa_, sb_)                                                                        \
+  do {                                                                                              \
+    const uint32_t ko_ = (uint32_t)((kt) < KT ? (kt) : KT - 1) * 128u;                              \
+    _Pragma("unroll") for (int j_ = 0; j_ < AJ; ++j_)                                               \
+        dma_to_lds<16>(xb + (da.off[j_] + ko_), (sa_) + (j_ * NW + wave) * 64);                     \
+    _Pragma("unroll") for (int j_ = 0; j_ < BJ; ++j_)                                               \
+        dma_to_lds<16>(wb + (db.off[j_] + ko_), (sb_) + (j_ * NW + wave) * 64);                     \
+    __builtin_amdgcn_sched_barrier(0);                                                              \
+  } while (0)
+// step kt on stage (ca, cb); loads of step kt+2 into (na, nb_), the stage step kt-1 read
+#define RT_STEP(kt, ca, cb, na, nb_)                                                                \
+  {                                                                                                 \
+    RT_DMA((kt) + 2, na, nb_);                                                                      \
+    _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                              \
+      const int slot_ = (ks * 2 + lk) ^ lds_swz(lrow);                                              \
+      bf16x8 a_[MB], b_[NB];                                                                        \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                             \
+          a_[mb] = __builtin_bit_cast(bf16x8, (ca)[(wt * MB * 32 + mb * 32 + lrow) * 8 + slot_]);    \
+      _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                             \
+          b_[nb] = __builtin_bit_cast(bf16x8, (cb)[(we * NB * 32 + nb * 32 + lrow) * 8 + slot_]);    \
+      _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                             \
+          _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                         \
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_[mb], b_[nb], acc[mb][nb], 0, 0, 0); \
+    }                                                                                               \
+    __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(AJ + BJ));                                          \
+    __builtin_amdgcn_s_barrier();                                                                   \
   }
-  // 16x16 accumulator layout: lane holds column (lane & 15), rows 4*(lane>>4) + i
-  float* out = logits + (size_t)s * T * E;
+  RT_DMA(0, sA0, sB0);
+  RT_DMA(1, sA1, sB1);
+  __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(AJ + BJ));
+  __builtin_amdgcn_s_barrier();
+  int kt = 0;
+  for (; kt + 3 <= KT; kt += 3) {
+    RT_STEP(kt, sA0, sB0, sA2, sB2)
+    RT_STEP(kt + 1, sA1, sB1, sA0, sB0)
+    RT_STEP(kt + 2, sA2, sB2, sA1, sB1)
+  }
+  if (kt < KT) RT_STEP(kt, sA0, sB0, sA2, sB2)
+  if (kt + 1 < KT) RT_STEP(kt + 1, sA1, sB1, sA0, sB0)
+#undef RT_DMA
+#undef RT_STEP
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // 32x32 accumulator layout: lane holds column (lane & 31), rows 8*(i/4) + 4*(lane>>5) + i%4
+  float* out = logits + (size_t)sp * T * E;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int e = e0 + nb * 16 + (lane & 15);
+    for (int nb = 0; nb < NB; ++nb) {
+      const int e = we * NB * 32 + nb * 32 + lrow;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + mb * 16 + (lane >> 4) * 4 + i;
+      for (int i = 0; i < 16; ++i) {
+        const int t = t0 + wt * MB * 32 + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
         if (t < T && e < E) out[(size_t)t * E + e] = acc[mb][nb][i];
       }
     }
@@ -133,10 +176,18 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t* __restrict_
 
 hipError_t launch_router_bf16(const void* x, const void* wrt, float* logits, int T, int H, int E,
                               int splits, hipStream_t s) {
-  dim3 grid((T + 31) / 32, splits);
+  const dim3 grid((T + 127) / 128, splits);
+  const uint8_t* xi = static_cast<const uint8_t*>(x);
+  const uint8_t* wi = static_cast<const uint8_t*>(wrt);
   return timed_launch("router_bf16", s, [&] {
-    hipLaunchKernelGGL(k_router_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(wrt), logits, T, H, E, splits);
+    if (E <= 32)
+      hipLaunchKernelGGL((k_router_bf16<4, 1, 1, 1>), grid, dim3(256), 0, s, xi, wi, logits, T, H, E, splits);
+    else if (E <= 64)
+      hipLaunchKernelGGL((k_router_bf16<4, 1, 1, 2>), grid, dim3(256), 0, s, xi, wi, logits, T, H, E, splits);
+    else if (E <= 128)
+      hipLaunchKernelGGL((k_router_bf16<2, 2, 2, 2>), grid, dim3(256), 0, s, xi, wi, logits, T, H, E, splits);
+    else
+      hipLaunchKernelGGL((k_router_bf16<1, 4, 4, 2>), grid, dim3(256), 0, s, xi, wi, logits, T, H, E, splits);
   });
 }
 

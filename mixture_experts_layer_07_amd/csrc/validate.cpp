@@ -73,9 +73,10 @@ moe_status check_config(const moe_config* c, std::string* why) {
 
 int route_splits(const moe_config& c) {
   if (c.dtype == MOE_F32) return 1;
-  const int mtiles = (c.T + 31) / 32;
+  const int mtiles = (c.T + 127) / 128;    // 128-token router tiles
   const int nk = c.H / 128;
-  int want = (256 + mtiles - 1) / mtiles;  // aim for >= 256 workgroups
+  int want = (256 + mtiles - 1) / mtiles;  // aim for >= 256 workgroups,
+  if (want > 16) want = 16;                // but keep the partial sums of the top-K kernel few
   if (want < 1) want = 1;
   return want < nk ? want : nk;
 }
