@@ -38,7 +38,10 @@ __device__ __forceinline__ void load_row_chunk(const uint8_t* row, int ch, float
   }
 }
 
-template <int EPC, bool YF32, bool OF32>
+// KC > 0: K known at compile time, so every row chunk of a step is loaded before the sum (all K
+// loads in flight at once); dropped pairs (pair_pos < 0) read row 0 and are left out by a select,
+// which keeps the sum bit-identical to skipping them. KC == 0: any K, one row at a time.
+template <int EPC, bool YF32, bool OF32, int KC>
 __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ pair_pos,
                                                  const float* __restrict__ w,
                                                  const uint8_t* __restrict__ y,
@@ -59,13 +62,29 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ pai
     float acc[EPC], v[EPC];
 #pragma unroll
     for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int r = spp[k];
-      if (r < 0) continue;
-      load_row_chunk<EPC, YF32>(y + (size_t)r * yrow, ch, v);
-      const float wk = sw[k];
+    if constexpr (KC > 0) {
+      float vk[KC][EPC];
 #pragma unroll
-      for (int j = 0; j < EPC; ++j) acc[j] = fmaf(wk, v[j], acc[j]);
+      for (int k = 0; k < KC; ++k) {
+        const int r = spp[k];
+        load_row_chunk<EPC, YF32>(y + (size_t)(r < 0 ? 0 : r) * yrow, ch, vk[k]);
+      }
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const bool live = spp[k] >= 0;
+        const float wk = sw[k];
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) acc[j] = live ? fmaf(wk, vk[k][j], acc[j]) : acc[j];
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        const int r = spp[k];
+        if (r < 0) continue;
+        load_row_chunk<EPC, YF32>(y + (size_t)r * yrow, ch, v);
+        const float wk = sw[k];
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) acc[j] = fmaf(wk, v[j], acc[j]);
+      }
     }
     if (ysh) {
       load_row_chunk<EPC, YF32>(ysh + (size_t)t * yrow, ch, v);
@@ -89,22 +108,36 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ pai
   }
 }
 
+template <int EPC, bool YF32, bool OF32>
+static void launch_combine_k(int K, dim3 grid, hipStream_t s, const int32_t* pair_pos, const float* w,
+                             const uint8_t* y, const uint8_t* ysh, uint8_t* o, int H) {
+  const dim3 block(256);
+  switch (K) {
+    case 1: hipLaunchKernelGGL((k_combine<EPC, YF32, OF32, 1>), grid, block, 0, s, pair_pos, w, y, ysh, o, H, K); break;
+    case 2: hipLaunchKernelGGL((k_combine<EPC, YF32, OF32, 2>), grid, block, 0, s, pair_pos, w, y, ysh, o, H, K); break;
+    case 4: hipLaunchKernelGGL((k_combine<EPC, YF32, OF32, 4>), grid, block, 0, s, pair_pos, w, y, ysh, o, H, K); break;
+    case 6: hipLaunchKernelGGL((k_combine<EPC, YF32, OF32, 6>), grid, block, 0, s, pair_pos, w, y, ysh, o, H, K); break;
+    case 8: hipLaunchKernelGGL((k_combine<EPC, YF32, OF32, 8>), grid, block, 0, s, pair_pos, w, y, ysh, o, H, K); break;
+    default: hipLaunchKernelGGL((k_combine<EPC, YF32, OF32, 0>), grid, block, 0, s, pair_pos, w, y, ysh, o, H, K);
+  }
+}
+
 hipError_t launch_combine(const moe_config& c, const int32_t* pair_pos, const float* w,
                           const void* y_perm, const void* y_shared, void* out, hipStream_t s) {
   const uint8_t* y = static_cast<const uint8_t*>(y_perm);
   const uint8_t* ysh = static_cast<const uint8_t*>(y_shared);
   uint8_t* o = static_cast<uint8_t*>(out);
-  const dim3 grid(c.T), block(256);
+  const dim3 grid(c.T);
   if (c.dtype == MOE_F32)
     return timed_launch("combine_f32", s, [&] {
-      hipLaunchKernelGGL((k_combine<4, true, true>), grid, block, 0, s, pair_pos, w, y, ysh, o, c.H, c.K);
+      launch_combine_k<4, true, true>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
     });
   if (c.dtype == MOE_BF16)
     return timed_launch("combine_f32_to_bf16", s, [&] {
-      hipLaunchKernelGGL((k_combine<8, true, false>), grid, block, 0, s, pair_pos, w, y, ysh, o, c.H, c.K);
+      launch_combine_k<8, true, false>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
     });
   return timed_launch("combine_bf16", s, [&] {
-    hipLaunchKernelGGL((k_combine<8, false, false>), grid, block, 0, s, pair_pos, w, y, ysh, o, c.H, c.K);
+    launch_combine_k<8, false, false>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
   });
 }
 
