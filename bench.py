@@ -55,7 +55,7 @@ def kernel_work(cfg, active, gather=True):
     xb = 4 if cfg.dtype == "f32" else 2          # x and out
     ab = 1 if q else xb                          # activation operand bytes (x_perm, h)
     wb = 0.5 if mx else ab                       # weight bytes per element (MX: two e2m1 per byte)
-    yb = 2 if q else 4                           # y rows: fp32 (f32/bf16 layers), bf16 (fp8 / MX layers)
+    yb = 4 if cfg.dtype == "f32" else 2          # y rows: fp32 (f32 layer), bf16 (the others)
     # scale bytes per element: fp8 one fp32 per 128 activations / per 128x128 weights; MX one
     # E8M0 byte per 32 elements of either operand
     sc = 4.0 / 128 if fp8 else (1.0 / 32 if mx else 0.0)
@@ -98,8 +98,7 @@ def kernel_work(cfg, active, gather=True):
             add(f"shared/quantize_{qn}", 0.0, T * H * 2 + T * H * (1 + sc))
         add("shared/build_tiles", 0.0, 8)
         ffn("shared/", T, 1, Is, T)
-    cname = {"f32": "combine_f32", "bf16": "combine_f32_to_bf16", "fp8": "combine_bf16",
-             "mxfp4": "combine_bf16"}[cfg.dtype]
+    cname = "combine_f32" if cfg.dtype == "f32" else "combine_bf16"
     add("combine/" + cname, 0.0, P * 4 + T * K * 4 + P * H * yb + (T * H * yb if Is else 0) + T * H * xb)
     return w
 

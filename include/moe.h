@@ -54,6 +54,8 @@ typedef enum moe_status {
  *               e4m3 for the experts; expert weights are e4m3 codes with one fp32 scale per
  *               128x128 block; the SwiGLU output is re-quantised per row per 128 channels;
  *               fp32 accumulation; y_perm, y_shared and out are bf16.
+ *  (MOE_BF16 likewise stores y_perm and y_shared as bf16, rounded once from the fp32
+ *  accumulators of Linear-2.)
  *  MOE_MXFP4    FP8 activations times FP4 weights ("DeepGEMM质变：从GEMM库到统一LLM计算原语平台",
  *               itsolotime.com, 1.1 and 5.3) in the OCP microscaling formats: x and W_r are
  *               bf16; the library quantises x to MXFP8 (e4m3 codes, one E8M0 scale per 32
@@ -167,8 +169,7 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
  *   w2         device [n_experts, H, inter] (MOE_MXFP4: [n_experts, H, inter/2] packed e2m1)
  *   w2_scale   MOE_FP8_E4M3: device [n_experts, H/128, inter/128] fp32; MOE_MXFP4: device
  *              [n_experts] MX scale arrays of H rows and inter channels; else NULL
- *   y_rows     device [n_rows,H] out: fp32 (MOE_F32 and MOE_BF16: the fp32 accumulators, so
- *              the combine rounds only once) or bf16 (MOE_FP8_E4M3, MOE_MXFP4)
+ *   y_rows     device [n_rows,H] out: fp32 (MOE_F32) or bf16 (MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4)
  * The SwiGLU output is kept in the workspace (bf16, fp32 for MOE_F32, e4m3 + scales for fp8 and
  * MX). */
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_experts, int32_t n_rows, int32_t inter,
@@ -201,7 +202,7 @@ moe_status moe_expert_ffn_gather(const moe_config* cfg, int32_t n_experts, int32
  * added before the residual, "MoE" chapter README, section 0).
  *   pair_pos     device [P] int32 from moe_permute
  *   topk_weights device [T,K] fp32 from moe_route
- *   y_perm       device [P,H] from moe_expert_ffn (fp32 for MOE_F32 / MOE_BF16, bf16 for fp8)
+ *   y_perm       device [P,H] from moe_expert_ffn (fp32 for MOE_F32, else bf16)
  *   y_shared     device [T,H] shared expert output (same dtype as y_perm), or NULL
  *   out          device [T,H] out (fp32 for MOE_F32, else bf16)
  * out[t] = sum_k topk_weights[t,k] * y_perm[pair_pos[t*K+k]] (+ y_shared[t]), accumulated in

@@ -22,6 +22,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values as a bf16 pair, lo in the low half: the hardware's packed conversion, which
+// rounds to nearest even as f32_to_bf16 does.
+__device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const f2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
+// bf16 stores from a 32x32 MFMA accumulator, whose lane holds one column (lane & 31) of runs of
+// four rows. Given w, this lane's bf16 pair of rows (2p, 2p+1) in its column, the even lane of a
+// column pair (2c, 2c+1) gets row 2p of both columns and the odd lane row 2p+1, so every lane
+// writes two adjacent columns with one 4-byte store (the odd lane's row is one further down).
+// The neighbour's word comes over DPP (quad permutation 1,0,3,2: lane ^ 1), the halves are picked
+// by a byte permute; sel = colpair_sel(lane). Both lanes of a pair must be active.
+__device__ __forceinline__ uint32_t colpair_sel(int lane) { return (lane & 1) ? 0x03020706u : 0x05040100u; }
+__device__ __forceinline__ uint32_t rowpair_to_colpair(uint32_t w, uint32_t sel) {
+  const uint32_t n = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);
+  return __builtin_amdgcn_perm(n, w, sel);
+}
+
 // e4m3 ("fn" variant: bias 7, max 448, no infinities) from fp32: round to nearest even,
 // saturate to +-448, keep the sign (a negative value that rounds to zero gives 0x80).
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {

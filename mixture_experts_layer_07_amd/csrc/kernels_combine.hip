@@ -7,7 +7,7 @@
 // atomics are needed and the result does not depend on scheduling. Accumulation is fp32 in k
 // order, the shared row last, then one rounding to the output type.
 //
-// Expert rows arrive as fp32 (fp32 and bf16 layers) or bf16 (fp8 layer); the output is fp32
+// Expert rows arrive as fp32 (fp32 layer) or bf16 (bf16, fp8 and MX layers); the output is fp32
 // (fp32 layer) or bf16. Each thread handles EPC consecutive channels per step.
 #include "device.h"
 #include "internal.h"
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ pai
       uint32_t u[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        u[j] = (uint32_t)f32_to_bf16(acc[2 * j]) | ((uint32_t)f32_to_bf16(acc[2 * j + 1]) << 16);
+        u[j] = bf16x2(acc[2 * j], acc[2 * j + 1]);
       reinterpret_cast<uint4*>(o)[ch] = make_uint4(u[0], u[1], u[2], u[3]);
     }
   }
@@ -131,10 +131,6 @@ hipError_t launch_combine(const moe_config& c, const int32_t* pair_pos, const fl
   if (c.dtype == MOE_F32)
     return timed_launch("combine_f32", s, [&] {
       launch_combine_k<4, true, true>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
-    });
-  if (c.dtype == MOE_BF16)
-    return timed_launch("combine_f32_to_bf16", s, [&] {
-      launch_combine_k<8, true, false>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
     });
   return timed_launch("combine_bf16", s, [&] {
     launch_combine_k<8, false, false>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);

@@ -217,7 +217,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
   g2.ldb = (size_t)I * ws_ / 2;
   g2.b_exp = (size_t)H * I * ws_ / 2;
   g2.C = static_cast<uint8_t*>(a.y);
-  g2.ldc = (size_t)H * (fp8 || mx ? 2 : 4);  // y rows: fp32 for bf16 layers, bf16 for fp8 / MX layers
+  g2.ldc = (size_t)H * 2;  // y rows: bf16
   g2.n_tiles_n = (H + 255) / 256;
   g1.a_scale = static_cast<const float*>(a.x_scale);
   g1.b_scale = static_cast<const float*>(a.w13_scale);

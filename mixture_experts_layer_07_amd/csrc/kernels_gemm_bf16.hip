@@ -117,17 +117,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, 
   // instead of being hoisted out of the tile loop and held in registers across the K loop.
   int rbase = r0 + lk * 4;
   asm volatile("" : "+v"(rbase));
+  // bf16 outputs go out as column pairs (rowpair_to_colpair): the odd lane writes the second row
+  const int odd = lane & 1;
+  const uint32_t sel = colpair_sel(lane);
   if (GLU) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int q = 0; q < NB / 2; ++q) {
-        const int col = ti.nt * 128 + c0 / 2 + q * 32 + lrow;
+        const int col2 = (ti.nt * 128 + c0 / 2 + q * 32 + lrow) & ~1;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
-          const float h = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
-          __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(h), rc, r * ldc + col * 2, 0, 0);
+        for (int i = 0; i < 16; i += 2) {
+          const float h0 = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
+          const float h1 = silu_fast(acc[mb][2 * q][i + 1]) * acc[mb][2 * q + 1][i + 1];
+          const int r = rbase + odd + mb * 32 + (i >> 2) * 8 + (i & 3);
+          __builtin_amdgcn_raw_buffer_store_b32(rowpair_to_colpair(bf16x2(h0, h1), sel), rc, r * ldc + col2 * 2,
+                                                0, 0);
         }
       }
   } else {
@@ -136,14 +141,20 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const TileInfo& ti, 
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = ti.nt * 256 + c0 + nb * 32 + lrow;
-        if (col < g.N_out) {
+        if (col < g.N_out) {  // (N_out is even: both lanes of a column pair pass or fail together)
+          if (OUTF32) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
-            if (OUTF32)
+            for (int i = 0; i < 16; ++i) {
+              const int r = rbase + mb * 32 + (i >> 2) * 8 + (i & 3);
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mb][nb][i]), rc, r * ldc + col * 4, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[mb][nb][i]), rc, r * ldc + col * 2, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+              const int r = rbase + odd + mb * 32 + (i >> 2) * 8 + (i & 3);
+              __builtin_amdgcn_raw_buffer_store_b32(rowpair_to_colpair(bf16x2(acc[mb][nb][i], acc[mb][nb][i + 1]), sel),
+                                                    rc, r * ldc + (col & ~1) * 2, 0, 0);
+            }
           }
         }
       }
@@ -461,12 +472,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& g1, const GemmArgs& g2, int variant,
     const int grid = round8(cus);
     if ((e = launch_one("gemm_bf16_gateup_swiglu", k_gemm_bf16_w4<true, false>, grid, 256, g1, s)) != hipSuccess)
       return e;
-    return launch_one("gemm_bf16_down", k_gemm_bf16_w4<false, true>, grid, 256, g2, s);
+    return launch_one("gemm_bf16_down", k_gemm_bf16_w4<false, false>, grid, 256, g2, s);
   }
   const int grid = round8(cus * 2);
   if ((e = launch_one("gemm_bf16_gateup_swiglu_m32", k_gemm_bf16_m32<true, false>, grid, 256, g1, s)) != hipSuccess)
     return e;
-  return launch_one("gemm_bf16_down_m32", k_gemm_bf16_m32<false, true>, grid, 256, g2, s);
+  return launch_one("gemm_bf16_down_m32", k_gemm_bf16_m32<false, false>, grid, 256, g2, s);
 }
 
 }  // namespace moe

@@ -265,12 +265,14 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int col = ti.nt * BN + wn * WN + nb * 32 + lrow;
-          if (col < g.N_out) {
+          if (col < g.N_out) {  // (N_out is even: both lanes of a column pair pass or fail together)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+            for (int i = 0; i < 16; i += 2) {
+              // bf16 column pairs, the odd lane writing the second row (rowpair_to_colpair)
+              const uint32_t w = rowpair_to_colpair(bf16x2(acc[mb][nb][i], acc[mb][nb][i + 1]), colpair_sel(lrow));
+              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3) + (lrow & 1);
               if (r < ti.mvalid)
-                reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(acc[mb][nb][i]);
+                *reinterpret_cast<uint32_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc + (col & ~1) * 2) = w;
             }
           }
         }
@@ -557,12 +559,14 @@ __global__ __launch_bounds__(P::NT, MINB) void k_gemm_mx_r3(GemmArgs g) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const int col = ti.nt * BN + wn * WN + nb * 32 + lrow;
-          if (col < g.N_out) {
+          if (col < g.N_out) {  // (N_out is even: both lanes of a column pair pass or fail together)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+            for (int i = 0; i < 16; i += 2) {
+              // bf16 column pairs, the odd lane writing the second row (rowpair_to_colpair)
+              const uint32_t w = rowpair_to_colpair(bf16x2(acc[mb][nb][i], acc[mb][nb][i + 1]), colpair_sel(lrow));
+              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3) + (lrow & 1);
               if (r < ti.mvalid)
-                reinterpret_cast<uint16_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc)[col] = f32_to_bf16(acc[mb][nb][i]);
+                *reinterpret_cast<uint32_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc + (col & ~1) * 2) = w;
             }
           }
         }

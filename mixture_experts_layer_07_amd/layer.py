@@ -50,8 +50,8 @@ class MoELayer:
             # the e4m3 codes of the T input rows, read by the gathered Linear-1 and the shared expert
             self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
             self.xq_scale = self._scales(T, H, dev)
-        # expert outputs: fp32 accumulators for fp32 / bf16 layers, bf16 for the fp8 / MX layers
-        ydt = torch.bfloat16 if self.quant else torch.float32
+        # expert outputs: fp32 for the fp32 layer, bf16 otherwise
+        ydt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
         self.y_perm = torch.empty((P, H), dtype=ydt, device=dev)
         self.out = torch.empty((T, H), dtype=act, device=dev)
         if self.shared is not None:
