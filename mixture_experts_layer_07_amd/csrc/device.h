@@ -31,6 +31,45 @@ __device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
+// Cross-lane moves over DPP (ctrl: 0xB1 lane ^ 1, 0x4E lane ^ 2 within a quad; 0x12n rotates each
+// row of 16 lanes right by n, lane l reading lane l - n).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) { return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v))); }
+
+// 4x4 transpose inside each quad of lanes: lane q of a quad holds a[j] = element (j, q) of a 4x4
+// block and ends with a[k] = element (q, k). Two exchange stages (lane ^ 2, then lane ^ 1), each
+// sending half of a lane's values and keeping the other half. All lanes of a quad must be active.
+__device__ __forceinline__ void quad_transpose4(float (&a)[4], int lane) {
+  const bool hi = lane & 2, odd = lane & 1;
+  float s0 = hi ? a[0] : a[2], s1 = hi ? a[1] : a[3];
+  float r0 = dpp_f32<0x4E>(s0), r1 = dpp_f32<0x4E>(s1);
+  a[0] = hi ? r0 : a[0];
+  a[1] = hi ? r1 : a[1];
+  a[2] = hi ? a[2] : r0;
+  a[3] = hi ? a[3] : r1;
+  s0 = odd ? a[0] : a[1];
+  s1 = odd ? a[2] : a[3];
+  r0 = dpp_f32<0xB1>(s0);
+  r1 = dpp_f32<0xB1>(s1);
+  a[0] = odd ? r0 : a[0];
+  a[1] = odd ? a[1] : r0;
+  a[2] = odd ? r1 : a[2];
+  a[3] = odd ? a[3] : r1;
+}
+
+// Maximum over the eight lanes of a 32-lane half that share lane & 3 (one lane per quad):
+// rotations by 4 and 8 inside each row of 16 lanes, then the other row of the half (lane ^ 16,
+// a bit-mask swizzle). Unsigned, so non-negative floats compare by their bit patterns.
+__device__ __forceinline__ uint32_t max_over_quads(uint32_t m) {
+  m = max(m, dpp_u32<0x124>(m));
+  m = max(m, dpp_u32<0x128>(m));
+  return max(m, (uint32_t)__builtin_amdgcn_ds_swizzle((int)m, 0x401F));
+}
+
 // bf16 stores from a 32x32 MFMA accumulator, whose lane holds one column (lane & 31) of runs of
 // four rows. Given w, this lane's bf16 pair of rows (2p, 2p+1) in its column, the even lane of a
 // column pair (2c, 2c+1) gets row 2p of both columns and the odd lane row 2p+1, so every lane

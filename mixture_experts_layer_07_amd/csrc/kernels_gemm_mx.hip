@@ -83,6 +83,42 @@ __device__ __forceinline__ void mma_step_mx(const u32x4* sta, const u32x4* stb, 
   mma_sub_mx<3, MB, NB>(la, lb, sA, sB, h, sa, sb, acc);
 }
 
+// Linear-1 epilogue of one 32 x 32 block of h = SiLU(gate) * up (gate and up accumulators of the
+// same columns; lane holds column lane & 31, rows 8*(i/4) + 4*(lane/32) + i%4). Each row's 32
+// values are one MX block: E8M0 code = biased exponent of the row maximum minus 8, clamped at 0,
+// codes = e4m3(h * 2^(127 - code)), rounded to nearest even and saturated at 448 (the hardware's
+// packed conversion after a clamp). A 4x4 transpose inside each quad gives every lane four
+// adjacent columns of one row, so the row maximum is the lane's own maximum reduced over the
+// eight quads of its half-wave, and the four codes leave as one 4-byte store. cbase points at
+// tile row 0 of the block's first column, sbase at tile row 0's scale byte of the block (rows 4
+// bytes apart); rows at or past mvalid are not stored. The whole wave must be active.
+__device__ __forceinline__ void mx_glu_block(const f32x16& gate, const f32x16& up, int lane, int rb, int mvalid,
+                                             uint8_t* cbase, size_t ldc, uint8_t* sbase) {
+  const int qd = lane & 3, cq = (lane & 31) >> 2, hh = lane >> 5;
+#pragma unroll
+  for (int gi = 0; gi < 4; ++gi) {
+    float a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = silu_fast(gate[4 * gi + j]) * up[4 * gi + j];
+    quad_transpose4(a, lane);  // a[k]: row rb + 8 gi + 4 hh + qd, column 4 cq + k
+    uint32_t m = max(max(__float_as_uint(a[0]) & 0x7FFFFFFFu, __float_as_uint(a[1]) & 0x7FFFFFFFu),
+                     max(__float_as_uint(a[2]) & 0x7FFFFFFFu, __float_as_uint(a[3]) & 0x7FFFFFFFu));
+    m = max_over_quads(m);
+    const int ex = (int)(m >> 23);
+    const int code = ex > 8 ? ex - 8 : 0;
+    float q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(a[k], 127 - code), -448.f, 448.f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+    const int r = rb + gi * 8 + hh * 4 + qd;
+    if (r < mvalid) {
+      *reinterpret_cast<uint32_t*>(cbase + (size_t)r * ldc + 4 * cq) = (uint32_t)w;
+      if (cq == 0) sbase[(size_t)r * 4] = (uint8_t)code;
+    }
+  }
+}
+
 // BM x BN tiles, NWM x NWN waves of WM x WN; one K step is 256 channels. Requires K % 256 == 0.
 template <int BM, int BN, int NWM, int NWN, bool GLU, int MINB>
 __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
@@ -238,27 +274,11 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
 #undef MOE_MX_STEP
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (GLU) {
-      // h for this wave's 32 columns (one MX block per row): lane = column, 16 rows per lane
-      uint8_t* csc = reinterpret_cast<uint8_t*>(g.c_scale);
-      const size_t c_sld = (size_t)g.c_scale_ld;  // rows of the h scale array
+      // h for this wave's 32 columns (one MX block per row)
+      uint8_t* sb = reinterpret_cast<uint8_t*>(g.c_scale) + ((size_t)ti.nt * g.c_scale_ld + ti.row0) * 4 + wn;
+      uint8_t* cb = g.C + (size_t)ti.row0 * g.ldc + ti.nt * 128 + wn * 32;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float hv = silu_fast(acc[mb][0][i]) * acc[mb][1][i];
-          float m = fabsf(hv);
-#pragma unroll
-          for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-          const int ex = (int)(__float_as_uint(m) >> 23);  // biased exponent of the block maximum
-          const int code = ex > 8 ? ex - 8 : 0;             // floor(log2 max) - 8 + 127, clamped at 0
-          const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-          if (r < ti.mvalid) {
-            const size_t row = (size_t)(ti.row0 + r);
-            const int col = ti.nt * 128 + wn * 32 + lrow;
-            g.C[row * g.ldc + col] = (uint8_t)f32_to_e4m3(__builtin_amdgcn_ldexpf(hv, 127 - code));
-            if (lrow == 0) csc[((size_t)ti.nt * c_sld + row) * 4 + wn] = (uint8_t)code;
-          }
-        }
+      for (int mb = 0; mb < MB; ++mb) mx_glu_block(acc[mb][0], acc[mb][1], lane, wm * WM + mb * 32, ti.mvalid, cb, g.ldc, sb);
     } else {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -531,28 +551,13 @@ __global__ __launch_bounds__(P::NT, MINB) void k_gemm_mx_r3(GemmArgs g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (GLU) {
       // this wave's WN / 2 h columns: NB / 2 MX blocks per row (gate / up pairs nb = 2q, 2q + 1)
-      uint8_t* csc = reinterpret_cast<uint8_t*>(g.c_scale);
-      const size_t c_sld = (size_t)g.c_scale_ld;
+      uint8_t* sb = reinterpret_cast<uint8_t*>(g.c_scale) + ((size_t)ti.nt * g.c_scale_ld + ti.row0) * 4 + wn * (NB / 2);
+      uint8_t* cb = g.C + (size_t)ti.row0 * g.ldc + ti.nt * 128 + wn * (WN / 2);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int q = 0; q < NB / 2; ++q)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float hv = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
-            float m = fabsf(hv);
-#pragma unroll
-            for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-            const int ex = (int)(__float_as_uint(m) >> 23);
-            const int code = ex > 8 ? ex - 8 : 0;
-            const int r = wm * WM + mb * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
-            if (r < ti.mvalid) {
-              const size_t row = (size_t)(ti.row0 + r);
-              const int col = ti.nt * 128 + wn * (WN / 2) + q * 32 + lrow;
-              g.C[row * g.ldc + col] = (uint8_t)f32_to_e4m3(__builtin_amdgcn_ldexpf(hv, 127 - code));
-              if (lrow == 0) csc[((size_t)ti.nt * c_sld + row) * 4 + wn * (NB / 2) + q] = (uint8_t)code;
-            }
-          }
+          mx_glu_block(acc[mb][2 * q], acc[mb][2 * q + 1], lane, wm * WM + mb * 32, ti.mvalid, cb + q * 32, g.ldc, sb + q);
     } else {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
