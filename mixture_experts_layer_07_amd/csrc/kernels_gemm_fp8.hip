@@ -208,42 +208,50 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (GLU) {
-      // per-row absmax over the tile's 128 h columns: lanes (32 columns) -> waves (through LDS)
-      float* red = reinterpret_cast<float*>(sA0);  // [BM][NWN]; every wave is past the last read
-      float hv[MB][NB / 2][16];
+      // per-row absmax over the tile's 128 h columns: lanes (32 columns) -> waves (through LDS).
+      // A 4x4 transpose inside each quad of lanes first gives every lane four adjacent columns of
+      // one row (row rb + 8 gi + 4 lk + (lane & 3), columns 4 ((lane & 31) / 4) + k of the wave's
+      // 32), so a row's maximum is the lane's own maximum reduced over the eight quads of its
+      // half-wave, and its four codes leave as one 4-byte store.
+      static_assert(NB == 2, "one gate/up block pair per wave: a wave holds 32 of the 128 h columns");
+      uint32_t* red = reinterpret_cast<uint32_t*>(sA0);  // [BM][NWN] maxima (bits); every wave is past the last read
+      const int qd = lane & 3, cq = lrow >> 2;
+      float hv[MB][4][4];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float m = 0.f;
+        for (int gi = 0; gi < 4; ++gi) {
 #pragma unroll
-          for (int q = 0; q < NB / 2; ++q) {
-            hv[mb][q][i] = silu_fast(acc[mb][2 * q][i]) * acc[mb][2 * q + 1][i];
-            m = fmaxf(m, fabsf(hv[mb][q][i]));
-          }
-#pragma unroll
-          for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-          const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
-          if (lrow == 0) red[r * NWN + wn] = m;
+          for (int j = 0; j < 4; ++j) hv[mb][gi][j] = silu_fast(acc[mb][0][4 * gi + j]) * acc[mb][1][4 * gi + j];
+          quad_transpose4(hv[mb][gi], lane);
+          uint32_t m = max(max(__float_as_uint(hv[mb][gi][0]) & 0x7FFFFFFFu, __float_as_uint(hv[mb][gi][1]) & 0x7FFFFFFFu),
+                           max(__float_as_uint(hv[mb][gi][2]) & 0x7FFFFFFFu, __float_as_uint(hv[mb][gi][3]) & 0x7FFFFFFFu));
+          m = max_over_quads(m);
+          const int r = wm * WM + mb * 32 + gi * 8 + lk * 4 + qd;
+          if (cq == 0) red[r * NWN + wn] = m;
         }
       __syncthreads();
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
-          float m = 0.f;
+        for (int gi = 0; gi < 4; ++gi) {
+          const int r = wm * WM + mb * 32 + gi * 8 + lk * 4 + qd;
+          uint32_t mb_ = 0;
 #pragma unroll
-          for (int w = 0; w < NWN; ++w) m = fmaxf(m, red[r * NWN + w]);
+          for (int w = 0; w < NWN; ++w) mb_ = max(mb_, red[r * NWN + w]);
+          const float m = __uint_as_float(mb_);
           const float scale = m / 448.0f;
-          if (r < ti.mvalid) {
-            uint8_t* crow = g.C + (size_t)(ti.row0 + r) * g.ldc;
+          // codes: e4m3(h / scale), RNE, saturating (the hardware's packed conversion after a clamp);
+          // an all-zero row block has scale 0 and codes 0
+          float q[4];
 #pragma unroll
-            for (int q = 0; q < NB / 2; ++q) {
-              const int col = ti.nt * 128 + (wn * (NB / 2) + q) * 32 + lrow;
-              crow[col] = m > 0.f ? (uint8_t)f32_to_e4m3(hv[mb][q][i] / scale) : (uint8_t)0;
-            }
-            if (wn == 0 && lrow == 0) g.c_scale[(size_t)(ti.row0 + r) * g.c_scale_ld + ti.nt] = scale;
+          for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(hv[mb][gi][k] / scale, -448.f, 448.f);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
+          if (!(m > 0.f)) w = 0;
+          if (r < ti.mvalid) {
+            *reinterpret_cast<uint32_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc + ti.nt * 128 + wn * 32 + 4 * cq) = (uint32_t)w;
+            if (wn == 0 && cq == 0) g.c_scale[(size_t)(ti.row0 + r) * g.c_scale_ld + ti.nt] = scale;
           }
         }
       __syncthreads();  // red[] aliases the first stage of the next tile
