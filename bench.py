@@ -4,7 +4,7 @@ One step = one whole layer forward (route -> permute -> expert FFN (+ shared exp
 over one batch of synthetic inputs already resident in HBM. Default workload: the Mixtral-shaped
 layer (T=4096, H=4096, I=14336, E=8, K=2, bf16). Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 25] [--config 2] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -26,8 +26,9 @@ HBM_PEAK = 8000.0                                       # GB/s
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    # (the shader clock settles over the first ~40 ms of back-to-back layers: warm-up covers that)
+    p.add_argument("--warmup", type=int, default=25)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--x-perm", action="store_true",

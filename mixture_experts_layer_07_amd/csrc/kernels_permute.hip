@@ -166,52 +166,66 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ sort
   } else {
     uint8_t* o = out + (size_t)i * cols;
     const int nblk = cols / 128;
-    for (int b0 = 0; b0 < nblk; b0 += 4) {
-      const int b = b0 + (lane >> 4);
-      const bool act = b < nblk;
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (act) raw = reinterpret_cast<const uint4*>(in)[(size_t)b * 16 + (lane & 15)];
-      float v[8];
-      v[0] = bf16_to_f32(raw.x & 0xFFFF); v[1] = bf16_to_f32(raw.x >> 16);
-      v[2] = bf16_to_f32(raw.y & 0xFFFF); v[3] = bf16_to_f32(raw.y >> 16);
-      v[4] = bf16_to_f32(raw.z & 0xFFFF); v[5] = bf16_to_f32(raw.z >> 16);
-      v[6] = bf16_to_f32(raw.w & 0xFFFF); v[7] = bf16_to_f32(raw.w >> 16);
-      float m = 0.f;
+    // the loads of up to kBatch rounds (4 groups each) are issued before any is encoded, so
+    // each lane keeps several 16-byte reads in flight instead of one
+    constexpr int kBatch = 8;
+    for (int g0 = 0; g0 < nblk; g0 += 4 * kBatch) {
+      uint4 raw[kBatch];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-      if (MODE == 1) {
+      for (int u = 0; u < kBatch; ++u) {
+        const int b = g0 + 4 * u + (lane >> 4);
+        raw[u] = b < nblk ? reinterpret_cast<const uint4*>(in)[(size_t)b * 16 + (lane & 15)] : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-        for (int o2 = 1; o2 < 16; o2 <<= 1) m = fmaxf(m, __shfl_xor(m, o2, 64));
-        const float scale = m / 448.0f;
-        uint32_t lo = 0, hi = 0;
-        if (m > 0.f) {
+      for (int u = 0; u < kBatch; ++u) {
+        if (g0 + 4 * u >= nblk) break;  // (uniform)
+        const int b = g0 + 4 * u + (lane >> 4);
+        const bool act = b < nblk;
+        float v[8];
+        v[0] = bf16_to_f32(raw[u].x & 0xFFFF); v[1] = bf16_to_f32(raw[u].x >> 16);
+        v[2] = bf16_to_f32(raw[u].y & 0xFFFF); v[3] = bf16_to_f32(raw[u].y >> 16);
+        v[4] = bf16_to_f32(raw[u].z & 0xFFFF); v[5] = bf16_to_f32(raw[u].z >> 16);
+        v[6] = bf16_to_f32(raw[u].w & 0xFFFF); v[7] = bf16_to_f32(raw[u].w >> 16);
+        uint32_t m = 0;  // absmax as bits (non-negative floats order as their bit patterns)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[j] / scale) << (8 * j);
+        for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(v[j]) & 0x7FFFFFFFu);
+        float q[8];
+        if (MODE == 1) {
+          m = max(m, dpp_u32<0xB1>(m));   // lane ^ 1
+          m = max(m, dpp_u32<0x4E>(m));   // lane ^ 2
+          m = max(m, dpp_u32<0x124>(m));  // the quads of the 16-lane row
+          m = max(m, dpp_u32<0x128>(m));
+          const float mf = __uint_as_float(m);
+          const float scale = mf / 448.0f;
+          // e4m3(v / scale): IEEE division, then the hardware's packed RNE conversion after a
+          // clamp to +-448 (the same codes as the software encoder)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[4 + j] / scale) << (8 * j);
-        }
-        if (act) {
-          reinterpret_cast<uint2*>(o)[(size_t)b * 16 + (lane & 15)] = make_uint2(lo, hi);
-          if ((lane & 15) == 0) static_cast<float*>(scales)[(size_t)i * nblk + b] = scale;
-        }
-      } else {
-        // 32-channel block = 4 lanes
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        const int ex = (int)(__float_as_uint(m) >> 23);
-        const int code = ex > 8 ? ex - 8 : 0;
-        uint32_t lo = 0, hi = 0;
+          for (int j = 0; j < 8; ++j) q[j] = __builtin_amdgcn_fmed3f(v[j] / scale, -448.f, 448.f);
+          uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false), true);
+          uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false), true);
+          if (!(mf > 0.f)) lo = hi = 0;
+          if (act) {
+            reinterpret_cast<uint2*>(o)[(size_t)b * 16 + (lane & 15)] = make_uint2(lo, hi);
+            if ((lane & 15) == 0) static_cast<float*>(scales)[(size_t)i * nblk + b] = scale;
+          }
+        } else {
+          // 32-channel block = 4 lanes
+          m = max(m, dpp_u32<0xB1>(m));
+          m = max(m, dpp_u32<0x4E>(m));
+          const int ex = (int)(m >> 23);
+          const int code = ex > 8 ? ex - 8 : 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(v[j], 127 - code)) << (8 * j);
+          for (int j = 0; j < 8; ++j) q[j] = __builtin_amdgcn_fmed3f(__builtin_amdgcn_ldexpf(v[j], 127 - code), -448.f, 448.f);
+          const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false), true);
+          const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false), true);
+          const int base = lane & ~15;
+          uint32_t word = 0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(v[4 + j], 127 - code)) << (8 * j);
-        const int base = lane & ~15;
-        uint32_t word = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) word |= (uint32_t)__shfl(code, base + 4 * q, 64) << (8 * q);
-        if (act) {
-          reinterpret_cast<uint2*>(o)[(size_t)b * 16 + (lane & 15)] = make_uint2(lo, hi);
-          if ((lane & 15) == 0) static_cast<uint32_t*>(scales)[(size_t)b * rows + i] = word;
+          for (int qq = 0; qq < 4; ++qq) word |= (uint32_t)__shfl(code, base + 4 * qq, 64) << (8 * qq);
+          if (act) {
+            reinterpret_cast<uint2*>(o)[(size_t)b * 16 + (lane & 15)] = make_uint2(lo, hi);
+            if ((lane & 15) == 0) static_cast<uint32_t*>(scales)[(size_t)b * rows + i] = word;
+          }
         }
       }
     }
