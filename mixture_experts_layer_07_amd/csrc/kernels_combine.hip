@@ -8,7 +8,7 @@
 // order, the shared row last, then one rounding to the output type.
 //
 // Expert rows arrive as fp32 (fp32 layer) or bf16 (bf16, fp8 and MX layers); the output is fp32
-// (fp32 layer) or bf16. Each thread handles EPC consecutive channels per step.
+// (fp32 layer) or bf16. A chunk is EPC consecutive channels (16 bytes of a y row).
 #include "device.h"
 #include "internal.h"
 
@@ -38,9 +38,28 @@ __device__ __forceinline__ void load_row_chunk(const uint8_t* row, int ch, float
   }
 }
 
-// KC > 0: K known at compile time, so every row chunk of a step is loaded before the sum (all K
-// loads in flight at once); dropped pairs (pair_pos < 0) read row 0 and are left out by a select,
-// which keeps the sum bit-identical to skipping them. KC == 0: any K, one row at a time.
+template <int EPC, bool OF32>
+__device__ __forceinline__ void store_out_chunk(uint8_t* o, int ch, const float (&acc)[EPC]) {
+  if constexpr (OF32) {
+#pragma unroll
+    for (int q = 0; q < EPC / 4; ++q)
+      reinterpret_cast<float4*>(o)[(size_t)ch * (EPC / 4) + q] =
+          make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+  } else {
+    static_assert(OF32 || EPC == 8, "bf16 output is written 8 channels at a time");
+    uint32_t u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = bf16x2(acc[2 * j], acc[2 * j + 1]);
+    reinterpret_cast<uint4*>(o)[ch] = make_uint4(u[0], u[1], u[2], u[3]);
+  }
+}
+
+// Block (t, y) covers chunks [512 y, 512 y + 512) of token t's row: thread tid takes chunks
+// 512 y + tid and 512 y + 256 + tid (chunk = EPC channels = 16 bytes of a y row).
+// KC > 0: K known at compile time, so every row chunk of both chunks, the shared expert's
+// included, is loaded before the sums (2 (K + 1) loads in flight per thread); dropped pairs
+// (pair_pos < 0) read row 0 and are left out by a select, which keeps the sum bit-identical to
+// skipping them. KC == 0: any K, one row at a time.
 template <int EPC, bool YF32, bool OF32, int KC>
 __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ pair_pos,
                                                  const float* __restrict__ w,
@@ -58,25 +77,48 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ pai
   const size_t yrow = (size_t)H * (YF32 ? 4 : 2);
   const size_t orow = (size_t)H * (OF32 ? 4 : 2);
   const int nch = H / EPC;
-  for (int ch = tid; ch < nch; ch += 256) {
-    float acc[EPC], v[EPC];
+  const int cb = blockIdx.y * 512 + tid;
+  uint8_t* o = out + (size_t)t * orow;
+  if constexpr (KC > 0) {
+    const int c[2] = {cb, cb + 256};
+    const bool live_c[2] = {c[0] < nch, c[1] < nch};
+    const int cc[2] = {live_c[0] ? c[0] : 0, live_c[1] ? c[1] : 0};  // (reads stay in the row)
+    float vk[2][KC][EPC], vs[2][EPC];
 #pragma unroll
-    for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
-    if constexpr (KC > 0) {
-      float vk[KC][EPC];
+    for (int k = 0; k < KC; ++k) {
+      const int r = spp[k];
+      const uint8_t* row = y + (size_t)(r < 0 ? 0 : r) * yrow;
+      load_row_chunk<EPC, YF32>(row, cc[0], vk[0][k]);
+      load_row_chunk<EPC, YF32>(row, cc[1], vk[1][k]);
+    }
+    if (ysh) {
+      load_row_chunk<EPC, YF32>(ysh + (size_t)t * yrow, cc[0], vs[0]);
+      load_row_chunk<EPC, YF32>(ysh + (size_t)t * yrow, cc[1], vs[1]);
+    }
 #pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        const int r = spp[k];
-        load_row_chunk<EPC, YF32>(y + (size_t)(r < 0 ? 0 : r) * yrow, ch, vk[k]);
-      }
+    for (int u = 0; u < 2; ++u) {
+      float acc[EPC];
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
         const bool live = spp[k] >= 0;
         const float wk = sw[k];
 #pragma unroll
-        for (int j = 0; j < EPC; ++j) acc[j] = live ? fmaf(wk, vk[k][j], acc[j]) : acc[j];
+        for (int j = 0; j < EPC; ++j) acc[j] = live ? fmaf(wk, vk[u][k][j], acc[j]) : acc[j];
       }
-    } else {
+      if (ysh) {
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) acc[j] += vs[u][j];
+      }
+      if (live_c[u]) store_out_chunk<EPC, OF32>(o, c[u], acc);
+    }
+  } else {
+    const int cend = min(nch, (int)blockIdx.y * 512 + 512);
+    for (int ch = cb; ch < cend; ch += 256) {
+      float acc[EPC], v[EPC];
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
       for (int k = 0; k < K; ++k) {
         const int r = spp[k];
         if (r < 0) continue;
@@ -85,25 +127,12 @@ __global__ __launch_bounds__(256) void k_combine(const int32_t* __restrict__ pai
 #pragma unroll
         for (int j = 0; j < EPC; ++j) acc[j] = fmaf(wk, v[j], acc[j]);
       }
-    }
-    if (ysh) {
-      load_row_chunk<EPC, YF32>(ysh + (size_t)t * yrow, ch, v);
+      if (ysh) {
+        load_row_chunk<EPC, YF32>(ysh + (size_t)t * yrow, ch, v);
 #pragma unroll
-      for (int j = 0; j < EPC; ++j) acc[j] += v[j];
-    }
-    uint8_t* o = out + (size_t)t * orow;
-    if constexpr (OF32) {
-#pragma unroll
-      for (int q = 0; q < EPC / 4; ++q)
-        reinterpret_cast<float4*>(o)[(size_t)ch * (EPC / 4) + q] =
-            make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-    } else {
-      static_assert(OF32 || EPC == 8, "bf16 output is written 8 channels at a time");
-      uint32_t u[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        u[j] = bf16x2(acc[2 * j], acc[2 * j + 1]);
-      reinterpret_cast<uint4*>(o)[ch] = make_uint4(u[0], u[1], u[2], u[3]);
+        for (int j = 0; j < EPC; ++j) acc[j] += v[j];
+      }
+      store_out_chunk<EPC, OF32>(o, ch, acc);
     }
   }
 }
@@ -127,11 +156,14 @@ hipError_t launch_combine(const moe_config& c, const int32_t* pair_pos, const fl
   const uint8_t* y = static_cast<const uint8_t*>(y_perm);
   const uint8_t* ysh = static_cast<const uint8_t*>(y_shared);
   uint8_t* o = static_cast<uint8_t*>(out);
-  const dim3 grid(c.T);
-  if (c.dtype == MOE_F32)
+  // 512 chunks (16 bytes each) of a row per block
+  if (c.dtype == MOE_F32) {
+    const dim3 grid(c.T, (c.H / 4 + 511) / 512);
     return timed_launch("combine_f32", s, [&] {
       launch_combine_k<4, true, true>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
     });
+  }
+  const dim3 grid(c.T, (c.H / 8 + 511) / 512);
   return timed_launch("combine_bf16", s, [&] {
     launch_combine_k<8, false, false>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
   });
