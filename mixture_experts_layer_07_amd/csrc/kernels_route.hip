@@ -207,6 +207,62 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// Selection order as one pair of words: hi = the key mapped to an unsigned integer in the same
+// order (-0 and +0 equal, -inf lowest), lo = ~id (a lower id ranks higher). (hi, lo) compared
+// lexicographically orders candidates exactly as better() does; (0, 0) is below every candidate.
+__device__ __forceinline__ uint32_t ord_key(float k) {
+  const uint32_t u = __float_as_uint(k + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ void pick_max(uint32_t& k, uint32_t& i, uint32_t ok, uint32_t oi) {
+  const bool take = ok > k || (ok == k && oi > i);
+  k = take ? ok : k;
+  i = take ? oi : i;
+}
+template <int CTRL>
+__device__ __forceinline__ void pick_max_dpp(uint32_t& k, uint32_t& i) {
+  pick_max(k, i, dpp_u32<CTRL>(k), dpp_u32<CTRL>(i));
+}
+__device__ __forceinline__ uint32_t swz16(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); }
+
+// Wave-wide maximum of (k, i), returned in every lane: over each 32-lane half by DPP (lane ^ 1,
+// lane ^ 2, rotations by 4 and 8 inside each row of 16) and a swizzle (lane ^ 16), then the two
+// halves through readlane. Every lane must be active.
+__device__ __forceinline__ void wave_pick_max(uint32_t& k, uint32_t& i) {
+  pick_max_dpp<0xB1>(k, i);
+  pick_max_dpp<0x4E>(k, i);
+  pick_max_dpp<0x124>(k, i);
+  pick_max_dpp<0x128>(k, i);
+  pick_max(k, i, swz16(k), swz16(i));
+  uint32_t k0 = (uint32_t)__builtin_amdgcn_readlane((int)k, 0), i0 = (uint32_t)__builtin_amdgcn_readlane((int)i, 0);
+  const uint32_t k1 = (uint32_t)__builtin_amdgcn_readlane((int)k, 32), i1 = (uint32_t)__builtin_amdgcn_readlane((int)i, 32);
+  pick_max(k0, i0, k1, i1);
+  k = k0;
+  i = i0;
+}
+
+// The two largest of a 32-lane half's values (b1 >= b2, as a multiset), in every lane of the half.
+// Each step merges the top-2 of two disjoint lane sets: lane ^ 1, lane ^ 2, then rotations by 4 and
+// 8 inside a row of 16 (which, after the quad steps, pair different quads), then the other row.
+__device__ __forceinline__ void merge_top2(float& b1, float& b2, float o1, float o2) {
+  const float n1 = fmaxf(b1, o1);
+  b2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+  b1 = n1;
+}
+template <int CTRL>
+__device__ __forceinline__ void merge_top2_dpp(float& b1, float& b2) {
+  merge_top2(b1, b2, dpp_f32<CTRL>(b1), dpp_f32<CTRL>(b2));
+}
+__device__ __forceinline__ void half_top2(float& b1, float& b2) {
+  merge_top2_dpp<0xB1>(b1, b2);
+  merge_top2_dpp<0x4E>(b1, b2);
+  merge_top2_dpp<0x124>(b1, b2);
+  merge_top2_dpp<0x128>(b1, b2);
+  merge_top2(b1, b2, __uint_as_float(swz16(__float_as_uint(b1))), __uint_as_float(swz16(__float_as_uint(b2))));
+}
+
+// SB: splits of partial logits loaded per round trip (4, or 16 for the many splits of a small batch).
+template <int SB>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
                                               const float* __restrict__ bias, TopkParams p,
                                               int32_t* __restrict__ ids, float* __restrict__ weights) {
@@ -214,38 +270,41 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
   __shared__ int skept[4][256];
   __shared__ int sid[4][256];
   __shared__ float sw[4][256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.x * 4 + wave;
   if (t >= p.T) return;  // whole wave leaves together; no workgroup barrier below
   const int E = p.E;
   float z[4], sc[4], key[4];
-  // Sum the split-K partial logits in split order. Four splits are loaded before they are
-  // added, so up to 16 loads per lane are in flight (a decode-sized batch has many splits and
-  // few tokens: this loop is latency-bound).
+  // Sum the split-K partial logits in split order, SB splits per round trip of loads. Split and
+  // column indices are clamped, so every load is unconditional and in bounds; the sum skips the
+  // repeats.
   {
-    const float* src = logits + (size_t)t * E + lane;
+    const float* src = logits + (size_t)t * E;
     const size_t stride = (size_t)p.T * E;
     bool in[4];
+    int col[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       in[j] = lane + 64 * j < E;
+      col[j] = in[j] ? lane + 64 * j : 0;
       z[j] = 0.f;
     }
-    int s = 0;
-    for (; s + 4 <= p.splits; s += 4) {
-      float v[4][4];
+    for (int s0 = 0; s0 < p.splits; s0 += SB) {
+      float v[SB][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < SB; ++u) {
+        const int sp = s0 + u < p.splits ? s0 + u : p.splits - 1;
+        const float* row = src + (size_t)sp * stride;  // (uniform)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[u][j] = in[j] ? src[(size_t)(s + u) * stride + 64 * j] : 0.f;
+        for (int j = 0; j < 4; ++j) v[u][j] = row[col[j]];
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < SB; ++u)
+        if (s0 + u < p.splits) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) z[j] += v[u][j];
+          for (int j = 0; j < 4; ++j) z[j] += v[u][j];
+        }
     }
-    for (; s < p.splits; ++s)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z[j] += in[j] ? src[(size_t)s * stride + 64 * j] : 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (!in[j]) z[j] = -INFINITY;
@@ -278,98 +337,108 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits,
   }
   if (p.n_group > 1) {
     const int gs = E / p.n_group;
+    if (gs == 32) {
+      // Groups of 32: register j of half-wave h holds group 2j + h (experts 64j + 32h ..), so
+      // each group's score is a reduction over one half-wave; the group choice then runs on
+      // values that are the same in every lane.
+      float gsc[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j < E) skey[wave][lane + 64 * j] = key[j];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    // group scores: lane g (and g+64, ...) scans its group's keys
-    float gsc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int g = lane + 64 * j;
-      float v = -INFINITY;
-      if (g < p.n_group) {
-        float b1 = -INFINITY, b2 = -INFINITY;
-        for (int i = 0; i < gs; ++i) {
-          const float k = skey[wave][g * gs + i];
-          if (k > b1) {
-            b2 = b1;
-            b1 = k;
-          } else if (k > b2) {
-            b2 = k;
-          }
-        }
-        v = p.group_top2 ? b1 + b2 : b1;
+      for (int j = 0; j < 4; ++j) {
+        float b1 = key[j], b2 = -INFINITY;
+        half_top2(b1, b2);
+        const float v = p.group_top2 ? b1 + b2 : b1;
+        gsc[2 * j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+        gsc[2 * j + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
       }
-      gsc[j] = v;
-    }
-    int kept[4] = {0, 0, 0, 0};
-    for (int it = 0; it < p.topk_group; ++it) {
-      float bk = -INFINITY;
-      int bi = 0x7fffffff;
+      // kept: fewer than topk_group groups rank above it (score desc, id asc: a strict order,
+      // so these are exactly the topk_group best)
+      bool kept[8];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        int above = 0;
+#pragma unroll
+        for (int g2 = 0; g2 < 8; ++g2)
+          above += (g2 != g && g2 < p.n_group && better(gsc[g2], g2, gsc[g], g)) ? 1 : 0;
+        kept[g] = g < p.n_group && above < p.topk_group;
+      }
+      const int h = lane >> 5;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool kg = h ? kept[2 * j + 1] : kept[2 * j];
+        if (!kg) key[j] = -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lane + 64 * j < E) skey[wave][lane + 64 * j] = key[j];
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      // group scores: lane g (and g+64, ...) scans its group's keys
+      float gsc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int g = lane + 64 * j;
-        if (g < p.n_group && !kept[j] && better(gsc[j], g, bk, bi)) {
-          bk = gsc[j];
-          bi = g;
+        float v = -INFINITY;
+        if (g < p.n_group) {
+          float b1 = -INFINITY, b2 = -INFINITY;
+          for (int i = 0; i < gs; ++i) {
+            const float k = skey[wave][g * gs + i];
+            if (k > b1) {
+              b2 = b1;
+              b1 = k;
+            } else if (k > b2) {
+              b2 = k;
+            }
+          }
+          v = p.group_top2 ? b1 + b2 : b1;
         }
+        gsc[j] = v;
       }
+      int kept[4] = {0, 0, 0, 0};
+      for (int it = 0; it < p.topk_group; ++it) {
+        uint32_t bk = 0, bi = 0;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ok = __shfl_xor(bk, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ok, oi, bk, bi)) {
-          bk = ok;
-          bi = oi;
+        for (int j = 0; j < 4; ++j) {
+          const int g = lane + 64 * j;
+          if (g < p.n_group && !kept[j]) pick_max(bk, bi, ord_key(gsc[j]), ~(uint32_t)g);
         }
+        wave_pick_max(bk, bi);
+        const int win = (int)~bi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (lane + 64 * j == win) kept[j] = 1;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (lane + 64 * j == bi) kept[j] = 1;
-    }
+        if (lane + 64 * j < p.n_group) skept[wave][lane + 64 * j] = kept[j];
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j < p.n_group) skept[wave][lane + 64 * j] = kept[j];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !skept[wave][e / gs]) key[j] = -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E && !skept[wave][e / gs]) key[j] = -INFINITY;
+      }
     }
   }
-  // K rounds of wave arg-max over (key desc, id asc)
-  bool taken[4] = {false, false, false, false};
+  // K rounds of a wave-wide maximum over (key desc, id asc)
+  uint32_t ok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ok[j] = lane + 64 * j < E ? ord_key(key[j]) : 0u;
   for (int k = 0; k < p.K; ++k) {
-    float bk = -INFINITY, bs = 0.f;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !taken[j] && better(key[j], e, bk, bi)) {
-        bk = key[j];
-        bi = e;
-        bs = sc[j];
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ok = __shfl_xor(bk, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      const float os = __shfl_xor(bs, o, 64);
-      if (better(ok, oi, bk, bi)) {
-        bk = ok;
-        bi = oi;
-        bs = os;
-      }
-    }
+    uint32_t bk = 0, bi = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == bi) taken[j] = true;
+      if (ok[j] != 0u) pick_max(bk, bi, ok[j], ~(uint32_t)(lane + 64 * j));
+    wave_pick_max(bk, bi);
+    const int win = (int)~bi;  // (the same in every lane)
+    const int wj = win >> 6;
+    const float s_sel = wj == 0 ? sc[0] : (wj == 1 ? sc[1] : (wj == 2 ? sc[2] : sc[3]));
+    const float bs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_sel), win & 63));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j == win) ok[j] = 0u;
     if (lane == 0) {
-      sid[wave][k] = bi;
+      sid[wave][k] = win;
       sw[wave][k] = bs;
     }
   }
@@ -401,7 +470,10 @@ hipError_t launch_topk(const moe_config& c, const float* logits, int splits, con
   p.group_top2 = c.group_score == MOE_GROUP_TOP2_SUM;
   p.route_scale = c.route_scale;
   return timed_launch("topk", s, [&] {
-    hipLaunchKernelGGL(k_topk, dim3((c.T + 3) / 4), dim3(256), 0, s, logits, bias, p, ids, weights);
+    if (splits > 4)
+      hipLaunchKernelGGL(k_topk<16>, dim3((c.T + 3) / 4), dim3(256), 0, s, logits, bias, p, ids, weights);
+    else
+      hipLaunchKernelGGL(k_topk<4>, dim3((c.T + 3) / 4), dim3(256), 0, s, logits, bias, p, ids, weights);
   });
 }
 
