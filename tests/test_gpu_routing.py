@@ -54,6 +54,61 @@ def test_route_logits(name):
         assert max(len(set((r // gs).tolist())) for r in ids_g) <= cfg.topk_group
 
 
+# Logits from a small discrete set (and a bias of 0 or 1, beyond the sigmoid's range): keys,
+# group scores and their orders are then either exactly equal or far apart, so every token's
+# choice is fixed by the tie rule (higher key, then lower id) and is compared without excusing
+# near ties. The shapes reach both group-scoring paths of the kernel (groups of 32, any count up
+# to 8; other sizes) and the plain top-K.
+TIE_CASES = {
+    "256-8x32-top2sum-sigmoid-bias": dict(T=257, E=256, K=8, n_group=8, topk_group=4, group_rule="top2_sum",
+                                          score="sigmoid", route_scale=2.5, bias=True),
+    "256-8x32-max-softmax": dict(T=130, E=256, K=8, n_group=8, topk_group=4, group_rule="max",
+                                 score="softmax", route_scale=1.0, bias=False),
+    "128-4x32-top2sum-sigmoid": dict(T=99, E=128, K=6, n_group=4, topk_group=2, group_rule="top2_sum",
+                                     score="sigmoid", route_scale=1.0, bias=True),
+    "64-2x32-max-softmax": dict(T=64, E=64, K=4, n_group=2, topk_group=1, group_rule="max",
+                                score="softmax", route_scale=1.0, bias=False),
+    "256-16x16-top2sum-sigmoid": dict(T=77, E=256, K=8, n_group=16, topk_group=5, group_rule="top2_sum",
+                                      score="sigmoid", route_scale=2.5, bias=True),
+    "72-8x9-max-sigmoid": dict(T=50, E=72, K=6, n_group=8, topk_group=3, group_rule="max",
+                               score="sigmoid", route_scale=1.0, bias=True),
+    "8-plain-softmax": dict(T=300, E=8, K=2, n_group=1, topk_group=1, group_rule="top2_sum",
+                            score="softmax", route_scale=1.0, bias=False),
+}
+
+
+@pytest.mark.parametrize("name", list(TIE_CASES))
+def test_route_logits_exact_ties(name):
+    kw = dict(TIE_CASES[name])
+    with_bias = kw.pop("bias")
+    cfg = KS.scaled(**kw)
+    print(f"route_logits exact-tie case {name}", flush=True)
+    rng = np.random.default_rng(len(name))
+    z = torch.from_numpy(rng.choice(np.array([-2.0, -1.0, 0.0, 0.5, 1.0, 2.0], np.float32), (cfg.T, cfg.E)))
+    bias = torch.from_numpy(rng.choice(np.array([0.0, 1.0], np.float32), cfg.E)) if with_bias else None
+    zb = z.double().numpy()
+    bb = None if bias is None else bias.double().numpy()
+    # the inputs are what they should be: every gap between distinct keys (and group scores) is wide
+    keys = orc.score(zb, cfg.score) + (0.0 if bb is None else bb[None, :])
+    if cfg.score == "softmax" and bb is None and cfg.n_group == 1:
+        keys = zb  # plain top-K over softmax ranks the logits
+    def min_nonzero_gap(a):
+        d = np.abs(a[:, :, None] - a[:, None, :])
+        d = d[d > 0]
+        return d.min() if d.size else np.inf  # (all equal: ties only)
+    assert min_nonzero_gap(keys) > 1e-5  # (fp32 rounding of a key is below 3e-7 here)
+    if cfg.n_group > 1:
+        assert min_nonzero_gap(orc.group_scores(keys, cfg.n_group, cfg.group_rule)) > 1e-5
+    ids = torch.empty((cfg.T, cfg.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.K), dtype=torch.float32, device="cuda")
+    B.moe_route_logits(cfg, z.cuda(), None if bias is None else bias.cuda(), ids, w)
+    torch.cuda.synchronize()
+    ids_o, w_o = orc.route(zb, cfg.score, cfg.K, bb, cfg.n_group, cfg.topk_group, cfg.group_rule,
+                           cfg.renorm, cfg.route_scale)
+    np.testing.assert_array_equal(ids.cpu().numpy().astype(np.int64), ids_o)
+    assert np.abs(w.cpu().numpy().astype(np.float64) - w_o).max() <= 1e-5 * cfg.route_scale
+
+
 @pytest.mark.parametrize("E", [256, 72, 1])
 def test_update_bias_bit_exact(E):
     print(f"update_bias E={E}", flush=True)
