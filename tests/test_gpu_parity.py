@@ -108,8 +108,20 @@ def test_large_tile_paths(dtype, gather):
     of the last m-tile: full, <= 128, <= 64, <= 32 rows; fp8 and MX: 128 rows; MX with a single
     K step in Linear-1) with caller-supplied ids; sampled rows of every expert, the last m-tile's
     among them, against the oracle."""
+    _large_tile_check(dtype, gather, 256, 2048)
+
+
+@pytest.mark.parametrize("H,I", [(128, 384), (640, 896)])
+def test_fp8_large_tile_k_step_counts(H, I):
+    """The fp8 128-row kernel at odd and short K step counts (its loop takes two steps at a time):
+    Linear-1 with 1 and 5 steps of 128 channels, Linear-2 with 3 and 7."""
+    _large_tile_check("fp8", True, H, I)
+
+
+def _large_tile_check(dtype, gather, H, I):
+    print(f"large-tile case {dtype} gather={gather} H={H} I={I}", flush=True)
     base = {"bf16": CONFIGS[2], "fp8": CONFIGS[5], "mxfp4": CONFIGS[7]}[dtype]
-    cfg = base.scaled(T=2048, H=256, I=2048, E=8, K=2, score="softmax", renorm=True, route_scale=1.0,
+    cfg = base.scaled(T=2048, H=H, I=I, E=8, K=2, score="softmax", renorm=True, route_scale=1.0,
                       n_group=1, topk_group=1, bias=None, I_shared=0)
     counts = [2000, 800, 500, 300, 220, 150, 90, 36]   # last m-tiles: 208, 32, 244, 44, 220, 150, 90, 36
     case = Case(cfg, gather=gather)
