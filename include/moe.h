@@ -49,13 +49,12 @@ typedef enum moe_status {
 
 /* Arithmetic type of a layer.
  *  MOE_F32      x, W_r, expert weights, y and out are fp32; fp32 accumulation.
- *  MOE_BF16     x, W_r, expert weights, intermediates and out are bf16; fp32 accumulation.
+ *  MOE_BF16     x, W_r, expert weights, intermediates (h, y_perm, y_shared) and out are bf16,
+ *               each rounded once from fp32 accumulators.
  *  MOE_FP8_E4M3 x and W_r are bf16; the library quantises x per token per 128 channels to
  *               e4m3 for the experts; expert weights are e4m3 codes with one fp32 scale per
  *               128x128 block; the SwiGLU output is re-quantised per row per 128 channels;
  *               fp32 accumulation; y_perm, y_shared and out are bf16.
- *  (MOE_BF16 likewise stores y_perm and y_shared as bf16, rounded once from the fp32
- *  accumulators of Linear-2.)
  *  MOE_MXFP4    FP8 activations times FP4 weights ("DeepGEMM质变：从GEMM库到统一LLM计算原语平台",
  *               itsolotime.com, 1.1 and 5.3) in the OCP microscaling formats: x and W_r are
  *               bf16; the library quantises x to MXFP8 (e4m3 codes, one E8M0 scale per 32
