@@ -18,7 +18,7 @@ exceptions are the two fp8 quantisation steps, which decide integer codes;
 those are taken in fp32, the precision the kernels use, so that codes can be
 compared bit for bit.
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings where the pages are silent or garbled:
   * ties in top-K are broken by the lower expert id (groups: lower group id),
     and selected ids are returned in descending key order;
   * the selection bias enters every selection step (group scores included),
