@@ -47,7 +47,7 @@ constexpr int kQueues = 8;
 // Tile-metadata region: tp[0 .. kMaxExperts], then the queue counters of both GEMMs, then the
 // split-tile arrival counters of both GEMMs.
 constexpr int kTileQueueOffset = kMaxExperts + 1;
-constexpr int kMaxSplitItems = 256;  // K-split work items per GEMM launch (32 per XCD range)
+constexpr int kMaxSplitItems = 512;  // K-split work items per GEMM launch (one per workgroup at most)
 constexpr int kSplitCntOffset = kTileQueueOffset + 2 * kQueues;
 static_assert(kSplitCntOffset + 2 * kMaxSplitItems <= kTileMetaInts, "tile metadata region too small");
 constexpr int kPartFloats = 256 * 256;  // one partial 256 x 256 tile
@@ -104,8 +104,10 @@ __device__ __forceinline__ SplitQueue split_queue(int total, int KT, int min_ste
   const int F = R / C, tail = R - F * C;
   int S = 1;
   // Only long K loops are cut: a piece pays a fixed cost (its own prologue, the partial tile
-  // written and read back through L2, the summation), which a short loop does not repay.
-  if (F > 0 && tail > 0 && KT >= 128 && C * kQueues <= kMaxSplitItems) {
+  // written and read back through L2, the summation), which a short loop does not repay. A range
+  // with fewer tiles than workgroups (F = 0: a small launch, e.g. a decode-sized shared expert)
+  // has every tile cut once its K loop has two pieces' worth of steps.
+  if (tail > 0 && C * kQueues <= kMaxSplitItems && (F > 0 ? KT >= 128 : KT >= 2 * min_steps)) {
     S = C / tail;
     if (S > MOE_MAX_K_PIECES) S = MOE_MAX_K_PIECES;
     if (S > KT / min_steps) S = KT / min_steps;

@@ -33,7 +33,7 @@ struct WsLayout {
 
 constexpr int kPermBlock = 256;   // pairs per block in the permutation kernels
 constexpr int kMaxExperts = 256;
-constexpr int kTileMetaInts = 1024;  // tile metadata of the expert GEMMs (prefix, queues, counters)
+constexpr int kTileMetaInts = 2048;  // tile metadata of the expert GEMMs (prefix, queues, counters)
 
 // Validation; returns MOE_OK or the failure status with a reason in *why.
 moe_status check_routing(const moe_config* c, std::string* why);

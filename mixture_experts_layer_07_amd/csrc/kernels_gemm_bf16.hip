@@ -307,7 +307,7 @@ constexpr int kWaitLgkm0Vm8 = wait_lgkm0_vm(8), kWaitLgkm0Vm0 = wait_lgkm0_vm(0)
     bool store = true;                                                                           \
     if (SPLIT && w.piece >= 0) {                                                                 \
       /* K piece: publish it; the last piece to arrive sums all of them in piece order */        \
-      w4::store_partial(g.part + (size_t)w.slot * kPartFloats, acc, tid);                        \
+      w4::store_partial(g.part + (size_t)w.slot * kPartStride, acc, tid);                        \
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                           \
       __syncthreads();                                                                           \
       if (tid == 0) s_slot[0] = atomicAdd(&g.split_cnt[w.first], 1);                             \
@@ -319,7 +319,7 @@ constexpr int kWaitLgkm0Vm8 = wait_lgkm0_vm(8), kWaitLgkm0Vm0 = wait_lgkm0_vm(0)
           _Pragma("unroll") for (int nb = 0; nb < (NB_); ++nb)                                   \
             _Pragma("unroll") for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;                 \
         for (int pc = 0; pc < sq.S; ++pc)                                                        \
-          w4::add_partial(g.part + (size_t)(w.first + pc) * kPartFloats, acc, tid);              \
+          w4::add_partial(g.part + (size_t)(w.first + pc) * kPartStride, acc, tid);              \
       }                                                                                          \
     }                                                                                            \
     if (store) w4::epilogue<MB_, NB_, GLU, OUTF32>(g, ti, acc, r0, c0, lane);                    \
@@ -341,6 +341,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 64;  // K is a multiple of 128: KT is even
   const SplitQueue sq = split_queue(total, KT, 16);
+  constexpr size_t kPartStride = kPartFloats;  // floats per partial tile
 
   for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {
     TileInfo ti = decode_tile(w.tile, tp, g, BM);
@@ -413,19 +414,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_m32(GemmArgs g) {
   __syncthreads();
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 64;  // even
-  const TileQueue tq = tile_queue(total);
-  SplitQueue sq{};
-  sq.S = 1;
-  WorkItem w{};
-  w.piece = -1;
+  // a launch with fewer tiles than workgroups (a decode-sized shared expert) cuts its tiles along
+  // K; a 32 x 256 partial tile is 32 KiB, so the last piece's sum stays cheap
+  const SplitQueue sq = split_queue(total, KT, 16);
+  constexpr size_t kPartStride = 32 * 256;  // floats per partial tile
 
-  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
-    TileInfo ti = decode_tile(t, tp, g, BM);
+  for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {
+    TileInfo ti = decode_tile(w.tile, tp, g, BM);
     ti.e = __builtin_amdgcn_readfirstlane(ti.e);
     ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
     ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
     ti.mvalid = __builtin_amdgcn_readfirstlane(ti.mvalid);
-    const int k0 = 0, k1 = KT;
+    const int k0 = __builtin_amdgcn_readfirstlane(w.k0), k1 = __builtin_amdgcn_readfirstlane(w.k1);
     const int arows = (ti.mvalid + 7) & ~7;
     const uint8_t* Ab = a_base(g, ti);
     const uint8_t* Be = g.B + (size_t)ti.e * g.b_exp;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_m32(GemmArgs g) {
         sA1[i] = z;
       }
     }
-    MOE_W4_TILE(1, 2, 0, wave * 64, false)
+    MOE_W4_TILE(1, 2, 0, wave * 64, true)
   }
 }
 
