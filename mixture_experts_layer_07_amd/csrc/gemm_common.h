@@ -94,7 +94,8 @@ struct SplitQueue {
 // The queue (range) is chosen by the XCD the workgroup runs on, so that every piece of a split
 // tile is computed under one L2. With one workgroup per CU all workgroups are resident and every
 // XCD serves its range.
-__device__ __forceinline__ SplitQueue split_queue(int total, int KT, int min_steps) {
+// max_slots: partial tiles the kernel's workspace region holds (pieces of one launch).
+__device__ __forceinline__ SplitQueue split_queue(int total, int KT, int min_steps, int max_slots) {
   const int q = xcc_id();
   const int per = (total + kQueues - 1) / kQueues;
   const int beg = q * per < total ? q * per : total;
@@ -107,7 +108,8 @@ __device__ __forceinline__ SplitQueue split_queue(int total, int KT, int min_ste
   // written and read back through L2, the summation), which a short loop does not repay. A range
   // with fewer tiles than workgroups (F = 0: a small launch, e.g. a decode-sized shared expert)
   // has every tile cut once its K loop has two pieces' worth of steps.
-  if (tail > 0 && C * kQueues <= kMaxSplitItems && (F > 0 ? KT >= 128 : KT >= 2 * min_steps)) {
+  if (tail > 0 && C * kQueues <= kMaxSplitItems && C * kQueues <= max_slots &&
+      (F > 0 ? KT >= 128 : KT >= 2 * min_steps)) {
     S = C / tail;
     if (S > MOE_MAX_K_PIECES) S = MOE_MAX_K_PIECES;
     if (S > KT / min_steps) S = KT / min_steps;
@@ -162,6 +164,34 @@ __device__ __forceinline__ WorkItem next_item(const GemmArgs& g, const SplitQueu
   w.first = sq.slot0 + tt * sq.S;
   w.slot = w.first + w.piece;
   return w;
+}
+
+// Partial tile of a K piece: a workgroup's NT threads' fp32 accumulators (MB x NB blocks each),
+// thread-major, so that the workgroup summing the pieces reads back the same lanes' values.
+template <int MB, int NB, int NT>
+__device__ __forceinline__ void store_partial_acc(float* part, const f32x16 (&acc)[MB][NB], int tid) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = {acc[mb][nb][4 * c], acc[mb][nb][4 * c + 1], acc[mb][nb][4 * c + 2], acc[mb][nb][4 * c + 3]};
+        reinterpret_cast<f32x4*>(part)[((mb * NB + nb) * 4 + c) * NT + tid] = v;
+      }
+}
+template <int MB, int NB, int NT>
+__device__ __forceinline__ void add_partial_acc(const float* part, f32x16 (&acc)[MB][NB], int tid) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 v = reinterpret_cast<const f32x4*>(part)[((mb * NB + nb) * 4 + c) * NT + tid];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mb][nb][4 * c + e] += v[e];
+      }
 }
 
 struct TileInfo {

@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   __syncthreads();
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 64;  // K is a multiple of 128: KT is even
-  const SplitQueue sq = split_queue(total, KT, 16);
+  const SplitQueue sq = split_queue(total, KT, 16, 256);  // (256 partial tiles of 256 x 256)
   constexpr size_t kPartStride = kPartFloats;  // floats per partial tile
 
   for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_m32(GemmArgs g) {
   const int KT = g.K / 64;  // even
   // a launch with fewer tiles than workgroups (a decode-sized shared expert) cuts its tiles along
   // K; a 32 x 256 partial tile is 32 KiB, so the last piece's sum stays cheap
-  const SplitQueue sq = split_queue(total, KT, 16);
+  const SplitQueue sq = split_queue(total, KT, 16, 512);  // (512 partial tiles of 32 x 256)
   constexpr size_t kPartStride = 32 * 256;  // floats per partial tile
 
   for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {

@@ -142,14 +142,19 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
   const int KT = g.K / 256;
   const int lrow = lane & 31, h = lane >> 5;
   __shared__ int s_slot[1];
-  const TileQueue tq = tile_queue(total);
+  // 32-row tiles: a launch with fewer tiles than workgroups (a decode-sized shared expert) cuts
+  // its tiles along K into pieces of >= 7 steps (1792 channels; shorter loops are not repaid),
+  // summed in piece order by the last piece to arrive
+  constexpr bool kSplit = BM == 32;
+  const SplitQueue sq = split_queue(total, KT, kSplit ? 7 : (1 << 20), 512);  // (512 partial tiles of 32 x 256)
   const uint32_t* a_sc = reinterpret_cast<const uint32_t*>(g.a_scale);
   const uint32_t* b_sc = reinterpret_cast<const uint32_t*>(g.b_scale);
   const size_t a_sld = (size_t)g.a_scale_ld;  // rows of the activation scale array
   const size_t b_sld = (size_t)g.b_scale_ld;  // rows of one expert's weight scale array
 
-  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
-    TileInfo ti = decode_tile(t, tp, g, BM);
+  for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {
+    TileInfo ti = decode_tile(w.tile, tp, g, BM);
+    const int k0 = __builtin_amdgcn_readfirstlane(w.k0), k1 = __builtin_amdgcn_readfirstlane(w.k1);
     ti.e = __builtin_amdgcn_readfirstlane(ti.e);
     ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
     ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
 // scale words of step kt (clamped into the loop) into SA / SB, pre-shifted for the lane half
 #define MOE_MX_SLOAD(SA, SB, kt)                                                                    \
   do {                                                                                              \
-    const size_t kg_ = (size_t)(2 * ((kt) < KT ? (kt) : KT - 1));                                   \
+    const size_t kg_ = (size_t)(2 * ((kt) < k1 ? (kt) : k1 - 1));                                   \
     _Pragma("unroll") for (int g_ = 0; g_ < 2; ++g_) {                                              \
       const uint32_t* pa_ = a_sc + (kg_ + g_) * a_sld;                                              \
       const uint32_t* pb_ = bsc_e + (kg_ + g_) * b_sld;                                             \
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
 #define MOE_MX_AISSUE(kt, sta) MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt) * 256u, sta, wave)
 #define MOE_MX_BLOAD(R, kt)                                                                         \
   do {                                                                                              \
-    const uint32_t ko_ = (uint32_t)((kt) < KT ? (kt) : KT - 1) * 128u;                              \
+    const uint32_t ko_ = (uint32_t)((kt) < k1 ? (kt) : k1 - 1) * 128u;                              \
     _Pragma("unroll") for (int j_ = 0; j_ < BJ; ++j_) {                                             \
       uint32_t o_ = ob[j_];                                                                         \
       asm volatile("" : "+v"(o_));                                                                  \
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
 #define MOE_MX_STEP(kt, ca, cb, na, nb_, RW, SA, SB, SAN, SBN)                                      \
   {                                                                                                 \
     MOE_MX_SLOAD(SAN, SBN, (kt) + 1);                                                               \
-    if ((kt) + 1 < KT) {                                                                            \
+    if ((kt) + 1 < k1) {                                                                            \
       MOE_MX_BWRITE(nb_, RW);                                                                       \
       MOE_MX_AISSUE((kt) + 1, na);                                                                  \
     }                                                                                               \
@@ -245,25 +250,26 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
     __builtin_amdgcn_s_barrier();                                                                   \
     MOE_MX_SSHIFT(SAN, SBN);                                                                        \
   }
-    // prologue: step 0 straight into the first stage, the weights of steps 1 and 2 in registers
-    MOE_MX_SLOAD(saA, sbA, 0);
-    MOE_MX_AISSUE(0, sA0);
+    // prologue: step k0 straight into the first stage, the weights of steps k0+1 and k0+2 in
+    // registers
+    MOE_MX_SLOAD(saA, sbA, k0);
+    MOE_MX_AISSUE(k0, sA0);
 #pragma unroll
-    for (int j = 0; j < BJ; ++j) dma_to_lds<16>(Be + ob[j], sB0 + (j * NW + wave) * 64);
+    for (int j = 0; j < BJ; ++j) dma_to_lds<16>(Be + (ob[j] + (uint32_t)k0 * 128u), sB0 + (j * NW + wave) * 64);
     __builtin_amdgcn_sched_barrier(0);
-    MOE_MX_BLOAD(RB1, 1);
-    MOE_MX_BLOAD(RB0, 2);
+    MOE_MX_BLOAD(RB1, k0 + 1);
+    MOE_MX_BLOAD(RB0, k0 + 2);
     // step 0 and the weights of step 1 landed: the loop's steady state, only the newest weight
     // loads outstanding
     __builtin_amdgcn_s_waitcnt(f8_wait_lgkm0_vm(BJ));
     __builtin_amdgcn_s_barrier();
     MOE_MX_SSHIFT(saA, sbA);
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
+    int kt = k0;
+    for (; kt + 1 < k1; kt += 2) {
       MOE_MX_STEP(kt, sA0, sB0, sA1, sB1, RB1, saA, sbA, saB, sbB)
       MOE_MX_STEP(kt + 1, sA1, sB1, sA0, sB0, RB0, saB, sbB, saA, sbA)
     }
-    if (kt < KT) {  // odd step count: the last step sits in the first stage
+    if (kt < k1) {  // odd step count: the last step sits in the first stage
       MOE_MX_STEP(kt, sA0, sB0, sA1, sB1, RB1, saA, sbA, saB, sbB)
     }
 #undef MOE_MX_SLOAD
@@ -273,6 +279,28 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
 #undef MOE_MX_BWRITE
 #undef MOE_MX_STEP
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bool store = true;
+    if (kSplit && w.piece >= 0) {
+      // K piece: publish it; the last piece to arrive sums all of them in piece order
+      constexpr size_t kPart = (size_t)MB * NB * 16 * NT;
+      store_partial_acc<MB, NB, NT>(g.part + (size_t)w.slot * kPart, acc, tid);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) s_slot[0] = atomicAdd(&g.split_cnt[w.first], 1);
+      __syncthreads();
+      store = __builtin_amdgcn_readfirstlane(s_slot[0]) == sq.S - 1;
+      __syncthreads();
+      if (store) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+        for (int pc = 0; pc < sq.S; ++pc) add_partial_acc<MB, NB, NT>(g.part + (size_t)(w.first + pc) * kPart, acc, tid);
+      }
+    }
+    if (!store) continue;
     if (GLU) {
       // h for this wave's 32 columns (one MX block per row)
       uint8_t* sb = reinterpret_cast<uint8_t*>(g.c_scale) + ((size_t)ti.nt * g.c_scale_ld + ti.row0) * 4 + wn;

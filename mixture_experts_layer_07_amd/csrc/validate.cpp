@@ -101,10 +101,11 @@ WsLayout layout(const moe_config& c) {
   off = align256(off + (size_t)L.perm_blocks * E * 4);
   L.tiles = off;
   off = align256(off + (size_t)kTileMetaInts * 4);
-  // partial tiles of K-split bf16 GEMM tiles (64 MiB): up to 256 of 256 x 256 fp32 (256-row
-  // tiles) or 512 of 32 x 256 (32-row tiles)
+  // partial tiles of K-split GEMM tiles: bf16 up to 256 of 256 x 256 fp32 (256-row tiles) or 512
+  // of 32 x 256 (32-row tiles), 64 MiB; MX up to 512 of 32 x 256, 16 MiB
   L.part = off;
-  off = align256(off + (c.dtype == MOE_BF16 ? (size_t)256 * 256 * 256 * 4 : 0));
+  off = align256(off + (c.dtype == MOE_BF16 ? (size_t)256 * 256 * 256 * 4
+                                            : (c.dtype == MOE_MXFP4 ? (size_t)512 * 32 * 256 * 4 : 0)));
   const size_t elem = c.dtype == MOE_F32 ? 4 : (c.dtype == MOE_BF16 ? 2 : 1);
   L.h = off;
   off = align256(off + P * maxI * elem);
