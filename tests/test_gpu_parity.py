@@ -38,6 +38,10 @@ SMALL = {
     # and 32-row tiles with an even one
     "dsv3-mxfp4": (CONFIGS[7].scaled(T=260, H=768, I=2048, E=32, K=8, I_shared=2048), None),
     "decode-mxfp4": (CONFIGS[7].scaled(T=24, H=512, I=2048, E=64, K=8, I_shared=2048), None),
+    # the shared expert's launch has fewer tiles than workgroups and a K loop long enough to be cut
+    # into pieces (bf16: 32 steps of 64 channels; MX: 14 steps of 256)
+    "decode-bf16-ksplit": (CONFIGS[4].scaled(T=24, H=2048, I=256, E=64, K=8, bias="normal", I_shared=256), "zipf"),
+    "decode-mxfp4-ksplit": (CONFIGS[7].scaled(T=24, H=3584, I=512, E=64, K=8, I_shared=512), None),
 }
 
 
