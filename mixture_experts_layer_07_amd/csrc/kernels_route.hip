@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256, 1) void k_router_bf16(const uint8_t* __restric
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wave / NWE, we = wave % NWE;
   const int t0 = blockIdx.x * TM;
+  const int e0 = blockIdx.z * TE;  // (a small batch spreads the experts over workgroups)
   const int nk = H / 128, sp = blockIdx.y;
   const int kc0 = (int)((long long)sp * nk / splits) * 128;
   const int kc1 = (int)((long long)(sp + 1) * nk / splits) * 128;
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(256, 1) void k_router_bf16(const uint8_t* __restric
 #pragma unroll
   for (int j = 0; j < BJ; ++j) {
     const int r = dma_row<NW>(j, wave, lane);
-    const int e = r < E ? r : E - 1;
+    const int e = e0 + r < E ? e0 + r : E - 1;
     db.off[j] = (uint32_t)e * (uint32_t)H * 2u + (uint32_t)dma_chunk(r, lane) * 16u;
   }
   f32x16 acc[MB][NB];
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256, 1) void k_router_bf16(const uint8_t* __restric
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int e = we * NB * 32 + nb * 32 + lrow;
+      const int e = e0 + we * NB * 32 + nb * 32 + lrow;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int t = t0 + wt * MB * 32 + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3);
@@ -180,7 +181,12 @@ hipError_t launch_router_bf16(const void* x, const void* wrt, float* logits, int
   const uint8_t* xi = static_cast<const uint8_t*>(x);
   const uint8_t* wi = static_cast<const uint8_t*>(wrt);
   return timed_launch("router_bf16", s, [&] {
-    if (E <= 32)
+    // a small batch (few token tiles even after the K splits) also spreads the experts: tiles of
+    // 64 experts, one per grid z
+    if (E > 64 && (int)(grid.x * grid.y) < 128)
+      hipLaunchKernelGGL((k_router_bf16<4, 1, 1, 2>), dim3(grid.x, grid.y, (E + 63) / 64), dim3(256), 0, s, xi, wi,
+                         logits, T, H, E, splits);
+    else if (E <= 32)
       hipLaunchKernelGGL((k_router_bf16<4, 1, 1, 1>), grid, dim3(256), 0, s, xi, wi, logits, T, H, E, splits);
     else if (E <= 64)
       hipLaunchKernelGGL((k_router_bf16<4, 1, 1, 2>), grid, dim3(256), 0, s, xi, wi, logits, T, H, E, splits);
