@@ -28,7 +28,8 @@ __device__ __forceinline__ void load_row_chunk(const uint8_t* row, int ch, float
     }
   } else {
     static_assert(EPC == 8, "bf16 rows are read 8 channels at a time");
-    const uint4 u = reinterpret_cast<const uint4*>(row)[ch];
+    // (each row chunk is read once: a non-temporal load does not keep it in the caches)
+    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + ch);
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

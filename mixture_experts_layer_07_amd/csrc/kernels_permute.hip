@@ -170,11 +170,13 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ sort
     // each lane keeps several 16-byte reads in flight instead of one
     constexpr int kBatch = 8;
     for (int g0 = 0; g0 < nblk; g0 += 4 * kBatch) {
-      uint4 raw[kBatch];
+      // (each row is read once here: non-temporal loads do not keep it in the caches)
+      u32x4 raw[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int b = g0 + 4 * u + (lane >> 4);
-        raw[u] = b < nblk ? reinterpret_cast<const uint4*>(in)[(size_t)b * 16 + (lane & 15)] : make_uint4(0, 0, 0, 0);
+        raw[u] = b < nblk ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(in) + ((size_t)b * 16 + (lane & 15)))
+                          : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
