@@ -189,10 +189,15 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
   int32_t* hist = at<int32_t>(ws, L.hist);
   int32_t* base = at<int32_t>(ws, L.base);
   int32_t* err = at<int32_t>(ws, L.err);
-  MOE_HIP(launch_perm_hist(topk_ids, P, c.E, hist, err, s), "perm_hist");
-  MOE_HIP(launch_perm_scan(hist, L.perm_blocks, c.E, base, counts, s), "perm_scan");
-  MOE_HIP(launch_perm_scatter(topk_ids, P, c.E, base, counts, offsets, sorted_pair, pair_pos, s),
-          "perm_scatter");
+  if (P <= kSmallPermPairs) {
+    MOE_HIP(launch_perm_small(topk_ids, P, c.E, counts, offsets, sorted_pair, pair_pos, err, s),
+            "perm_small");
+  } else {
+    MOE_HIP(launch_perm_hist(topk_ids, P, c.E, hist, err, s), "perm_hist");
+    MOE_HIP(launch_perm_scan(hist, L.perm_blocks, c.E, base, counts, s), "perm_scan");
+    MOE_HIP(launch_perm_scatter(topk_ids, P, c.E, base, counts, offsets, sorted_pair, pair_pos, s),
+            "perm_scatter");
+  }
   if (x) MOE_HIP(launch_gather(c, sorted_pair, x, x_perm, x_perm_scale, s), "gather");
   return MOE_OK;
 }

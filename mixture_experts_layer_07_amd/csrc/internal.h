@@ -32,6 +32,7 @@ struct WsLayout {
 };
 
 constexpr int kPermBlock = 256;   // pairs per block in the permutation kernels
+constexpr int kSmallPermPairs = 4096;  // up to this many pairs: one-workgroup permutation
 constexpr int kMaxExperts = 256;
 constexpr int kTileMetaInts = 2048;  // tile metadata of the expert GEMMs (prefix, queues, counters)
 
@@ -85,6 +86,8 @@ hipError_t launch_topk(const moe_config& c, const float* logits, int splits, con
 // permute
 hipError_t launch_update_bias(const int32_t* counts, int E, float* bias, float gamma, hipStream_t s);
 hipError_t launch_clear_words(int32_t* p, int n, hipStream_t s);
+hipError_t launch_perm_small(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos, int32_t* err, hipStream_t s);
 hipError_t launch_perm_hist(const int32_t* ids, int P, int E, int32_t* hist, int32_t* err,
                             hipStream_t s);
 hipError_t launch_perm_scan(const int32_t* hist, int nblk, int E, int32_t* base, int32_t* counts,

@@ -138,6 +138,99 @@ hipError_t launch_perm_scatter(const int32_t* ids, int P, int E, const int32_t* 
   });
 }
 
+// Small batches (P <= kSmallPermPairs, e.g. decode): the same stable counting sort in one
+// workgroup and one launch instead of three. The pairs are taken as P/64 groups of 64 in order
+// ("virtual waves"); pass 1 stores each group's count of every expert, a per-expert exclusive
+// prefix over the groups turns them into the group's base within the expert, and pass 2 places
+// each pair at offsets[e] + its group's base + its rank among the equal ids of its group (the same
+// ballots as k_perm_scatter). Results are identical to the three-pass kernels.
+__global__ __launch_bounds__(256) void k_perm_small(const int32_t* __restrict__ ids, int P, int E,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ sorted_pair,
+                                                    int32_t* __restrict__ pair_pos,
+                                                    int32_t* __restrict__ err) {
+  __shared__ uint16_t gcnt[kSmallPermPairs / 64][kMaxExperts];  // counts, then bases (<= 4096)
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int sbuf[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ngroups = (P + 63) / 64;
+  for (int i = tid; i < ngroups * kMaxExperts; i += 256) (&gcnt[0][0])[i] = 0;
+  __syncthreads();
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // all of this thread's ids are loaded at once (independent loads, one round trip) and kept
+  constexpr int kChunks = kSmallPermPairs / 256;
+  int ev[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int p = c * 256 + tid;
+    ev[c] = p < P ? ids[p] : -1;
+  }
+  // validity and equal-id lane mask of the pair in chunk c (called by whole waves)
+  auto classify = [&](int c, bool& ok, unsigned long long& mask) {
+    const int e = ev[c];
+    ok = c * 256 + tid < P && e >= 0 && e < E;
+    mask = __ballot(ok);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool set = ok && ((e >> bit) & 1);
+      const unsigned long long b = __ballot(set);
+      mask &= set ? b : ~b;
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    if (c * 256 >= P) break;
+    bool ok;
+    unsigned long long mask;
+    classify(c, ok, mask);
+    if (c * 256 + tid < P && !ok) atomicOr(err, 1);
+    if (ok && __popcll(mask & lt) == 0) gcnt[c * 4 + wave][ev[c]] = (uint16_t)__popcll(mask);
+  }
+  __syncthreads();
+  int total = 0;
+  if (tid < E) {
+    for (int gi = 0; gi < ngroups; ++gi) {
+      const int t = gcnt[gi][tid];
+      gcnt[gi][tid] = (uint16_t)total;
+      total += t;
+    }
+    counts[tid] = total;
+  }
+  {
+    int tot;
+    const int ex = block_exscan_256(tid < E ? total : 0, sbuf, &tot);
+    if (tid < E) off[tid] = offsets[tid] = ex;
+    if (tid == 0) off[E] = offsets[E] = tot;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    if (c * 256 >= P) break;
+    const int p = c * 256 + tid;
+    bool ok;
+    unsigned long long mask;
+    classify(c, ok, mask);
+    if (ok) {
+      const int e = ev[c];
+      const int pos = off[e] + gcnt[c * 4 + wave][e] + __popcll(mask & lt);
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+    } else if (p < P) {
+      pair_pos[p] = -1;
+    }
+  }
+}
+
+hipError_t launch_perm_small(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos, int32_t* err, hipStream_t s) {
+  if (P > kSmallPermPairs || E > kMaxExperts) return hipErrorInvalidValue;
+  return timed_launch("perm_small", s, [&] {
+    hipLaunchKernelGGL(k_perm_small, dim3(1), dim3(256), 0, s, ids, P, E, counts, offsets,
+                       sorted_pair, pair_pos, err);
+  });
+}
+
 // ------------------------------------------------------------------ gather / fp8 and MX quantise
 // One wave per destination row. bf16 / fp32: 16-byte copies. fp8: the bf16 row is read in
 // 128-channel blocks (16 lanes x 8 channels), the block absmax is reduced over its 16 lanes,

@@ -74,9 +74,11 @@ def test_single_token_and_all_experts():
         full_check(Case(cfg))
 
 
-def test_permute_skewed_ids_and_ragged_experts():
-    # caller-supplied ids: expert 3 gets every token (2 m-tiles of 256 plus a tail), most experts none
-    cfg = CONFIGS[2].scaled(T=300, H=256, I=256, E=16, K=2)
+# P = T*K up to 4096 takes the one-workgroup permutation, above it the three-pass one
+@pytest.mark.parametrize("T", [300, 2100], ids=["one-workgroup", "three-pass"])
+def test_permute_skewed_ids_and_ragged_experts(T):
+    # caller-supplied ids: expert 3 gets every token (m-tiles of 256 plus a tail), most experts none
+    cfg = CONFIGS[2].scaled(T=T, H=256, I=256, E=16, K=2)
     case = Case(cfg)
     L = case.layer
     t = torch.arange(cfg.T)
@@ -89,6 +91,26 @@ def test_permute_skewed_ids_and_ragged_experts():
     assert (L.offsets.cpu().numpy() == offsets).all()
     assert (L.sorted_pair.cpu().numpy() == sp).all() and (L.pair_pos.cpu().numpy() == pp).all()
     check_ffn(case, offsets, np.arange(cfg.P), {})
+    assert B.moe_get_device_error(L.ws) == 0
+
+
+@pytest.mark.parametrize("T", [2048, 2049], ids=["P4096", "P4098"])
+def test_permute_at_the_path_boundary(T):
+    # both permutation paths against the oracle on 256 experts with Zipf-skewed ids
+    cfg = CONFIGS[2].scaled(T=T, H=256, I=128, E=256, K=2)
+    case = Case(cfg)
+    L = case.layer
+    rng = np.random.default_rng(T)
+    w = 1.0 / np.arange(1, cfg.E + 1)
+    first = rng.choice(cfg.E, size=T, p=w / w.sum())
+    second = (first + 1 + rng.integers(0, cfg.E - 1, size=T)) % cfg.E
+    ids = torch.from_numpy(np.stack([first, second], 1).astype(np.int32))
+    L.topk_ids.copy_(ids)
+    L.permute(case.xd)
+    torch.cuda.synchronize()
+    counts, offsets, sp, pp = orc.permute(ids.numpy(), cfg.E)
+    assert (L.counts.cpu().numpy() == counts).all() and (L.offsets.cpu().numpy() == offsets).all()
+    assert (L.sorted_pair.cpu().numpy() == sp).all() and (L.pair_pos.cpu().numpy() == pp).all()
     assert B.moe_get_device_error(L.ws) == 0
 
 
@@ -150,8 +172,9 @@ def _large_tile_check(dtype, gather, H, I):
     print(dtype, rep)
 
 
-def test_out_of_range_ids_set_the_device_error():
-    cfg = CONFIGS[2].scaled(T=64, H=256, I=128, E=8, K=2)
+@pytest.mark.parametrize("T", [64, 2100], ids=["one-workgroup", "three-pass"])
+def test_out_of_range_ids_set_the_device_error(T):
+    cfg = CONFIGS[2].scaled(T=T, H=256, I=128, E=8, K=2)
     case = Case(cfg)
     L = case.layer
     ids = torch.randint(0, 8, (cfg.T, cfg.K), dtype=torch.int32)
