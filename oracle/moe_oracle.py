@@ -58,6 +58,13 @@ transposed operand fails at least one of them:
     against exhaustive nearest-value search and torch's float8_e4m3fn;
   * quantize_rows_fp8: exactly representable rows round-trip, zero blocks,
     saturation and the per-block scale definition.
+  * the fp8 layer path (moe_layer(fp8=True), swiglu_expert(fp8_hidden=True),
+    dequantize_weight_blocks): on activations and weights that e4m3 holds exactly
+    at power-of-two block scales, the layer equals an fp64 layer written out in the
+    test (weights decoded block by block, the SwiGLU output re-quantised per row per
+    128 channels by a table search), and differs from the same layer without the
+    re-quantisation; the hidden re-quantisation moves an expert output by at most
+    |W2| times half an e4m3 ulp of each hidden value, with per-row block scales.
   * MX codecs: all 16 e2m1 codes against the format's value table, all 256 E8M0
     codes against torch's float8_e8m0fnu; the scale exponent at binade edges;
     quantize_rows_mx: exactly representable blocks round-trip (so a wrong emax,

@@ -332,16 +332,144 @@ def test_weight_block_dequant_orientation():
     assert (w[:128] == 2.0).all() and (w[128:] == 3.0).all()
 
 
-def test_fp8_layer_path_matches_exactly_representable_fp32():
-    # x and weights exactly representable in e4m3 at power-of-two scales: the fp8
-    # quantisation of x is lossless, so only the hidden re-quantisation differs.
-    T, H, I = 4, 128, 128
+def _e4m3_value(code):
+    """e4m3 "fn" value written out from the format's fields (bias 7, subnormals below exponent 1),
+    independently of the oracle's codec table."""
+    code = int(code)
+    sign = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    return sign * (m / 8.0 * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7))
+
+
+def _representable_fp8_rows(rng, T, C, exps):
+    """Rows that the per-row per-128-channel quantiser maps onto themselves: every 128-block is
+    e4m3 codes times 2^exps[t, b] with one element at code 0x7E (448), so absmax / 448 = 2^exps
+    exactly and every value divided by it is its own code."""
+    codes = rng.integers(0, 0x7E, size=(T, C)).astype(np.uint8)
+    codes |= (rng.integers(0, 2, size=(T, C)) << 7).astype(np.uint8)
+    codes[:, ::128] = 0x7E
+    vals = np.vectorize(_e4m3_value)(codes)
+    return vals * np.repeat(2.0 ** np.asarray(exps, np.float64), 128, axis=1)
+
+
+def _hand_blocks(codes, scales):
+    """A weight matrix [N,K] from e4m3 codes and one scale per 128 x 128 block, written as an
+    explicit loop over the blocks: block (i, j) covers output rows 128i.. and input channels 128j.."""
+    vals = np.vectorize(_e4m3_value)(codes)
+    out = np.empty_like(vals)
+    for i in range(codes.shape[0] // 128):
+        for j in range(codes.shape[1] // 128):
+            out[128 * i:128 * i + 128, 128 * j:128 * j + 128] = (
+                vals[128 * i:128 * i + 128, 128 * j:128 * j + 128] * scales[i, j])
+    return out
+
+
+def _requant_rows_by_hand(h):
+    """Per row, per 128 consecutive channels: scale = absmax / 448 (fp32), value -> the nearest
+    e4m3 value of h / scale (ties to the even code), times the scale. Written with a sorted table
+    of every finite non-negative e4m3 value, independently of quantize_rows_fp8."""
+    table = np.array(sorted({_e4m3_value(c) for c in range(0x7F)}))
+    h32 = np.asarray(h, np.float32)
+    out = np.empty(h32.shape, np.float64)
+    for r in range(h32.shape[0]):
+        for b in range(h32.shape[1] // 128):
+            blk = h32[r, 128 * b:128 * b + 128]
+            s = np.float32(np.abs(blk).max()) / np.float32(448.0)
+            if s == 0:
+                out[r, 128 * b:128 * b + 128] = 0.0
+                continue
+            for j, v in enumerate(blk):
+                a = min(abs(float(np.float32(v) / s)), 448.0)
+                i = int(np.searchsorted(table, a))
+                cand = [table[i]] if i == 0 or (i < table.size and table[i] == a) else \
+                    [table[i - 1]] + ([table[i]] if i < table.size else [])
+                if len(cand) == 2:
+                    d0, d1 = a - cand[0], cand[1] - a
+                    # ties to the even code: the codes of consecutive table entries alternate parity
+                    pick = cand[0] if d0 < d1 or (d0 == d1 and (i - 1) % 2 == 0) else cand[1]
+                else:
+                    pick = cand[0]
+                out[r, 128 * b + j] = math.copysign(pick, v) * float(s)
+    return out
+
+
+def test_fp8_layer_path_on_representable_inputs():
+    # Activations and weights that e4m3 holds exactly (power-of-two block scales): the layer's
+    # per-token per-128-channel quantisation of x is lossless and the weights decode to known
+    # values, so moe_layer(fp8=True) must equal the fp64 layer on those values whose SwiGLU output
+    # is re-quantised per row per 128 channels, and nothing else. Dropping the re-quantisation,
+    # quantising h per column, or reading the weight block scales transposed fails here.
     rng = np.random.default_rng(10)
-    x = orc.e4m3_decode_array(rng.integers(0, 0x70, size=(T, H)).astype(np.uint8))
-    x[:, 0] = 448.0
+    T, H, I, E, K, Is = 6, 256, 256, 4, 2, 256
+    x = _representable_fp8_rows(rng, T, H, rng.integers(-7, -3, size=(T, H // 128)))
     q, s = orc.quantize_rows_fp8(x)
     np.testing.assert_array_equal(orc.dequantize_rows_fp8(q, s), x)
+    w_r = rng.normal(size=(H, E))
 
+    def weights(n, k):
+        codes = rng.integers(0, 0x7F, size=(n, k)).astype(np.uint8) | (rng.integers(0, 2, (n, k)) << 7).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x30                  # no NaN codes
+        # distinct power-of-two scales per block, none symmetric under transposition
+        scales = (2.0 ** -rng.permutation(np.arange(13, 13 + (n // 128) * (k // 128)))).reshape(n // 128, k // 128)
+        return codes, scales.astype(np.float32)
+
+    raw = [(weights(2 * I, H), weights(H, I)) for _ in range(E + 1)]
+    dec = [(orc.dequantize_weight_blocks(*a), orc.dequantize_weight_blocks(*b)) for a, b in raw]
+    hand = [(_hand_blocks(*a), _hand_blocks(*b)) for a, b in raw]
+    for (d13, d2), (h13, h2) in zip(dec, hand):
+        np.testing.assert_array_equal(d13, h13)
+        np.testing.assert_array_equal(d2, h2)
+    out, ids, wts = orc.moe_layer(x, w_r, lambda e: dec[e], "softmax", K, E, fp8=True,
+                                  get_shared=lambda: dec[E])
+
+    def expert_by_hand(xr, e):
+        w13, w2 = hand[e]
+        g, u = xr @ w13[:I].T, xr @ w13[I:].T
+        h = g / (1.0 + np.exp(-g)) * u
+        return _requant_rows_by_hand(h) @ w2.T, h @ w2.T
+
+    ref = np.zeros((T, H))
+    plain = np.zeros((T, H))
+    for t in range(T):
+        for k in range(K):
+            y, yp = expert_by_hand(x[t:t + 1], ids[t, k])
+            ref[t] += wts[t, k] * y[0]
+            plain[t] += wts[t, k] * yp[0]
+    ys, yps = expert_by_hand(x, E)
+    ref += ys
+    plain += yps
+    tol = 1e-12 * np.abs(ref).max()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=tol)
+    # the re-quantisation is on the path: without it the layer is measurably different
+    assert np.abs(plain - ref).max() > 1e3 * tol
+
+
+def test_fp8_hidden_requantisation_bound():
+    # with fp8_hidden the expert output moves by at most |W2| times the bound of one e4m3 rounding
+    # of each hidden value (half an ulp: 2^-4 of the value in the normal range, 2^-10 of the
+    # block scale in the subnormal range), and it does move
+    rng = np.random.default_rng(25)
+    M, H, I = 6, 128, 256
+    x = rng.normal(size=(M, H))
+    w13 = rng.normal(size=(2 * I, H)) / 8
+    w2 = rng.normal(size=(H, I)) / 10
+    w13[:, :5] *= 0.0                                           # (rows stay generic)
+    y = orc.swiglu_expert(x, w13, w2)
+    y8 = orc.swiglu_expert(x, w13, w2, fp8_hidden=True)
+    h = orc.swiglu_hidden(x, w13)
+    _, s = orc.quantize_rows_fp8(h)
+    sc = np.repeat(s.astype(np.float64), 128, 1)
+    bound = np.maximum(np.abs(h) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 2.0 ** -20) + np.abs(h) * 2.0 ** -23
+    assert (np.abs(y8 - y) <= bound @ np.abs(w2).T * (1 + 1e-9) + 1e-12).all()
+    assert np.abs(y8 - y).max() > 0
+    # the per-row block scale: each row's h blocks are scaled independently (a per-column or
+    # per-tensor scale would give other values on these rows, whose ranges differ by 2^6)
+    x2 = np.vstack([x[:1], x[:1] * 8.0])
+    h2 = orc.swiglu_hidden(x2, w13)
+    q2, s2 = orc.quantize_rows_fp8(h2)
+    np.testing.assert_allclose(orc.swiglu_expert(x2, w13, w2, fp8_hidden=True),
+                               orc.dequantize_rows_fp8(q2, s2) @ w2.T, rtol=0, atol=1e-13)
+    assert s2[1, 0] > 32 * s2[0, 0]
 
 
 # ------------------------------------------------------------------ MX (fp8 x fp4) codecs
