@@ -1,10 +1,11 @@
 """Benchmark of the MoE layer forward on one MI355X.
 
 One step = one whole layer forward (route -> permute -> expert FFN (+ shared expert) -> combine)
-over one batch of synthetic inputs already resident in HBM. Default workload: the Mixtral-shaped
-layer (T=4096, H=4096, I=14336, E=8, K=2, bf16). Prints one JSON line.
+over one batch of synthetic inputs already resident in HBM. Default workload: the DeepSeek-V3-shaped
+layer (T=8192, H=7168, I=2048, E=256, K=8, grouped sigmoid routing, one shared expert, bf16), the
+largest layer of the set that one GPU holds. Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 25] [--config 2] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 25] [--config 3] [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -21,6 +22,7 @@ PEAK = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 5000.0, "f32": 157.3}
 DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3", "mxfp4": "mxfp8_e4m3 x mxfp4_e2m1"}
 QUANT = ("fp8", "mxfp4")
 HBM_PEAK = 8000.0                                       # GB/s
+SMALL_PERM_PAIRS = 4096   # up to this many pairs the permutation is one one-workgroup launch
 
 
 def parse():
@@ -29,7 +31,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     # (the shader clock settles over the first ~40 ms of back-to-back layers: warm-up covers that)
     p.add_argument("--warmup", type=int, default=25)
-    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--config", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--x-perm", action="store_true",
                    help="time the path that writes the permuted activations x_perm instead of "
@@ -53,7 +55,7 @@ def kernel_work(cfg, active, gather=True):
     T, H, I, E, K, P, Is = cfg.T, cfg.H, cfg.I, cfg.E, cfg.K, cfg.P, cfg.I_shared
     fp8, mx = cfg.dtype == "fp8", cfg.dtype == "mxfp4"
     q = fp8 or mx
-    xb = 4 if cfg.dtype == "f32" else 2          # x and out
+    xb = 4 if cfg.dtype == "f32" else 2          # x
     ab = 1 if q else xb                          # activation operand bytes (x_perm, h)
     wb = 0.5 if mx else ab                       # weight bytes per element (MX: two e2m1 per byte)
     yb = 4 if cfg.dtype == "f32" else 2          # y rows: fp32 (f32 layer), bf16 (the others)
@@ -81,9 +83,12 @@ def kernel_work(cfg, active, gather=True):
         T * H * rb + H * E * rb + T * E * 4)
     add("route/router_transpose", 0.0, 2.0 * H * E * 2)
     add("route/topk", 0.0, T * E * 4 + T * K * 8 + (E * 4 if cfg.bias else 0))
-    add("permute/perm_hist", 0.0, P * 4 + E * 4)
-    add("permute/perm_scan", 0.0, E * 8)
-    add("permute/perm_scatter", 0.0, P * 4 + P * 8)
+    if P <= SMALL_PERM_PAIRS:   # one workgroup: ids in, counts / offsets and the two orders out
+        add("permute/perm_small", 0.0, P * 4 + E * 4 + (E + 1) * 4 + P * 8)
+    else:
+        add("permute/perm_hist", 0.0, P * 4 + E * 4)
+        add("permute/perm_scan", 0.0, E * 8)
+        add("permute/perm_scatter", 0.0, P * 4 + P * 8)
     if gather:
         if q:
             add(f"permute/quantize_{qn}", 0.0, T * H * 2 + T * H * (1 + sc))
@@ -99,8 +104,9 @@ def kernel_work(cfg, active, gather=True):
             add(f"shared/quantize_{qn}", 0.0, T * H * 2 + T * H * (1 + sc))
         add("shared/build_tiles", 0.0, 8)
         ffn("shared/", T, 1, Is, T)
-    cname = "combine_f32" if cfg.dtype == "f32" else "combine_bf16"
-    add("combine/" + cname, 0.0, P * 4 + T * K * 4 + P * H * yb + (T * H * yb if Is else 0) + T * H * xb)
+    ob = 4 if cfg.out == "f32" else 2           # layer output
+    cname = "combine_f32" if cfg.dtype == "f32" else ("combine_bf16_f32out" if cfg.out == "f32" else "combine_bf16")
+    add("combine/" + cname, 0.0, P * 4 + T * K * 4 + P * H * yb + (T * H * yb if Is else 0) + T * H * ob)
     return w
 
 
@@ -204,6 +210,9 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": by / n_launch / avg_s / 1e9,
                 "peak": HBM_PEAK, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # both roofs of the dominant kernel, whichever binds
+    roof["frac_mfma"] = fl / n_launch / avg_s / 1e12 / PEAK[dtype] if fl else 0.0
+    roof["frac_hbm"] = by / n_launch / avg_s / 1e9 / HBM_PEAK
     roof["traffic"] = measured_traffic(cfg.name, dom)
     roof["algorithmic_per_launch"] = {"flops": fl / n_launch, "bytes": by / n_launch}
 
@@ -218,7 +227,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": DTYPE_NAME[dtype], "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
-                   "I_shared": cfg.I_shared, "global_batch": cfg.T, "seq_len": cfg.T,
+                   "I_shared": cfg.I_shared, "output": cfg.out, "global_batch": cfg.T, "seq_len": cfg.T,
                    "parallelism": "single-gpu",
                    "linear1_input": "x_perm copy" if args.x_perm else "token rows gathered in place"},
         "tokens_per_s": round(tokens_s, 1),
@@ -391,6 +400,12 @@ def cpu_baseline(cfg, x, w_r, bias, ex, sh, layer, ntok):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     if ntok <= 0:
         # about 10-30 s of host work on a 16-core box for the large layers
         ntok = min(cfg.T, 64 if cfg.H * cfg.I <= 2 ** 20 else 1024)
@@ -435,7 +450,8 @@ def cpu_baseline(cfg, x, w_r, bias, ex, sh, layer, ntok):
     from mixture_experts_layer_07_amd.configs import active_flops
     fl = active_flops(cfg) / cfg.T * ntok
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "tokens_per_s": round(ntok / dt, 3),
-            "cores": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "cores": cores, "nproc": os.cpu_count(), "cpu_model": model, "kind": "oracle",
+            "seconds": round(dt, 2),
             "sample": f"{ntok} of {cfg.T} tokens (every {cfg.T // ntok}-th) through the fp64 oracle layer"}
 
 

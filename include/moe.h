@@ -49,19 +49,20 @@ typedef enum moe_status {
 
 /* Arithmetic type of a layer.
  *  MOE_F32      x, W_r, expert weights, y and out are fp32; fp32 accumulation.
- *  MOE_BF16     x, W_r, expert weights, intermediates (h, y_perm, y_shared) and out are bf16,
- *               each rounded once from fp32 accumulators.
+ *  MOE_BF16     x, W_r, expert weights and intermediates (h, y_perm, y_shared) are bf16, each
+ *               rounded once from fp32 accumulators; out is fp32 or bf16 (cfg->out_dtype).
  *  MOE_FP8_E4M3 x and W_r are bf16; the library quantises x per token per 128 channels to
  *               e4m3 for the experts; expert weights are e4m3 codes with one fp32 scale per
  *               128x128 block; the SwiGLU output is re-quantised per row per 128 channels;
- *               fp32 accumulation; y_perm, y_shared and out are bf16.
+ *               fp32 accumulation; y_perm and y_shared are bf16, out fp32 or bf16.
  *  MOE_MXFP4    FP8 activations times FP4 weights ("DeepGEMM质变：从GEMM库到统一LLM计算原语平台",
  *               itsolotime.com, 1.1 and 5.3) in the OCP microscaling formats: x and W_r are
  *               bf16; the library quantises x to MXFP8 (e4m3 codes, one E8M0 scale per 32
  *               channels, see moe_quantize_mx) for the experts; expert weights are MXFP4 (e2m1
  *               codes, two per byte, element 2j in the low nibble, one E8M0 scale per 32
  *               channels); the SwiGLU output is re-quantised to MXFP8; fp32 accumulation (the
- *               MFMA applies the block scales); y_perm, y_shared and out are bf16.
+ *               MFMA applies the block scales); y_perm and y_shared are bf16, out fp32 or
+ *               bf16.
  *
  * MX scale arrays. An operand of R rows and C channels (C a multiple of 128) has its E8M0 scale
  * codes (value 2^(code-127)) stored as [C/128][R][4] bytes: the 4-byte word at (g, r) holds the
@@ -83,11 +84,15 @@ typedef struct moe_config {
   int32_t group_score;     /* MOE_GROUP_MAX | MOE_GROUP_TOP2_SUM */
   int32_t dtype;           /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 | MOE_MXFP4 */
   int32_t I_shared;        /* intermediate size of the one shared expert; 0 = none */
+  int32_t out_dtype;       /* type of the layer output `out` (moe_combine): MOE_F32 or MOE_BF16;
+                              MOE_F32 layers take MOE_F32 only. The combine accumulates in fp32
+                              either way; MOE_F32 stores that sum, MOE_BF16 rounds it once. */
 } moe_config;
 
 /* Validates a config (no device access). Limits: T >= 1, 1 <= K <= E <= 256, H, I and I_shared
  * multiples of 128 for bf16/fp8, of 256 for MXFP4 and of 4 for fp32, E % n_group == 0,
- * K <= topk_group*E/n_group, T*K < 2^31. */
+ * K <= topk_group*E/n_group, T*K < 2^31, out_dtype MOE_F32 or MOE_BF16 (MOE_F32 for fp32
+ * layers). */
 moe_status moe_check_config(const moe_config* cfg);
 
 /* Bytes of device workspace that moe_route, moe_permute and moe_expert_ffn (routed and
@@ -203,9 +208,9 @@ moe_status moe_expert_ffn_gather(const moe_config* cfg, int32_t n_experts, int32
  *   topk_weights device [T,K] fp32 from moe_route
  *   y_perm       device [P,H] from moe_expert_ffn (fp32 for MOE_F32, else bf16)
  *   y_shared     device [T,H] shared expert output (same dtype as y_perm), or NULL
- *   out          device [T,H] out (fp32 for MOE_F32, else bf16)
+ *   out          device [T,H] out, of type cfg->out_dtype (fp32 or bf16)
  * out[t] = sum_k topk_weights[t,k] * y_perm[pair_pos[t*K+k]] (+ y_shared[t]), accumulated in
- * fp32 in k order, rounded once. Needs no workspace. */
+ * fp32 in k order; stored as that fp32 sum, or rounded once to bf16. Needs no workspace. */
 moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const float* topk_weights,
                        const void* y_perm, const void* y_shared, void* out, void* stream);
 

@@ -35,7 +35,7 @@ class MoeConfig(ctypes.Structure):
                 ("renorm", ctypes.c_int32), ("route_scale", ctypes.c_float),
                 ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
                 ("group_score", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("I_shared", ctypes.c_int32)]
+                ("I_shared", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -94,7 +94,7 @@ def make_config(cfg: LayerConfig) -> MoeConfig:
                      1 if cfg.renorm else 0, float(cfg.route_scale), cfg.n_group,
                      cfg.topk_group if cfg.n_group > 1 else 1,
                      MOE_GROUP_TOP2_SUM if cfg.group_rule == "top2_sum" else MOE_GROUP_MAX,
-                     dt, cfg.I_shared)
+                     dt, cfg.I_shared, MOE_F32 if cfg.out == "f32" else MOE_BF16)
 
 
 def _cfg(cfg):

@@ -30,6 +30,7 @@ class LayerConfig:
     dtype: str           # "f32" | "bf16" | "fp8" | "mxfp4" (MXFP8 activations x MXFP4 weights)
     I_shared: int        # shared expert intermediate size (0 = none)
     seed: int
+    out: str = "bf16"    # type of the layer output: "f32" | "bf16" (fp32 layers: "f32")
 
     @property
     def P(self):
@@ -42,16 +43,16 @@ class LayerConfig:
 CONFIGS = {
     1: LayerConfig("tiny-fp32", T=64, H=128, I=256, E=8, K=2, score="softmax", renorm=True,
                    route_scale=1.0, n_group=1, topk_group=1, group_rule="top2_sum", bias=None,
-                   dtype="f32", I_shared=0, seed=0),
+                   dtype="f32", I_shared=0, seed=0, out="f32"),
     2: LayerConfig("mixtral-bf16", T=4096, H=4096, I=14336, E=8, K=2, score="softmax",
                    renorm=True, route_scale=1.0, n_group=1, topk_group=1, group_rule="top2_sum",
-                   bias=None, dtype="bf16", I_shared=0, seed=1),
+                   bias=None, dtype="bf16", I_shared=0, seed=1, out="f32"),
     3: LayerConfig("dsv3-bf16", T=8192, H=7168, I=2048, E=256, K=8, score="sigmoid",
                    renorm=True, route_scale=2.5, n_group=8, topk_group=4, group_rule="top2_sum",
-                   bias="normal", dtype="bf16", I_shared=2048, seed=2),
+                   bias="normal", dtype="bf16", I_shared=2048, seed=2, out="f32"),
     4: LayerConfig("decode-zipf-bf16", T=128, H=7168, I=2048, E=256, K=8, score="sigmoid",
                    renorm=True, route_scale=2.5, n_group=8, topk_group=4, group_rule="top2_sum",
-                   bias="zipf", dtype="bf16", I_shared=2048, seed=3),
+                   bias="zipf", dtype="bf16", I_shared=2048, seed=3, out="f32"),
     5: LayerConfig("dsv3-fp8", T=8192, H=7168, I=2048, E=256, K=8, score="sigmoid",
                    renorm=True, route_scale=2.5, n_group=8, topk_group=4, group_rule="top2_sum",
                    bias="normal", dtype="fp8", I_shared=2048, seed=4),

@@ -8,6 +8,7 @@
 
 #include "device.h"
 #include "internal.h"
+#include "tile_plan.h"
 
 namespace moe {
 
@@ -43,17 +44,12 @@ struct GemmArgs {
 // and a cheap tile (a ragged last m-tile) frees its workgroup early instead of stalling a fixed
 // round. Every tile is computed by one workgroup from start to end, so results do not depend on
 // the order.
-constexpr int kQueues = 8;
 // Tile-metadata region: tp[0 .. kMaxExperts], then the queue counters of both GEMMs, then the
 // split-tile arrival counters of both GEMMs.
 constexpr int kTileQueueOffset = kMaxExperts + 1;
-constexpr int kMaxSplitItems = 512;  // K-split work items per GEMM launch (one per workgroup at most)
 constexpr int kSplitCntOffset = kTileQueueOffset + 2 * kQueues;
 static_assert(kSplitCntOffset + 2 * kMaxSplitItems <= kTileMetaInts, "tile metadata region too small");
 constexpr int kPartFloats = 256 * 256;  // one partial 256 x 256 tile
-#ifndef MOE_MAX_K_PIECES
-#define MOE_MAX_K_PIECES 4  // most pieces a tail tile is cut into along K
-#endif
 
 struct TileQueue {
   int beg, end;
@@ -77,93 +73,48 @@ __device__ __forceinline__ int next_tile(const GemmArgs& g, const TileQueue& tq,
   return t < tq.end ? t : -1;
 }
 
-// Tile queue whose last round is split along K. A range of R tiles served by C workgroups takes
-// F = R / C full rounds; the R - F*C tiles left would keep only part of the XCD busy for a whole
-// tile, so each is cut into S pieces of K (S*tail <= C), one work item each. The pieces write
-// fp32 partial tiles; the last piece to arrive (an atomic counter per tile) sums them in piece
-// order, so the result does not depend on timing, and runs the epilogue.
-struct SplitQueue {
-  int beg;     // first tile of the range
-  int nfull;   // items [0, nfull) are whole tiles beg + item
-  int S;       // pieces per tail tile
-  int items;   // items in the range
-  int slot0;   // first partial-tile slot of the range
-  int q;       // range (= XCD) index
-};
-
-// The queue (range) is chosen by the XCD the workgroup runs on, so that every piece of a split
-// tile is computed under one L2. With one workgroup per CU all workgroups are resident and every
-// XCD serves its range.
+// Tile queue whose last round is split along K: the plan (split_plan) and the item decode
+// (plan_item) are pure integer arithmetic in tile_plan.h; here they are fed the workgroup's range
+// and drawn from the range's counter.
+// The range is chosen by the workgroup id (b % 8), so every range is served by exactly
+// gridDim.x / 8 workgroups (the grid is a multiple of 8) and drains whatever the placement.
+// Workgroups are dispatched round-robin over the 8 XCDs, so the workgroups of a range, and the
+// pieces of a split tile, normally share one XCD and its L2; the handoff of the pieces
+// (split_arrive) does not rely on that.
 // max_slots: partial tiles the kernel's workspace region holds (pieces of one launch).
 __device__ __forceinline__ SplitQueue split_queue(int total, int KT, int min_steps, int max_slots) {
-  const int q = xcc_id();
-  const int per = (total + kQueues - 1) / kQueues;
-  const int beg = q * per < total ? q * per : total;
-  const int end = beg + per < total ? beg + per : total;
-  const int R = end - beg;
-  const int C = gridDim.x / kQueues;  // workgroups serving this range
-  const int F = R / C, tail = R - F * C;
-  int S = 1;
-  // Only long K loops are cut: a piece pays a fixed cost (its own prologue, the partial tile
-  // written and read back through L2, the summation), which a short loop does not repay. A range
-  // with fewer tiles than workgroups (F = 0: a small launch, e.g. a decode-sized shared expert)
-  // has every tile cut once its K loop has two pieces' worth of steps.
-  if (tail > 0 && C * kQueues <= kMaxSplitItems && C * kQueues <= max_slots &&
-      (F > 0 ? KT >= 128 : KT >= 2 * min_steps)) {
-    S = C / tail;
-    if (S > MOE_MAX_K_PIECES) S = MOE_MAX_K_PIECES;
-    if (S > KT / min_steps) S = KT / min_steps;
-    if (S < 1) S = 1;
-  }
-  SplitQueue sq;
-  sq.beg = beg;
-  sq.S = S;
-  sq.nfull = S > 1 ? F * C : R;
-  sq.items = sq.nfull + (R - sq.nfull) * S;
-  sq.slot0 = q * C;
-  sq.q = q;
-  return sq;
+  return split_plan(blockIdx.x % kQueues, total, KT, min_steps, max_slots, gridDim.x / kQueues,
+                    kMaxSplitItems, MOE_MAX_K_PIECES);
 }
 
-struct WorkItem {
-  int tile;   // tile index in the expert-major list
-  int piece;  // -1: whole tile; else the K piece of a split tile
-  int k0, k1; // K steps [k0, k1)
-  int slot;   // partial-tile slot of this piece
-  int first;  // slot of piece 0 of the same tile (its arrival counter index as well)
-};
-
 // Next work item of this workgroup's range, or item.tile = -1. All threads must call (two barriers).
-// K steps are counted in units of `step`; pieces keep an even number of steps.
 __device__ __forceinline__ WorkItem next_item(const GemmArgs& g, const SplitQueue& sq, int KT, int* s_slot) {
   if (threadIdx.x == 0) s_slot[0] = atomicAdd(&g.queue[sq.q], 1);
   __syncthreads();
   // the same for every lane; readfirstlane tells the compiler so (scalar registers, uniform branches)
   const int it = __builtin_amdgcn_readfirstlane(s_slot[0]);
   __syncthreads();
-  WorkItem w;
-  if (it >= sq.items) {
-    w.tile = -1;
-    return w;
+  return plan_item(sq, it, KT);
+}
+
+// Arrival of a K piece whose partial tile every thread of the workgroup has stored: returns true
+// (uniformly) for the last piece of the tile to arrive, which then sums all pieces. The pieces may
+// run on different XCDs, whose L2 caches are not kept coherent for plain stores, so the arrival is
+// a release at agent scope (this XCD's L2 written back first) and the last arriver acquires at
+// agent scope (its caches invalidated) before it reads the other pieces' partial tiles.
+// All threads must call (three barriers).
+__device__ __forceinline__ bool split_arrive(int32_t* cnt, int S, int* s_slot) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    s_slot[0] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (it < sq.nfull) {
-    w.tile = sq.beg + it;
-    w.piece = -1;
-    w.k0 = 0;
-    w.k1 = KT;
-    w.slot = w.first = 0;
-    return w;
-  }
-  const int j = it - sq.nfull;
-  const int tt = j / sq.S;
-  w.tile = sq.beg + sq.nfull + tt;
-  w.piece = j - tt * sq.S;
-  const int chunk = (KT / sq.S) & ~1;
-  w.k0 = w.piece * chunk;
-  w.k1 = w.piece == sq.S - 1 ? KT : w.k0 + chunk;
-  w.first = sq.slot0 + tt * sq.S;
-  w.slot = w.first + w.piece;
-  return w;
+  __syncthreads();
+  const bool last = __builtin_amdgcn_readfirstlane(s_slot[0]) == S - 1;
+  __syncthreads();
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
 }
 
 // Partial tile of a K piece: a workgroup's NT threads' fp32 accumulators (MB x NB blocks each),

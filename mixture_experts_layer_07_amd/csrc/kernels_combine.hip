@@ -7,8 +7,9 @@
 // atomics are needed and the result does not depend on scheduling. Accumulation is fp32 in k
 // order, the shared row last, then one rounding to the output type.
 //
-// Expert rows arrive as fp32 (fp32 layer) or bf16 (bf16, fp8 and MX layers); the output is fp32
-// (fp32 layer) or bf16. A chunk is EPC consecutive channels (16 bytes of a y row).
+// Expert rows arrive as fp32 (fp32 layer) or bf16 (bf16, fp8 and MX layers); the output is the
+// fp32 sum itself or its bf16 rounding (the config's output type). A chunk is EPC consecutive
+// channels (16 bytes of a y row).
 #include "device.h"
 #include "internal.h"
 
@@ -165,6 +166,10 @@ hipError_t launch_combine(const moe_config& c, const int32_t* pair_pos, const fl
     });
   }
   const dim3 grid(c.T, (c.H / 8 + 511) / 512);
+  if (c.out_dtype == MOE_F32)
+    return timed_launch("combine_bf16_f32out", s, [&] {
+      launch_combine_k<8, false, true>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
+    });
   return timed_launch("combine_bf16", s, [&] {
     launch_combine_k<8, false, false>(c.K, grid, s, pair_pos, w, y, ysh, o, c.H);
   });

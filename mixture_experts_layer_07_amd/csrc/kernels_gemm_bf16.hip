@@ -68,10 +68,8 @@ __device__ __forceinline__ void mfmas(f32x16 (&acc)[MB][NB], const bf16x8 (&a)[M
 }
 
 // Partial tiles of K-split work items (2 x 2 layout): float4 v of thread t at [v][t] (coalesced
-// 4 KiB rows). All pieces of a tile run on one XCD (the split queue is chosen by the XCD id), so
-// the partials meet in that XCD's L2: plain stores completed before the arrival counter is
-// incremented, and plain loads after it (no L1 line of another piece's partial is ever read
-// before in a launch).
+// 4 KiB rows). The pieces hand their partials over through split_arrive (release / acquire at
+// agent scope).
 template <int MB, int NB>
 __device__ __forceinline__ void store_partial(float* part, const f32x16 (&acc)[MB][NB], int tid) {
 #pragma unroll
@@ -308,12 +306,7 @@ constexpr int kWaitLgkm0Vm8 = wait_lgkm0_vm(8), kWaitLgkm0Vm0 = wait_lgkm0_vm(0)
     if (SPLIT && w.piece >= 0) {                                                                 \
       /* K piece: publish it; the last piece to arrive sums all of them in piece order */        \
       w4::store_partial(g.part + (size_t)w.slot * kPartStride, acc, tid);                        \
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                           \
-      __syncthreads();                                                                           \
-      if (tid == 0) s_slot[0] = atomicAdd(&g.split_cnt[w.first], 1);                             \
-      __syncthreads();                                                                           \
-      store = __builtin_amdgcn_readfirstlane(s_slot[0]) == sq.S - 1;                             \
-      __syncthreads();                                                                           \
+      store = split_arrive(&g.split_cnt[w.first], sq.S, s_slot);                                 \
       if (store) {                                                                               \
         _Pragma("unroll") for (int mb = 0; mb < (MB_); ++mb)                                     \
           _Pragma("unroll") for (int nb = 0; nb < (NB_); ++nb)                                   \

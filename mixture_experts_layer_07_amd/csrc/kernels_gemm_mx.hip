@@ -284,12 +284,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
       // K piece: publish it; the last piece to arrive sums all of them in piece order
       constexpr size_t kPart = (size_t)MB * NB * 16 * NT;
       store_partial_acc<MB, NB, NT>(g.part + (size_t)w.slot * kPart, acc, tid);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (tid == 0) s_slot[0] = atomicAdd(&g.split_cnt[w.first], 1);
-      __syncthreads();
-      store = __builtin_amdgcn_readfirstlane(s_slot[0]) == sq.S - 1;
-      __syncthreads();
+      store = split_arrive(&g.split_cnt[w.first], sq.S, s_slot);
       if (store) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)

@@ -55,6 +55,10 @@ moe_status check_config(const moe_config* c, std::string* why) {
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16 && c->dtype != MOE_FP8_E4M3 && c->dtype != MOE_MXFP4)
     return bad(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (c->I_shared < 0) return bad(MOE_ERR_INVALID_ARG, "I_shared must be >= 0");
+  if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
+    return bad(MOE_ERR_INVALID_ARG, "out_dtype must be MOE_F32 or MOE_BF16");
+  if (c->dtype == MOE_F32 && c->out_dtype != MOE_F32)
+    return bad(MOE_ERR_UNSUPPORTED, "fp32 layers write fp32 output");
   const int q = channel_multiple(c->dtype);
   if (c->H % q || c->I % q || c->I_shared % q)
     return bad(MOE_ERR_UNSUPPORTED,

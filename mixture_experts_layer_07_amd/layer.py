@@ -53,7 +53,8 @@ class MoELayer:
         # expert outputs: fp32 for the fp32 layer, bf16 otherwise
         ydt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
         self.y_perm = torch.empty((P, H), dtype=ydt, device=dev)
-        self.out = torch.empty((T, H), dtype=act, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.float32 if cfg.out == "f32" else torch.bfloat16,
+                               device=dev)
         if self.shared is not None:
             self.y_shared = torch.empty((T, H), dtype=ydt, device=dev)
             self.shared_offsets = torch.tensor([0, T], **i32)

@@ -5,11 +5,17 @@ near-tie routing flip cannot cascade), plus the end-to-end output.
 Bars:
   * ids, counts, offsets, the permutation, x_perm and fp8 / MX codes and scales: bit-exact;
   * routing weights: |dw| <= 1e-5 * route_scale;
-  * rows of y_perm, y_shared (fp32 for the fp32 layer, else bf16) and out: |err_j| <= tol * rms(ref
-    row) with tol = 1e-4 (fp32), 2e-2 (bf16), 6e-2 (fp8, MXFP8 x MXFP4), plus, where the row is stored as bf16,
-    half a bf16 ulp of the value itself (2^-8 |ref_j|): the format cannot hold the exact result
-    any closer, and that alone reaches 2e-2 * rms at a 5-sigma element;
-  * the combine alone: |out - ref| <= 2^-8 |ref| + 1e-6 rms (one rounding), 1e-6 (fp32).
+  * layer output rows: max_j |out - ref| <= tol * rms(ref row), tol = 1e-4 (fp32), 2e-2 (bf16),
+    6e-2 (fp8, MXFP8 x MXFP4), asserted on the raw error: the bf16 layers write an fp32 output,
+    the fp8 and MX layers a bf16 one. Only a bf16 layer asked for a bf16 output gets half a bf16
+    ulp of the value on top (2^-8 |ref_j|): that rounding alone reaches 1.8e-2 * rms at a
+    4.5-sigma element, and the bf16 SwiGLU output that Linear-2's bf16 MFMA reads adds noise of
+    about 1.6e-3 * rms, so the bare bound would fail on about 1 % of such rows;
+  * intermediate rows (y_perm, y_shared: fp32 for the fp32 layer, else bf16) are stored
+    outputs of a bf16 rounding: the same tol, plus that rounding where they are bf16 (the raw
+    figure is reported beside it);
+  * the combine alone: |out - ref| <= 2^-8 |ref| + 1e-6 rms (bf16 output, one rounding),
+    1e-6 (|ref| + rms) (fp32 output).
 Near ties: tokens whose routing rests on a key gap < 1e-5 may differ in ids (counted, excluded
 from the id comparison; downstream checks use the GPU's routing).
 """
@@ -128,16 +134,25 @@ def expert_rows(case, x_rows, owner, shared=False):
 
 
 def assert_rows(got, ref, tol, what, report, bf16_out=False):
-    """|got - ref| <= tol * rms(ref row) (+ 2^-8 |ref| when the rows are stored as bf16)."""
+    """|got - ref| <= tol * rms(ref row) (+ 2^-8 |ref| when bf16_out: rows stored as bf16 whose
+    own rounding the bound allows). The raw maximum is always reported."""
     rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
     rms = np.where(rms == 0, 1.0, rms)
     d = np.abs(got - ref)
     report[f"{what}_max_err_rms"] = float((d / rms).max())
-    beyond = np.maximum(d - (2.0 ** -8 * np.abs(ref) if bf16_out else 0.0), 0.0) / rms
-    if bf16_out:
-        report[f"{what}_max_err_rms_beyond_bf16_rounding"] = float(beyond.max())
     assert np.isfinite(d).all(), f"{what}: non-finite output"
-    assert beyond.max() <= tol, f"{what}: max |err|/rms beyond the output rounding = {beyond.max():.3e}"
+    if bf16_out:
+        beyond = np.maximum(d - 2.0 ** -8 * np.abs(ref), 0.0) / rms
+        report[f"{what}_max_err_rms_beyond_bf16_rounding"] = float(beyond.max())
+        assert beyond.max() <= tol, f"{what}: max |err|/rms beyond the bf16 rounding = {beyond.max():.3e}"
+    else:
+        assert (d / rms).max() <= tol, f"{what}: max |err|/rms = {(d / rms).max():.3e} > {tol}"
+
+
+def output_allowance(cfg):
+    """Whether the layer output check allows the bf16 rounding of the output (only a bf16 layer
+    asked for a bf16 output; every other layer is held to the raw bound)."""
+    return cfg.dtype == "bf16" and cfg.out == "bf16"
 
 
 def check_route(case, report):
@@ -243,7 +258,7 @@ def check_combine(case, pp, w_g, tokens, report):
     ref = orc.combine(np.arange(need.size), w_g[toks], y_rows, ysh)
     got = rows_of(L.out, toks)
     rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
-    if case.cfg.dtype == "f32":
+    if case.cfg.out == "f32":
         bound = 1e-6 * np.abs(ref) + 1e-6 * rms
     else:
         bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * rms
@@ -261,7 +276,7 @@ def check_end_to_end(case, ids_g, w_g, tokens, report):
                               c.group_rule, c.renorm, c.route_scale, fp8=c.dtype == "fp8",
                               get_shared=get_sh, tokens=toks, ids=ids_g, weights=w_g,
                               mx=c.dtype == "mxfp4")
-    assert_rows(rows_of(L.out, toks), ref, TOL[c.dtype], "e2e", report, bf16_out=c.dtype != "f32")
+    assert_rows(rows_of(L.out, toks), ref, TOL[c.dtype], "e2e", report, bf16_out=output_allowance(c))
 
 
 def full_check(case, ffn_rows=None, tokens=None, perm_rows=None):

@@ -56,6 +56,16 @@ def test_check_config(lib):
     c = cfg(3)
     c.dtype = 7
     assert lib.moe_check_config(ctypes.byref(c)) == INVALID
+    c = cfg(3)
+    c.out_dtype = 2    # the output is fp32 or bf16
+    assert lib.moe_check_config(ctypes.byref(c)) == INVALID
+    c = cfg(1)
+    c.out_dtype = B.MOE_BF16   # an fp32 layer writes fp32
+    assert lib.moe_check_config(ctypes.byref(c)) == UNSUPPORTED
+    for i in (3, 5):
+        c = cfg(i)
+        c.out_dtype = B.MOE_BF16 if c.out_dtype == B.MOE_F32 else B.MOE_F32
+        assert lib.moe_check_config(ctypes.byref(c)) == OK
     c = cfg(1)
     c.H = 130          # fp32 needs multiples of 4
     assert lib.moe_check_config(ctypes.byref(c)) == UNSUPPORTED

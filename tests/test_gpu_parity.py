@@ -42,6 +42,8 @@ SMALL = {
     # into pieces (bf16: 32 steps of 64 channels; MX: 14 steps of 256)
     "decode-bf16-ksplit": (CONFIGS[4].scaled(T=24, H=2048, I=256, E=64, K=8, bias="normal", I_shared=256), "zipf"),
     "decode-mxfp4-ksplit": (CONFIGS[7].scaled(T=24, H=3584, I=512, E=64, K=8, I_shared=512), None),
+    # a bf16 layer asked for a bf16 output (the output check then allows that rounding)
+    "dsv3-bf16-bf16out": (CONFIGS[3].scaled(T=520, H=256, I=256, E=32, K=8, I_shared=128, out="bf16"), None),
 }
 
 
@@ -318,3 +320,32 @@ def test_whole_layer_graph_replays_match_eager(name):
     torch.cuda.synchronize()
     assert torch.equal(L.out.view(torch.int16), want2.view(torch.int16)), "replay on new inputs"
     assert B.moe_get_device_error(L.ws) == 0
+
+
+def test_k_split_tail_after_full_rounds_every_row():
+    """The 256 x 256 bf16 kernel's K-split path with full rounds before the tail (F > 0, K loops
+    of >= 128 steps): Linear-2 with I = 8192 over 8 experts of ~1100 rows on H = 2048 has about
+    40 tiles per range of 32 workgroups, so each range runs one full round and cuts its tail
+    tiles into K pieces. Every row of y (so every row of every split tile) against the oracle."""
+    cfg = CONFIGS[2].scaled(T=4500, H=2048, I=8192, E=8, K=2)
+    print(f"k-split case T={cfg.T} H={cfg.H} I={cfg.I}", flush=True)
+    case = Case(cfg, wdev="cuda")
+    L = case.layer
+    case.run()
+    offsets = L.offsets.cpu().numpy()
+    # the plan of the Linear-2 launch (tile_plan.h): tiles per range, workgroups per range
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    C = ((cus + 7) // 8 * 8) // 8
+    mtiles = sum((int(n) + 255) // 256 for n in np.diff(offsets) if n > 0)
+    total = mtiles * (cfg.H // 256)
+    per = (total + 7) // 8
+    ranges = [min(total, (q + 1) * per) - min(total, q * per) for q in range(8)]
+    assert avg_rows(offsets) >= 128 and any(R > C and R % C for R in ranges), (ranges, C)
+    rep = {}
+    check_ffn(case, offsets, np.arange(cfg.P), rep)
+    assert B.moe_get_device_error(L.ws) == 0
+    print(rep, "tiles per range:", ranges, "workgroups per range:", C)
+
+
+def avg_rows(offsets):
+    return int(offsets[-1]) // (len(offsets) - 1)
