@@ -156,6 +156,23 @@ moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* 
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
                        void* x_perm, void* x_perm_scale, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_permute_noalloc -- moe_permute for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument. Its scratch (the per-block expert histogram and bases of the three-pass sort, and an
+ * error word) lives in one static device array of 2 MiB + 256 bytes, one copy on each device the
+ * library runs on, held until the process ends; the call allocates and frees nothing.
+ *   Arguments, outputs and ordering as moe_permute, whose results it reproduces bit for bit.
+ *   Limit: 2 * ceil(T*K / 256) * E * 4 bytes <= 2 MiB (e.g. T*K <= 262144 at E = 256);
+ *   larger configs return MOE_ERR_UNSUPPORTED before any device call.
+ *   Out-of-range ids are dropped as in moe_permute (pair_pos -1, offsets[E] < T*K) but are not
+ *   reported through moe_get_device_error, which reads a caller's workspace.
+ *   Every call on a device shares that device's scratch: calls that overlap in time on one
+ *   device (two streams, two threads) race and must be serialised by the caller. Nothing in the
+ *   scratch needs clearing between calls (every entry read is written first in the same call). */
+moe_status moe_permute_noalloc(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                               const void* x, void* x_perm, void* x_perm_scale, void* stream);
+
 /* moe_expert_ffn -- SwiGLU experts over expert-grouped rows, as two grouped GEMMs
  * ("MoE 路由入门", sections 1 and 5.2; Linear-1 = gate and up together, "SwiGLU / FP8 Cast",
  * Linear-2, from "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", section 5.1).

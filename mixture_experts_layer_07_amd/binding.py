@@ -47,6 +47,7 @@ _SIGS = {
     "moe_route_logits": (_I, [_P, _P, _P, _P, _P, _P]),
     "moe_update_bias": (_I, [_I, _P, _P, ctypes.c_float, _P]),
     "moe_permute": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_permute_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_gather": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                    _P]),
@@ -154,6 +155,14 @@ def moe_permute(cfg, topk_ids, counts, offsets, sorted_pair, pair_pos, x, x_perm
     _check(lib().moe_permute(pc, _p(topk_ids), _p(counts), _p(offsets), _p(sorted_pair),
                              _p(pair_pos), _p(x), _p(x_perm), _p(x_perm_scale), _p(ws),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_permute")
+
+
+def moe_permute_noalloc(cfg, topk_ids, counts, offsets, sorted_pair, pair_pos, x, x_perm, x_perm_scale,
+                        stream=None):
+    c, pc = _cfg(cfg)
+    _check(lib().moe_permute_noalloc(pc, _p(topk_ids), _p(counts), _p(offsets), _p(sorted_pair),
+                                     _p(pair_pos), _p(x), _p(x_perm), _p(x_perm_scale), _stream(stream)),
+           "moe_permute_noalloc")
 
 
 def moe_expert_ffn(cfg, n_experts, n_rows, inter, offsets, x_rows, x_scale, w13, w13_scale, w2,

@@ -166,40 +166,81 @@ moe_status moe_update_bias(int32_t n_experts, const int32_t* counts, float* bias
   return MOE_OK;
 }
 
-moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
-                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
-                       void* x_perm, void* x_perm_scale, void* ws, size_t ws_bytes,
-                       void* stream) {
+// Shared body of moe_permute and moe_permute_noalloc: argument checks (before any device call).
+static moe_status permute_args(const char* where, const moe_config* cfg, const int32_t* topk_ids,
+                               const int32_t* counts, const int32_t* offsets, const int32_t* sorted_pair,
+                               const int32_t* pair_pos, const void* x, const void* x_perm,
+                               const void* x_perm_scale) {
   MOE_TRY(checked_config(cfg));
   const moe_config& c = *cfg;
+  const std::string w(where);
   if (!topk_ids || !counts || !offsets || !sorted_pair || !pair_pos)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: NULL buffer");
+    return fail(MOE_ERR_INVALID_ARG, w + ": NULL buffer");
   if ((x == nullptr) != (x_perm == nullptr))
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: x and x_perm must both be given or both NULL");
+    return fail(MOE_ERR_INVALID_ARG, w + ": x and x_perm must both be given or both NULL");
   const bool quant = c.dtype == MOE_FP8_E4M3 || c.dtype == MOE_MXFP4;
   if (x && quant && !x_perm_scale)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: fp8 and MX layers need x_perm_scale");
+    return fail(MOE_ERR_INVALID_ARG, w + ": fp8 and MX layers need x_perm_scale");
   if (!quant && x_perm_scale)
-    return fail(MOE_ERR_INVALID_ARG, "moe_permute: x_perm_scale is only for fp8 and MX layers");
-  WsLayout L;
-  MOE_TRY(check_ws(c, ws, ws_bytes, &L));
-  MOE_TRY(ensure_device());
-  hipStream_t s = static_cast<hipStream_t>(stream);
+    return fail(MOE_ERR_INVALID_ARG, w + ": x_perm_scale is only for fp8 and MX layers");
+  return MOE_OK;
+}
+
+// The launches of the permutation with its scratch at err / hist / base.
+static moe_status permute_launch(const moe_config& c, const int32_t* topk_ids, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                 const void* x, void* x_perm, void* x_perm_scale, int32_t* err,
+                                 int32_t* hist, int32_t* base, hipStream_t s) {
   const int P = c.T * c.K;
-  int32_t* hist = at<int32_t>(ws, L.hist);
-  int32_t* base = at<int32_t>(ws, L.base);
-  int32_t* err = at<int32_t>(ws, L.err);
+  const int nblk = (P + kPermBlock - 1) / kPermBlock;
   if (P <= kSmallPermPairs) {
     MOE_HIP(launch_perm_small(topk_ids, P, c.E, counts, offsets, sorted_pair, pair_pos, err, s),
             "perm_small");
   } else {
     MOE_HIP(launch_perm_hist(topk_ids, P, c.E, hist, err, s), "perm_hist");
-    MOE_HIP(launch_perm_scan(hist, L.perm_blocks, c.E, base, counts, s), "perm_scan");
+    MOE_HIP(launch_perm_scan(hist, nblk, c.E, base, counts, s), "perm_scan");
     MOE_HIP(launch_perm_scatter(topk_ids, P, c.E, base, counts, offsets, sorted_pair, pair_pos, s),
             "perm_scatter");
   }
   if (x) MOE_HIP(launch_gather(c, sorted_pair, x, x_perm, x_perm_scale, s), "gather");
   return MOE_OK;
+}
+
+moe_status moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, const void* x,
+                       void* x_perm, void* x_perm_scale, void* ws, size_t ws_bytes,
+                       void* stream) {
+  MOE_TRY(permute_args("moe_permute", cfg, topk_ids, counts, offsets, sorted_pair, pair_pos, x, x_perm,
+                       x_perm_scale));
+  const moe_config& c = *cfg;
+  WsLayout L;
+  MOE_TRY(check_ws(c, ws, ws_bytes, &L));
+  MOE_TRY(ensure_device());
+  return permute_launch(c, topk_ids, counts, offsets, sorted_pair, pair_pos, x, x_perm, x_perm_scale,
+                        at<int32_t>(ws, L.err), at<int32_t>(ws, L.hist), at<int32_t>(ws, L.base),
+                        static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute_noalloc(const moe_config* cfg, const int32_t* topk_ids, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                               const void* x, void* x_perm, void* x_perm_scale, void* stream) {
+  MOE_TRY(permute_args("moe_permute_noalloc", cfg, topk_ids, counts, offsets, sorted_pair, pair_pos, x,
+                       x_perm, x_perm_scale));
+  const moe_config& c = *cfg;
+  const size_t nblk = ((size_t)c.T * c.K + kPermBlock - 1) / kPermBlock;
+  const size_t need = 2 * nblk * (size_t)c.E * 4;
+  if (need > kNoAllocScratchBytes - 256)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_permute_noalloc: 2 * ceil(T*K/256) * E * 4 = " + std::to_string(need) +
+                                         " bytes of scratch exceed its " +
+                                         std::to_string(kNoAllocScratchBytes - 256) + " (use moe_permute)");
+  MOE_TRY(ensure_device());
+  void* sp = nullptr;
+  MOE_HIP(noalloc_scratch(&sp), "hipGetSymbolAddress(scratch)");
+  int32_t* err = static_cast<int32_t*>(sp);
+  int32_t* hist = err + 64;
+  int32_t* base = hist + nblk * c.E;
+  return permute_launch(c, topk_ids, counts, offsets, sorted_pair, pair_pos, x, x_perm, x_perm_scale, err,
+                        hist, base, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -35,6 +35,9 @@ constexpr int kPermBlock = 256;   // pairs per block in the permutation kernels
 constexpr int kSmallPermPairs = 4096;  // up to this many pairs: one-workgroup permutation
 constexpr int kMaxExperts = 256;
 constexpr int kTileMetaInts = 2048;  // tile metadata of the expert GEMMs (prefix, queues, counters)
+// moe_permute_noalloc: its scratch (error word + per-block histogram and bases) in a static device
+// array of this many bytes; the histogram and bases take 2 * ceil(P / 256) * E * 4 of them.
+constexpr size_t kNoAllocScratchBytes = (size_t(2) << 20) + 256;
 
 // Validation; returns MOE_OK or the failure status with a reason in *why.
 moe_status check_routing(const moe_config* c, std::string* why);
@@ -86,6 +89,9 @@ hipError_t launch_topk(const moe_config& c, const float* logits, int splits, con
 // permute
 hipError_t launch_update_bias(const int32_t* counts, int E, float* bias, float gamma, hipStream_t s);
 hipError_t launch_clear_words(int32_t* p, int n, hipStream_t s);
+// Device address of moe_permute_noalloc's static scratch on the current device (looked up once
+// per device).
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_perm_small(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                              int32_t* sorted_pair, int32_t* pair_pos, int32_t* err, hipStream_t s);
 hipError_t launch_perm_hist(const int32_t* ids, int P, int E, int32_t* hist, int32_t* err,

@@ -12,10 +12,37 @@
 //            base for e + the count of e in earlier waves of the block + its rank among the
 //            equal ids of its wave (found with 8 ballots over the id bits)
 // then the gather copies (or, for the fp8 layer, quantises) token rows into x_perm.
+#include <map>
+#include <mutex>
+
 #include "device.h"
 #include "internal.h"
 
 namespace moe {
+
+// Scratch of moe_permute_noalloc: the error word (first 256 bytes), then the per-block histogram
+// and the per-block bases, [nblk][E] int32 each. One copy per device, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only stands for the
+// symbol); it takes the device address from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / 4];
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // (the device is current)
+    if (e != hipSuccess) return e;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
+}
 
 __global__ void k_clear_words(int32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;

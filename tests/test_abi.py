@@ -114,6 +114,14 @@ def test_entry_points_validate_before_device(lib):
     assert lib.moe_permute(p8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                            lib.moe_workspace_size(p8), None) == INVALID      # fp8 without x_perm_scale
     assert lib.moe_combine(pc, None, FAKE, FAKE, None, FAKE, None) == INVALID
+    # the no-allocation permutation: the same argument checks, and a config whose histogram and
+    # bases exceed the static scratch (2 * ceil(T*K/256) * E * 4 > 2 MiB) is refused up front
+    assert lib.moe_permute_noalloc(pc, None, FAKE, FAKE, FAKE, FAKE, None, None, None, None) == INVALID
+    assert lib.moe_permute_noalloc(pc, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INVALID
+    big = cfg(3, T=40000)      # ceil(320000 / 256) * 256 * 8 bytes = 2.56 MB
+    assert lib.moe_permute_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                   None) == UNSUPPORTED
+    assert "moe_permute" in lib.moe_last_error().decode()
     assert lib.moe_quantize_fp8(4, 100, FAKE, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_fp8(4, 256, None, FAKE, FAKE, None) == INVALID
     assert lib.moe_quantize_mx(4, 100, FAKE, FAKE, FAKE, None) == INVALID
