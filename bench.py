@@ -6,6 +6,7 @@ layer (T=8192, H=7168, I=2048, E=256, K=8, grouped sigmoid routing, one shared e
 largest layer of the set that one GPU holds. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 25] [--config 3] [--no-cpu-baseline]
+                  [--single-launch]   (decode-sized bf16 layers: the whole layer in one kernel launch)
 """
 import argparse
 import json
@@ -36,6 +37,9 @@ def parse():
     p.add_argument("--x-perm", action="store_true",
                    help="time the path that writes the permuted activations x_perm instead of "
                         "gathering the token rows in Linear-1")
+    p.add_argument("--single-launch", action="store_true",
+                   help="time the whole layer as one kernel launch (moe_layer_decode; bf16 layers "
+                        "with T*K <= 4096)")
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = auto)")
     p.add_argument("--copy-calibration-gib", type=float, default=0.0,
                    help="after the measurement, run one plain copy-like pass over this many GiB "
@@ -110,6 +114,16 @@ def kernel_work(cfg, active, gather=True):
     return w
 
 
+def single_launch_work(cfg, active):
+    """Work of the single-launch layer: the whole layer's flops and the bytes of every operand the
+    separate launches read and write (each once), less the router-weight transpose (the single
+    launch reads the router weights K-major as given) and the tile lists (built in LDS)."""
+    w = kernel_work(cfg, active, True)
+    fl = sum(v[0] for k, v in w.items() if not k.endswith(("router_transpose", "build_tiles")))
+    by = sum(v[1] for k, v in w.items() if not k.endswith(("router_transpose", "build_tiles")))
+    return {"layer/layer_decode_bf16": (fl, by)}
+
+
 def variant_free(name):
     """Kernel name without its tile-variant suffix (the work model does not depend on it)."""
     for suf in ("_m32", "_m128", "_m256"):
@@ -143,8 +157,12 @@ def main():
     ex = make_expert_weights(cfg, dev)
     sh = make_expert_weights(cfg, dev, shared=True) if cfg.I_shared else None
     clean = lambda d: None if d is None else {k: v for k, v in d.items() if v is not None}  # noqa: E731
+    if args.single_launch and not (cfg.dtype == "bf16" and cfg.P <= SMALL_PERM_PAIRS and cfg.E % 8 == 0):
+        print(f"bench.py: --single-launch takes bf16 layers with T*K <= {SMALL_PERM_PAIRS} "
+              f"({cfg.name} is {cfg.dtype}, T*K = {cfg.P})", file=sys.stderr)
+        sys.exit(2)
     layer = MoELayer(cfg, w_r.to(dev), None if bias is None else bias.to(dev), clean(ex), clean(sh), dev,
-                     gather=not args.x_perm)
+                     gather=not args.x_perm, fused=args.single_launch)
     xd = x.to(dev)
     stream = torch.cuda.current_stream()
 
@@ -168,6 +186,8 @@ def main():
     stages = [("route", lambda: layer.route(xd)), ("permute", lambda: layer.permute(xd)),
               ("ffn", lambda: layer.expert_ffn(xd)), ("shared", lambda: layer.shared_ffn(xd)),
               ("combine", layer.combine)]
+    if args.single_launch:
+        stages = [("layer", lambda: layer(xd))]
     B.profile_enable(True)
     prof = {}
     for _ in range(args.steps):
@@ -186,7 +206,7 @@ def main():
     tokens_s = cfg.T / (ms * 1e-3)
     dtype = cfg.dtype
     active = int((layer.counts > 0).sum().item())
-    work = kernel_work(cfg, active, layer.gather)
+    work = single_launch_work(cfg, active) if args.single_launch else kernel_work(cfg, active, layer.gather)
     kernels = {}
     for k, (tot_ms, n) in prof.items():
         fl, by = work.get(variant_free(k), (0.0, 0.0))
@@ -229,7 +249,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "K": cfg.K,
                    "I_shared": cfg.I_shared, "output": cfg.out, "global_batch": cfg.T, "seq_len": cfg.T,
                    "parallelism": "single-gpu",
-                   "linear1_input": "x_perm copy" if args.x_perm else "token rows gathered in place"},
+                   "linear1_input": "x_perm copy" if args.x_perm else "token rows gathered in place",
+                   "launches": "one (moe_layer_decode)" if args.single_launch else "one per stage"},
         "tokens_per_s": round(tokens_s, 1),
         "mfma_peak_frac": round(tflops / PEAK[dtype], 4),
         "active_experts": active,

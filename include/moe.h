@@ -95,8 +95,8 @@ typedef struct moe_config {
  * layers). */
 moe_status moe_check_config(const moe_config* cfg);
 
-/* Bytes of device workspace that moe_route, moe_permute and moe_expert_ffn (routed and
- * shared) need for this config; 0 if the config is invalid. */
+/* Bytes of device workspace that moe_route, moe_permute, moe_expert_ffn (routed and shared) and
+ * moe_layer_decode need for this config; 0 if the config is invalid. */
 size_t moe_workspace_size(const moe_config* cfg);
 
 /* moe_route -- router projection, scores and (grouped) top-K.
@@ -231,6 +231,40 @@ moe_status moe_expert_ffn_gather(const moe_config* cfg, int32_t n_experts, int32
 moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const float* topk_weights,
                        const void* y_perm, const void* y_shared, void* out, void* stream);
 
+/* moe_layer_decode -- the whole layer (moe_route, moe_permute, moe_expert_ffn_gather for the
+ * routed experts, moe_expert_ffn for the shared expert, moe_combine) in one kernel launch, for
+ * decode-sized bf16 batches. The persistent-kernel design of "MoE 优化的探索：从 MiniMax-01、Comet、
+ * FlashMoE 到 DeepSeek-V4" (wqh011128.github.io, 4.1-4.7) and the fused dispatch-to-combine kernel
+ * of "DeepGEMM质变：从GEMM库到统一LLM计算原语平台" (itsolotime.com, 1.2), on one GPU: the
+ * workgroups pull router, top-K, permutation, GEMM-tile and combine tasks in a fixed order and
+ * hand results over through counters in the workspace.
+ *   Supported: dtype MOE_BF16, T*K <= 4096, E a multiple of 8 (MOE_ERR_UNSUPPORTED otherwise,
+ *   before any device call).
+ *   x, bias             as moe_route (bf16 x [T,H]; bias [E] fp32 or NULL)
+ *   w_router_t          device [E,H] bf16: the router weights K-major (W_r transposed, the layout
+ *                       of the expert weights), z[t][e] = sum_h x[t][h] w_router_t[e][h]
+ *   w13, w2             routed experts as moe_expert_ffn with n_experts = E, inter = I (bf16)
+ *   shared_w13, shared_w2  the shared expert (one expert, inter = I_shared), NULL iff I_shared == 0
+ *   topk_ids, topk_weights, counts, offsets, sorted_pair, pair_pos
+ *                       out: as moe_route and moe_permute
+ *   y_perm              device [T*K,H] bf16 out: the routed expert rows, as moe_expert_ffn_gather
+ *   y_shared            device [T,H] bf16 out: the shared expert rows, NULL iff I_shared == 0
+ *   out                 device [T,H] out, of type cfg->out_dtype, as moe_combine
+ * Every step computes what the separate entry points compute; the router sums its fp32 MFMA
+ * products in other K pieces than moe_route's, so logits, and through them near-tie selections,
+ * may differ from moe_route's in the last bits. The result is deterministic.
+ * The workgroups wait for one another's results; the layer completes with any number of them
+ * resident, but a wait that runs past about a second (the device held by other work all that
+ * time) sets device error code 2 and the layer's outputs are then undefined.
+ * The workspace (moe_workspace_size) needs no initialisation; a workspace serves one call at a
+ * time (calls in flight together on one workspace race). The call may be captured in a HIP
+ * graph. */
+moe_status moe_layer_decode(const moe_config* cfg, const void* x, const void* w_router_t, const float* bias,
+                            const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
+                            int32_t* topk_ids, float* topk_weights, int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_pair, int32_t* pair_pos, void* y_perm, void* y_shared, void* out,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* moe_quantize_fp8 -- e4m3 row quantisation of bf16 rows (the shared expert's input in the
  * fp8 layer): per row per 128 columns, scale = absmax/448 (fp32), code = e4m3(v / scale),
  * round to nearest even, saturating; an all-zero block gets scale 0 and codes 0.
@@ -251,7 +285,8 @@ moe_status moe_quantize_mx(int32_t rows, int32_t cols, const void* in, uint8_t* 
 
 /* Reads (and clears) the device error word kept at the start of `ws`, waiting for `stream`.
  * *code = 0 when no kernel flagged bad data since the last read; otherwise the returned
- * status is MOE_ERR_DEVICE and *code says what: 1 = expert id out of range in moe_permute. */
+ * status is MOE_ERR_DEVICE and *code says what (bits): 1 = expert id out of range in moe_permute,
+ * 2 = a wait of moe_layer_decode gave up. */
 moe_status moe_get_device_error(void* ws, int32_t* code, void* stream);
 
 /* Static text for a status code. */

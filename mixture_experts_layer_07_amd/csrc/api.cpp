@@ -339,6 +339,53 @@ moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const flo
   return MOE_OK;
 }
 
+moe_status moe_layer_decode(const moe_config* cfg, const void* x, const void* w_router_t, const float* bias,
+                            const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
+                            int32_t* topk_ids, float* topk_weights, int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_pair, int32_t* pair_pos, void* y_perm, void* y_shared, void* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(checked_config(cfg));
+  const moe_config& c = *cfg;
+  std::string why;
+  if (!decode_supported(c, &why)) return fail(MOE_ERR_UNSUPPORTED, "moe_layer_decode: " + why);
+  if (!x || !w_router_t || !w13 || !w2 || !topk_ids || !topk_weights || !counts || !offsets || !sorted_pair ||
+      !pair_pos || !y_perm || !out)
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: NULL buffer");
+  const bool sh = c.I_shared > 0;
+  if (sh && (!shared_w13 || !shared_w2 || !y_shared))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: I_shared > 0 needs shared_w13, shared_w2 and y_shared");
+  if (!sh && (shared_w13 || shared_w2 || y_shared))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: shared expert buffers given with I_shared == 0");
+  WsLayout L;
+  MOE_TRY(check_ws(c, ws, ws_bytes, &L));
+  MOE_TRY(ensure_device());
+  DecodeCall d;
+  d.c = c;
+  d.x = x;
+  d.w_router = w_router_t;
+  d.bias = bias;
+  d.w13 = w13;
+  d.w2 = w2;
+  d.sh_w13 = shared_w13;
+  d.sh_w2 = shared_w2;
+  d.ids = topk_ids;
+  d.weights = topk_weights;
+  d.counts = counts;
+  d.offsets = offsets;
+  d.sorted_pair = sorted_pair;
+  d.pair_pos = pair_pos;
+  d.y_perm = y_perm;
+  d.y_shared = y_shared;
+  d.out = out;
+  d.err = at<int32_t>(ws, L.err);
+  d.ctrl = at<int32_t>(ws, L.dctrl);
+  d.logits = at<float>(ws, L.dlogits);
+  d.h = at<void>(ws, L.h);
+  d.h_shared = at<void>(ws, L.dhsh);
+  MOE_HIP(launch_layer_decode(d, static_cast<hipStream_t>(stream)), "layer_decode");
+  return MOE_OK;
+}
+
 moe_status moe_quantize_fp8(int32_t rows, int32_t cols, const void* in, uint8_t* codes,
                             float* scales, void* stream) {
   if (rows < 0 || cols < 128 || cols % 128)

@@ -13,6 +13,32 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Cache-policy bits of a device-scope store (sc1): the encoding the compiler gives an agent-scope
+// atomic store. Such a store, once complete (its vmcnt retired), is visible to every XCD, so a
+// consumer on another XCD that acquires at agent scope (its caches invalidated) reads it without
+// the producer writing back its L2.
+constexpr int kCpolSc1 = 16;
+
+// Store of one 32-bit value, as an agent-scope relaxed atomic store (the device-scope sc1 store)
+// when SC1, else a plain store.
+template <bool SC1, class T>
+__device__ __forceinline__ void store_dev(T* p, T v) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  if constexpr (SC1)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+// threadIdx.x through an empty asm: values derived from it are formed where they are used, instead
+// of being hoisted out of a caller's loop and held in registers across everything else it runs
+// (the single-launch layer kernel runs many kinds of task in one loop).
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Round to nearest even (inputs here are never NaN).

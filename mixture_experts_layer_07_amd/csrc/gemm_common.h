@@ -276,6 +276,11 @@ __device__ __forceinline__ void dma_wait_and_barrier() {
 // compiler's own wait insertion accounts for it.
 __host__ __device__ constexpr int f8_wait_lgkm0_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 
+// Arguments of the two grouped GEMMs of one expert FFN call (kernels_ffn.hip). The fp32 kernels
+// set their own operands; an MX Linear-1 with gathered rows reads x_scale_grouped, which the
+// caller fills (k_gather_scale_words).
+void ffn_gemm_args(const FfnArgs& a, GemmArgs& g1, GemmArgs& g2);
+
 // Declared launchers (kernels_gemm_*.hip)
 hipError_t launch_gemm_bf16(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmArgs& g1, const GemmArgs& g2, int variant, int cus, hipStream_t s);

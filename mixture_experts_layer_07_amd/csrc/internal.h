@@ -24,9 +24,13 @@ namespace moe {
 //   hscale   [max_rows][max_I/128] fp32 (fp8 layer) / [max_I/128][rows] E8M0 words (MX layer)
 //   xscale   [H/128][T*K] E8M0 words (MX layer): the activation scales of a gathered Linear-1 in
 //            grouped row order
+//   the single-launch decode layer's regions (bf16 layers with T*K <= kSmallPermPairs, else empty):
+//   dctrl    kDecodeCtrlInts int32 control block (task counters, flags, the m-tile prefix)
+//   dlogits  [S][T][E] fp32 partial router logits (S = decode_router_splits)
+//   dhsh     [T][I_shared] bf16 SwiGLU output of the shared expert (the routed one is in h)
 struct WsLayout {
   size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, part = 0, h = 0, hscale = 0, xscale = 0,
-         total = 0;
+         dctrl = 0, dlogits = 0, dhsh = 0, total = 0;
   int route_splits = 1;
   int perm_blocks = 0;
 };
@@ -38,6 +42,7 @@ constexpr int kTileMetaInts = 2048;  // tile metadata of the expert GEMMs (prefi
 // moe_permute_noalloc: its scratch (error word + per-block histogram and bases) in a static device
 // array of this many bytes; the histogram and bases take 2 * ceil(P / 256) * E * 4 of them.
 constexpr size_t kNoAllocScratchBytes = (size_t(2) << 20) + 256;
+constexpr int kDecodeCtrlInts = 2048;  // control block of the single-launch decode layer
 
 // Validation; returns MOE_OK or the failure status with a reason in *why.
 moe_status check_routing(const moe_config* c, std::string* why);
@@ -48,6 +53,10 @@ int channel_multiple(int dtype);
 WsLayout layout(const moe_config& c);
 // Router split-K factor chosen from the shape (deterministic, host-side).
 int route_splits(const moe_config& c);
+// Whether moe_layer_decode takes this (valid) config, with the reason if not.
+bool decode_supported(const moe_config& c, std::string* why);
+// Splits of H in the single-launch decode layer's router (deterministic, host-side).
+int decode_router_splits(const moe_config& c);
 
 // ---------------------------------------------------------------- profiling
 bool profiling_enabled();
@@ -128,6 +137,32 @@ struct FfnArgs {
   float* part = nullptr;      // workspace, partial tiles of K-split GEMM tiles
 };
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s);
+// single-launch decode layer
+struct DecodeCall {
+  moe_config c;
+  const void* x = nullptr;
+  const void* w_router = nullptr;
+  const float* bias = nullptr;
+  const void* w13 = nullptr;
+  const void* w2 = nullptr;
+  const void* sh_w13 = nullptr;
+  const void* sh_w2 = nullptr;
+  int32_t* ids = nullptr;
+  float* weights = nullptr;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* sorted_pair = nullptr;
+  int32_t* pair_pos = nullptr;
+  void* y_perm = nullptr;
+  void* y_shared = nullptr;
+  void* out = nullptr;
+  int32_t* err = nullptr;     // workspace
+  int32_t* ctrl = nullptr;    // workspace
+  float* logits = nullptr;    // workspace
+  void* h = nullptr;          // workspace
+  void* h_shared = nullptr;   // workspace
+};
+hipError_t launch_layer_decode(const DecodeCall& d, hipStream_t s);
 // combine
 hipError_t launch_combine(const moe_config& c, const int32_t* pair_pos, const float* w,
                           const void* y_perm, const void* y_shared, void* out, hipStream_t s);

@@ -143,10 +143,10 @@ static hipError_t build_tiles(const FfnArgs& a, int BM, int32_t* tp, hipStream_t
 
 static int round8(int v) { return ((v + 7) / 8) * 8; }
 
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
-  const int cus = dev_info().cus;
+void ffn_gemm_args(const FfnArgs& a, GemmArgs& g1, GemmArgs& g2) {
   const int H = a.H, I = a.I;
-  GemmArgs g1{}, g2{};
+  g1 = GemmArgs{};
+  g2 = GemmArgs{};
   g1.offsets = g2.offsets = a.offsets;
   // Linear-1 may gather its rows from the activations; Linear-2 reads h in grouped order
   g1.a_rows = a.x_rows_index;
@@ -155,10 +155,12 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
   g2.a_rows = nullptr;
   g2.a_div = g2.a_limit = 1;
   g1.tp = g2.tp = a.tiles;
-  g1.queue = a.tiles + kTileQueueOffset;
-  g2.queue = a.tiles + kTileQueueOffset + kQueues;
-  g1.split_cnt = a.tiles + kSplitCntOffset;
-  g2.split_cnt = a.tiles + kSplitCntOffset + kMaxSplitItems;
+  if (a.tiles) {
+    g1.queue = a.tiles + kTileQueueOffset;
+    g2.queue = a.tiles + kTileQueueOffset + kQueues;
+    g1.split_cnt = a.tiles + kSplitCntOffset;
+    g2.split_cnt = a.tiles + kSplitCntOffset + kMaxSplitItems;
+  }
   g1.part = g2.part = a.part;  // the two GEMMs run one after the other on the stream
   g1.n_exp = g2.n_exp = a.n_exp;
   // Linear-1 (gate + up) with the SwiGLU epilogue: [rows,H] x [2I,H]^T -> h [rows,I]
@@ -171,35 +173,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
   g2.N_out = H;
   g2.Nb = H;
   g2.glu_I = 0;
-  hipError_t e;
-  if (a.dtype == MOE_F32) {
-    const size_t es = 4;
-    g1.A = static_cast<const uint8_t*>(a.x);
-    g1.lda = (size_t)H * es;
-    g1.B = static_cast<const uint8_t*>(a.w13);
-    g1.ldb = (size_t)H * es;
-    g1.b_exp = (size_t)2 * I * H * es;
-    g1.C = static_cast<uint8_t*>(a.h);
-    g1.ldc = (size_t)I * es;
-    g1.n_tiles_n = (I + 63) / 64;
-    g2.A = static_cast<const uint8_t*>(a.h);
-    g2.lda = (size_t)I * es;
-    g2.B = static_cast<const uint8_t*>(a.w2);
-    g2.ldb = (size_t)I * es;
-    g2.b_exp = (size_t)H * I * es;
-    g2.C = static_cast<uint8_t*>(a.y);
-    g2.ldc = (size_t)H * es;
-    g2.n_tiles_n = (H + 63) / 64;
-    if ((e = build_tiles(a, 64, a.tiles, s)) != hipSuccess) return e;
-    const int grid = round8(cus * 2);
-    if ((e = timed_launch("gemm_f32_gateup_swiglu", s, [&] {
-           hipLaunchKernelGGL(k_gemm_f32<true>, dim3(grid), dim3(256), 0, s, g1);
-         })) != hipSuccess)
-      return e;
-    return timed_launch("gemm_f32_down", s, [&] {
-      hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid), dim3(256), 0, s, g2);
-    });
-  }
+  if (a.dtype == MOE_F32) return;  // (the fp32 kernels set their own operands)
   const bool fp8 = a.dtype == MOE_FP8_E4M3, mx = a.dtype == MOE_MXFP4;
   const size_t es = fp8 || mx ? 1 : 2;  // bytes per activation element
   const size_t ws_ = mx ? 1 : es * 2;   // bytes per two weight elements
@@ -235,18 +209,9 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
   }
   if (mx) {
     // [K/128][rows] words: the scale arrays' row counts. The MX kernels read activation scales in
-    // grouped row order; a gathered Linear-1 gets its rows' scales gathered first.
-    if (a.x_rows_index) {
-      const int groups = H / 128;
-      const dim3 grid((a.n_rows + 255) / 256, groups < 8 ? groups : 8);
-      if ((e = timed_launch("gather_scales_mx", s, [&] {
-             hipLaunchKernelGGL(k_gather_scale_words, grid, dim3(256), 0, s, a.x_rows_index, a.x_rows_div,
-                                a.x_rows_limit, static_cast<const uint32_t*>(a.x_scale),
-                                static_cast<uint32_t*>(a.x_scale_grouped), a.n_rows, groups);
-           })) != hipSuccess)
-        return e;
-      g1.a_scale = static_cast<const float*>(a.x_scale_grouped);
-    }
+    // grouped row order; a gathered Linear-1 reads its rows' scales gathered first
+    // (k_gather_scale_words into x_scale_grouped).
+    if (a.x_rows_index) g1.a_scale = static_cast<const float*>(a.x_scale_grouped);
     g1.a_scale_ld = a.n_rows;
     g1.b_scale_ld = 2 * I;
     g1.b_scale_exp = (size_t)(H / 128) * 2 * I;
@@ -254,6 +219,53 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
     g2.a_scale_ld = a.n_rows;
     g2.b_scale_ld = H;
     g2.b_scale_exp = (size_t)(I / 128) * H;
+  }
+}
+
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
+  const int cus = dev_info().cus;
+  const int H = a.H, I = a.I;
+  GemmArgs g1, g2;
+  ffn_gemm_args(a, g1, g2);
+  hipError_t e;
+  if (a.dtype == MOE_F32) {
+    const size_t es = 4;
+    g1.A = static_cast<const uint8_t*>(a.x);
+    g1.lda = (size_t)H * es;
+    g1.B = static_cast<const uint8_t*>(a.w13);
+    g1.ldb = (size_t)H * es;
+    g1.b_exp = (size_t)2 * I * H * es;
+    g1.C = static_cast<uint8_t*>(a.h);
+    g1.ldc = (size_t)I * es;
+    g1.n_tiles_n = (I + 63) / 64;
+    g2.A = static_cast<const uint8_t*>(a.h);
+    g2.lda = (size_t)I * es;
+    g2.B = static_cast<const uint8_t*>(a.w2);
+    g2.ldb = (size_t)I * es;
+    g2.b_exp = (size_t)H * I * es;
+    g2.C = static_cast<uint8_t*>(a.y);
+    g2.ldc = (size_t)H * es;
+    g2.n_tiles_n = (H + 63) / 64;
+    if ((e = build_tiles(a, 64, a.tiles, s)) != hipSuccess) return e;
+    const int grid = round8(cus * 2);
+    if ((e = timed_launch("gemm_f32_gateup_swiglu", s, [&] {
+           hipLaunchKernelGGL(k_gemm_f32<true>, dim3(grid), dim3(256), 0, s, g1);
+         })) != hipSuccess)
+      return e;
+    return timed_launch("gemm_f32_down", s, [&] {
+      hipLaunchKernelGGL(k_gemm_f32<false>, dim3(grid), dim3(256), 0, s, g2);
+    });
+  }
+  const bool fp8 = a.dtype == MOE_FP8_E4M3, mx = a.dtype == MOE_MXFP4;
+  if (mx && a.x_rows_index) {
+    const int groups = H / 128;
+    const dim3 grid((a.n_rows + 255) / 256, groups < 8 ? groups : 8);
+    if ((e = timed_launch("gather_scales_mx", s, [&] {
+           hipLaunchKernelGGL(k_gather_scale_words, grid, dim3(256), 0, s, a.x_rows_index, a.x_rows_div,
+                              a.x_rows_limit, static_cast<const uint32_t*>(a.x_scale),
+                              static_cast<uint32_t*>(a.x_scale_grouped), a.n_rows, groups);
+         })) != hipSuccess)
+      return e;
   }
   // Tile shape from the mean rows per expert (a host-side choice; the API has no knob): large M
   // tiles when experts are well filled (weights then stream once per n-tile) and the large tiles

@@ -1,0 +1,567 @@
+// Single-launch decode layer (bf16): router, top-K, permutation, the routed and shared experts'
+// Linear-1 and Linear-2, and the weighted combine in one persistent kernel.
+//
+// The persistent-kernel idea is FlashMoE's ("MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到
+// DeepSeek-V4", wqh011128.github.io, 4.1-4.7: one launch, blocks that pull ready tasks, tile-sized
+// tasks) and MegaMoE's ("DeepGEMM质变：从GEMM库到统一LLM计算原语平台", itsolotime.com, 1.2: dispatch,
+// Linear-1, SwiGLU, Linear-2 and combine fused in one kernel), without the communication: on one
+// GPU what it removes is the chain of small launches of a decode-sized layer and the drains
+// between them.
+//
+// Work is a fixed sequence of segments; every workgroup walks them in order, pulling tasks from
+// one counter per segment, and a task waits only for tasks of earlier segments:
+//   0 router     32 x 256 tiles of the router GEMM z = x W_r (K-major W_r) over a piece of H:
+//                partial logits, fp32 (the grouped-GEMM tile code with one "expert")
+//   1 shared L1  32 x 256 tiles of the shared expert's gate/up GEMM with SwiGLU (reads x only)
+//   2 top-K      one token: waits for the router tiles of its 32-token block
+//   3 permute    one task: the one-workgroup counting sort, then the m-tile prefix of the
+//                routed experts; publishes "routing ready"
+//   4 routed L1  32 x 256 tiles over the expert-grouped pairs (rows gathered from x in place)
+//   5 shared L2  waits for the shared L1 tiles of its m-tile
+//   6 routed L2  waits for the L1 tiles of its expert m-tile
+//   7 combine    token x 2048-channel block: waits for every Linear-2 tile
+// Tasks are pulled in list order (expert-major for the GEMMs), so the Linear-1 tiles finish
+// roughly in the order the Linear-2 tiles are pulled and Linear-2 rarely waits. A workgroup moves
+// to the next segment only once every task of the current one has been pulled, and a task waits
+// only on tasks of earlier segments, which some running workgroup has pulled; so the layer
+// completes with any number of resident workgroups (by induction over the segments). Each wait is
+// bounded all the same: past the limit the workgroup sets the device error word (code 2) and a
+// kernel-wide abort flag, and every workgroup then runs to its end without waiting.
+//
+// Hand-offs between workgroups: every result another workgroup reads (partial logits, ids and
+// weights, the permutation, the m-tile prefix, h, y) is written with device-scope stores (sc1, the
+// encoding of an agent-scope atomic store), which are visible to every XCD once complete; the
+// producer waits for its stores (s_waitcnt), the workgroup meets at a barrier and one thread
+// increments a counter. The consumer polls the counter with agent-scope atomic loads and acquires
+// at agent scope (its L1 and L2 invalidated, so no stale line of an earlier call is read) before
+// reading. A release fence would do the producer's part as well, but it writes back the whole L2
+// of the XCD and costs a workgroup about as long as streaming a few hundred KB, once per tile.
+// Linear-2 completions are counted once per workgroup, as it leaves that segment (only the
+// combine waits for them, and for all of them). A workgroup entering Linear-2 reads every
+// Linear-1 m-tile counter once; a Linear-2 tile whose m-tile was then complete does not poll.
+// Every result is computed by one workgroup in a fixed order, so the layer is deterministic.
+//
+// The control block (counters, flags, the routed m-tile prefix) sits in the workspace. Every
+// launch carries a 64-bit epoch, unique per host call. If the block does not hold the launch's
+// epoch yet, workgroup 0 clears the counters and then publishes the epoch, and the other
+// workgroups wait for it before touching a counter; the last workgroup to finish clears the
+// counters again. A replay of a captured launch (same epoch) thus finds them cleared by the
+// previous replay, and a fresh workspace needs no initialisation.
+#include <atomic>
+#include <chrono>
+#include <map>
+#include <mutex>
+#include <random>
+
+#include "combine_rows.h"
+#include "gemm_bf16_tile.h"
+#include "perm_small.h"
+#include "route_topk.h"
+
+namespace moe {
+
+namespace dec {
+constexpr int kSegs = 8;
+enum Seg { kRouter = 0, kSh1, kTopk, kPerm, kL1, kSh2, kL2, kComb };
+constexpr int kMaxTokBlocks = kSmallPermPairs / 32;  // 32-token router m-tiles (T <= P <= 4096)
+constexpr int kMaxMTiles = kSmallPermPairs / 32 + kMaxExperts;
+// control block (int32 words)
+constexpr int kQ = 0;                              // [kSegs] task counters
+constexpr int kReady = kQ + kSegs;                 // routing outputs and the m-tile prefix written
+constexpr int kTopkDone = kReady + 1;              // top-K tasks done
+constexpr int kL2Done = kTopkDone + 1;             // Linear-2 tiles done (routed and shared)
+constexpr int kAbort = kL2Done + 1;                // a wait ran past its limit
+constexpr int kExit = kAbort + 1;                  // workgroups finished
+constexpr int kShOff = kExit + 1;                  // offsets {0, T} of the one-"expert" GEMMs
+constexpr int kRouterDone = 32;                    // [kMaxTokBlocks] router tiles done per m-tile
+constexpr int kL1Done = kRouterDone + kMaxTokBlocks;  // [kMaxMTiles] routed L1 tiles per m-tile
+constexpr int kL1sDone = kL1Done + kMaxMTiles;        // [kSmallPermPairs / 32] shared L1 per m-tile
+constexpr int kTp = kL1sDone + kSmallPermPairs / 32;  // [kMaxExperts + 1] routed m-tile prefix
+constexpr int kClear = kTp + kMaxExperts + 1;         // words cleared at the start
+constexpr int kEpoch = (kClear + 1) & ~1;             // 64-bit launch epoch
+static_assert(kShOff + 2 <= kRouterDone, "control block layout");
+static_assert(kEpoch + 2 <= kDecodeCtrlInts, "control block too small");
+constexpr unsigned long long kWaitLimit = 200000000ull;  // 2 s of the 100 MHz real-time counter
+}  // namespace dec
+
+struct DecodeArgs {
+  TopkParams tk;          // tk.splits = router K pieces S
+  const float* bias;      // [E] or nullptr
+  int T, H, E, K;
+  int mts, nyb;           // 32-token m-tiles, combine blocks per token
+  int has_shared, out_f32;
+  unsigned long long epoch;
+  float* logits;          // [S][T][E] partial logits
+  int32_t* ids;
+  float* weights;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  int32_t* err;           // device error word
+  int32_t* ctrl;          // control block
+  GemmArgs gr;            // router GEMM: x [T,H] x W_r^T [E,H] -> logits (C of piece 0)
+  GemmArgs g1, g2;        // routed Linear-1 (gathered rows) and Linear-2
+  GemmArgs s1, s2;        // shared expert
+  const uint8_t* y;       // routed expert rows [P][H] bf16
+  const uint8_t* ysh;     // shared expert rows [T][H] bf16 or nullptr
+  uint8_t* out;           // [T][H] fp32 or bf16
+};
+
+// ---------------------------------------------------------------- hand-offs
+// All threads call. Hand-off of results written with device-scope stores: every wave's stores
+// have completed before the barrier, then one counter increment.
+__device__ __forceinline__ void handoff_add(int32_t* p, int v) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// All threads call. Sets ok[m] = 1 for every routed m-tile m < n whose Linear-1 tiles are all done
+// (counter == per), then acquires: their h rows may then be read without polling.
+__device__ __forceinline__ void snapshot_l1(const int32_t* ctrl, int n, int per, int* ok) {
+  if (threadIdx.x < 64) {
+    for (int m = threadIdx.x; m < n; m += 64)
+      ok[m] = __hip_atomic_load(ctrl + dec::kL1Done + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= per;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// Polling: every poll is a read at the memory side (agent scope), and hundreds of workgroups may
+// wait on one counter at once (for the routing, at the end for the last Linear-2 tiles), so the
+// interval between polls doubles from about 0.25 us up to about 4 us; a wait gives up after
+// kWaitLimit of the 100 MHz real-time counter.
+__device__ __forceinline__ void poll_pause(int units) {
+  for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(8);  // (about 512 cycles each)
+}
+
+// All threads call. Waits until *p >= target (thread 0 polls), then acquires. Returns false
+// (uniformly) if the wait gave up or another workgroup's did.
+__device__ __forceinline__ bool wait_geq(const DecodeArgs& a, int idx, int target, int* s_flag) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    int32_t* p = a.ctrl + idx;
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      int units = 1;
+      do {
+        poll_pause(units);
+        if (units < 16) {
+          units *= 2;
+        } else {  // a long wait: has another workgroup given up, or has this one waited too long?
+          if (__hip_atomic_load(a.ctrl + dec::kAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+            ok = 0;
+            break;
+          }
+          if (__builtin_amdgcn_s_memrealtime() - t0 > dec::kWaitLimit) {
+            ok = 0;
+            __hip_atomic_store(a.ctrl + dec::kAbort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(a.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+      } while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_flag[0] = ok;
+  }
+  __syncthreads();
+  const bool ok = __builtin_amdgcn_readfirstlane(s_flag[0]) != 0;
+  __syncthreads();
+  return ok;
+}
+
+// K piece p of S over KT steps: an even number of steps, at least two (S <= KT / 2).
+__device__ __forceinline__ int piece_k(int p, int S, int KT) { return (int)((long long)p * (KT / 2) / S) * 2; }
+
+// ---------------------------------------------------------------- combine task
+template <bool OF32>
+__device__ __forceinline__ void combine_task(const DecodeArgs& a, int task, int* spp, float* sw) {
+  const int t = task / a.nyb, yb = task - t * a.nyb;
+  switch (a.K) {
+    case 8: combine_block<8, false, OF32, 8, 1>(t, yb, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K, spp, sw); break;
+    case 2: combine_block<8, false, OF32, 2, 1>(t, yb, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K, spp, sw); break;
+    default: combine_block<8, false, OF32, 0, 1>(t, yb, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K, spp, sw);
+  }
+}
+
+// ---------------------------------------------------------------- the kernel
+template <bool OF32>
+__global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
+  __shared__ u32x4 sA0[m32::kStageA];
+  __shared__ u32x4 sA1[m32::kStageA];
+  __shared__ u32x4 sB0[w4::kStageB];
+  __shared__ u32x4 sB1[w4::kStageB];
+  __shared__ int s_tp[kMaxExperts + 1];
+  __shared__ int s_tps[2];
+  __shared__ int s_slot[4];
+  __shared__ int s_l1ok[dec::kMaxMTiles];
+  const int tid = threadIdx.x;
+  int32_t* ctrl = a.ctrl;
+  unsigned long long* epoch = reinterpret_cast<unsigned long long*>(ctrl + dec::kEpoch);
+
+  // start: unless the block holds this launch's epoch, workgroup 0 clears the counters and
+  // publishes the epoch; the others wait for it
+  if (blockIdx.x == 0) {
+    if (tid == 0)
+      s_slot[0] = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(s_slot[0])) {
+      for (int i = tid; i < dec::kClear; i += 256) store_dev<true>(ctrl + i, (int32_t)(i == dec::kShOff + 1 ? a.T : 0));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(epoch, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (tid == 0) {
+    int ok = 1;
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > dec::kWaitLimit) {  // (the counters were never cleared)
+        __hip_atomic_fetch_or(a.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      poll_pause(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_slot[1] = ok;
+  }
+  if (tid == 0) {
+    s_tps[0] = 0;
+    s_tps[1] = a.mts;
+  }
+  __syncthreads();
+  if (blockIdx.x != 0 && !__builtin_amdgcn_readfirstlane(s_slot[1])) return;
+
+  const SplitQueue sq0 = {0, 0, 1, 0, 0, 0};  // (whole work items: no hand-over of K pieces)
+  const int S = a.tk.splits;
+  const int rtiles = a.mts * a.gr.n_tiles_n;  // router tiles per K piece
+  bool routed = false;  // s_tp holds the routed m-tile prefix
+  bool l2_all = false;  // every Linear-2 tile is done (the combine may run)
+  bool alive = true;
+  int n_l2 = 0;    // Linear-2 tiles (routed and shared) done and not yet counted
+  bool snap = false;  // s_l1ok holds a snapshot of the Linear-1 m-tile counters
+  float* f0 = reinterpret_cast<float*>(sB0);
+  float* f1 = reinterpret_cast<float*>(sB1);
+
+  for (int seg = 0; seg < dec::kSegs && alive; ++seg) {
+    if ((seg == dec::kL1 || seg == dec::kL2 || seg == dec::kComb) && !routed) {
+      alive = wait_geq(a, dec::kReady, 1, s_slot);
+      if (!alive) break;
+      for (int i = tid; i <= a.E; i += 256) s_tp[i] = ctrl[dec::kTp + i];
+      __syncthreads();
+      routed = true;
+    }
+    int n = 0;
+    switch (seg) {
+      case dec::kRouter: n = rtiles * S; break;
+      case dec::kSh1: n = a.has_shared ? a.mts * a.s1.n_tiles_n : 0; break;
+      case dec::kTopk: n = a.T; break;
+      case dec::kPerm: n = 1; break;
+      case dec::kL1: n = s_tp[a.E] * a.g1.n_tiles_n; break;
+      case dec::kSh2: n = a.has_shared ? a.mts * a.s2.n_tiles_n : 0; break;
+      case dec::kL2: n = s_tp[a.E] * a.g2.n_tiles_n; break;
+      default: n = a.T * a.nyb; break;
+    }
+    for (;;) {
+      int task = n;
+      if (n > 0) {
+        if (tid == 0) s_slot[0] = atomicAdd(&ctrl[dec::kQ + seg], 1);
+        __syncthreads();
+        task = __builtin_amdgcn_readfirstlane(s_slot[0]);
+        __syncthreads();
+      }
+      if (task >= n) {
+        // leaving Linear-2: count this workgroup's Linear-2 tiles (and shared ones) as done
+        if (seg == dec::kL2 && n_l2 > 0) {
+          handoff_add(ctrl + dec::kL2Done, n_l2);
+          n_l2 = 0;
+        }
+        break;
+      }
+      WorkItem w;
+      w.tile = task;
+      w.piece = -1;
+      w.slot = w.first = 0;
+      w.k0 = 0;
+      if (seg == dec::kRouter) {
+        // piece p of H for router tile `tile`: its partial logits go to slice p
+        const int p = task / rtiles;
+        w.tile = task - p * rtiles;
+        const int KT = a.gr.K / 64;
+        w.k0 = piece_k(p, S, KT);
+        w.k1 = piece_k(p + 1, S, KT);
+        GemmArgs g = a.gr;
+        g.C += (size_t)p * a.T * a.E * 4;
+        m32_item<false, true, false, kCpolSc1>(g, s_tps, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        const TileInfo ti = decode_tile(w.tile, s_tps, a.gr, 32);
+        handoff_add(ctrl + dec::kRouterDone + ti.mt, 1);
+      } else if (seg == dec::kSh1) {
+        w.k1 = a.s1.K / 64;
+        m32_item<true, false, false, kCpolSc1>(a.s1, s_tps, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        const TileInfo ti = decode_tile(task, s_tps, a.s1, 32);
+        handoff_add(ctrl + dec::kL1sDone + ti.mt, 1);
+      } else if (seg == dec::kTopk) {
+        // token `task`: its router m-tile's every n-tile and piece must be done; the four waves
+        // stage the S partial logits in LDS (one round of loads), then wave 0 sums them in split
+        // order and selects
+        if (!(alive = wait_geq(a, dec::kRouterDone + task / 32, a.gr.n_tiles_n * S, s_slot))) break;
+        {
+          // loads in flight eight at a time (S * E / 4 <= 64 * 64: at most two rounds), then the
+          // LDS stores
+          const int E4 = a.E / 4, n4 = S * E4;
+          for (int i0 = 0; i0 < n4; i0 += 8 * 256) {
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int i = i0 + tid + 256 * u;
+              if (i < n4) {
+                const int sp = i / E4, c = i - sp * E4;
+                v[u] = reinterpret_cast<const f32x4*>(a.logits + ((size_t)sp * a.T + task) * a.E)[c];
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int i = i0 + tid + 256 * u;
+              if (i < n4) {
+                const int sp = i / E4, c = i - sp * E4;
+                reinterpret_cast<f32x4*>(sp < 32 ? f0 + sp * 256 : f1 + (sp - 32) * 256)[c] = v[u];
+              }
+            }
+          }
+        }
+        __syncthreads();
+        if (tid < 64) {
+          // the partial logits summed in split order, eight rows read ahead at a time
+          float z[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) z[j] = 0.f;
+          for (int s0 = 0; s0 < S; s0 += 8) {
+            float r[8][4];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int sp = s0 + u < S ? s0 + u : S - 1;
+              const float* row = sp < 32 ? f0 + sp * 256 : f1 + (sp - 32) * 256;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) r[u][j] = row[tid + 64 * j];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (s0 + u < S) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) z[j] += r[u][j];
+              }
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (tid + 64 * j >= a.E) z[j] = -INFINITY;
+          float* lw = reinterpret_cast<float*>(sA0);  // (4 KB: the selection's scratch)
+          topk_select<true>(z, a.bias, a.tk, a.ids, a.weights, task, lw, reinterpret_cast<int*>(lw + 256),
+                            reinterpret_cast<int*>(lw + 512), lw + 768);
+        }
+        handoff_add(ctrl + dec::kTopkDone, 1);
+      } else if (seg == dec::kPerm) {
+        if (!(alive = wait_geq(a, dec::kTopkDone, a.T, s_slot))) break;
+        int* off = reinterpret_cast<int*>(f1);
+        int* sbuf = off + 512;
+        perm_small_block<true>(a.ids, a.T * a.K, a.E, a.counts, a.offsets, a.sorted_pair, a.pair_pos, a.err,
+                               reinterpret_cast<uint16_t(*)[kMaxExperts]>(f0), off, sbuf);
+        __syncthreads();
+        // m-tile prefix of the routed experts (32-row tiles)
+        const int c = tid < a.E ? off[tid + 1] - off[tid] : 0;
+        int tot;
+        const int ex = block_exscan_256(c > 0 ? (c + 31) / 32 : 0, sbuf, &tot);
+        if (tid < a.E) store_dev<true>(ctrl + dec::kTp + tid, (int32_t)ex);
+        if (tid == 0) store_dev<true>(ctrl + dec::kTp + a.E, (int32_t)tot);
+        handoff_add(ctrl + dec::kReady, 1);
+      } else if (seg == dec::kL1) {
+        w.k1 = a.g1.K / 64;
+        m32_item<true, false, false, kCpolSc1>(a.g1, s_tp, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        const TileInfo ti = decode_tile(task, s_tp, a.g1, 32);
+        handoff_add(ctrl + dec::kL1Done + s_tp[ti.e] + ti.mt, 1);
+      } else if (seg == dec::kSh2) {
+        const TileInfo ti = decode_tile(task, s_tps, a.s2, 32);
+        if (!(alive = wait_geq(a, dec::kL1sDone + ti.mt, a.s1.n_tiles_n, s_slot))) break;
+        w.k1 = a.s2.K / 64;
+        m32_item<false, false, false, kCpolSc1>(a.s2, s_tps, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        ++n_l2;
+      } else if (seg == dec::kL2) {
+        const TileInfo ti = decode_tile(task, s_tp, a.g2, 32);
+        const int m = s_tp[ti.e] + ti.mt;
+        if (!snap) {
+          snapshot_l1(ctrl, s_tp[a.E], a.g1.n_tiles_n, s_l1ok);
+          snap = true;
+        }
+        if (!s_l1ok[m]) {
+          if (!(alive = wait_geq(a, dec::kL1Done + m, a.g1.n_tiles_n, s_slot))) break;
+          snapshot_l1(ctrl, s_tp[a.E], a.g1.n_tiles_n, s_l1ok);
+        }
+        w.k1 = a.g2.K / 64;
+        m32_item<false, false, false, kCpolSc1>(a.g2, s_tp, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        ++n_l2;
+      } else {
+        if (!l2_all) {
+          const int total = s_tp[a.E] * a.g2.n_tiles_n + (a.has_shared ? a.mts * a.s2.n_tiles_n : 0);
+          if (!(alive = wait_geq(a, dec::kL2Done, total, s_slot))) break;
+          l2_all = true;
+        }
+        combine_task<OF32>(a, task, reinterpret_cast<int*>(sA0), reinterpret_cast<float*>(sA0) + kMaxExperts);
+      }
+    }
+  }
+  // exit: the last workgroup out clears the counters for the next launch (every other workgroup's
+  // counter updates have completed before its exit increment: the wait orders them)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) s_slot[0] = __hip_atomic_fetch_add(ctrl + dec::kExit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(s_slot[0]) == (int)gridDim.x - 1) {
+    for (int i = tid; i < dec::kClear; i += 256)
+      if (i != dec::kShOff && i != dec::kShOff + 1) ctrl[i] = 0;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+// Launch epochs: a process-wide counter started at a random 64-bit value, so that the epoch word
+// a workspace holds from an earlier launch (or from whatever the memory held before) does not
+// match the new launch's.
+static unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> ctr{[] {
+    std::random_device rd;
+    unsigned long long v = ((unsigned long long)rd() << 32) ^ rd();
+    v ^= (unsigned long long)std::chrono::high_resolution_clock::now().time_since_epoch().count();
+    return v;
+  }()};
+  unsigned long long e;
+  do e = ++ctr; while (e == 0);
+  return e;
+}
+
+// One workgroup per resident slot: two per CU (the 32 x 256 GEMM tiles' LDS and registers allow
+// two), fewer if the occupancy query says so. (More would only queue behind the resident ones;
+// the layer does not need them all resident, see the top of this file.)
+static hipError_t decode_grid(const void* kernel, int* grid) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = cache.find(key);
+  if (it == cache.end()) {
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 256, 0);
+    if (e != hipSuccess) return e;
+    if (nb > 2) nb = 2;
+    const int g = nb * dev_info().cus;
+    if (g < 1) return hipErrorInvalidConfiguration;
+    it = cache.emplace(key, g).first;
+  }
+  *grid = it->second;
+  return hipSuccess;
+}
+
+hipError_t launch_layer_decode(const DecodeCall& d, hipStream_t s) {
+  const moe_config& c = d.c;
+  DecodeArgs a{};
+  a.bias = d.bias;
+  a.T = c.T;
+  a.H = c.H;
+  a.E = c.E;
+  a.K = c.K;
+  a.tk.T = c.T;
+  a.tk.E = c.E;
+  a.tk.K = c.K;
+  a.tk.splits = decode_router_splits(c);
+  a.tk.sigmoid = c.score_fn == MOE_SIGMOID;
+  a.tk.renorm = c.renorm;
+  a.tk.n_group = c.n_group;
+  a.tk.topk_group = c.topk_group;
+  a.tk.group_top2 = c.group_score == MOE_GROUP_TOP2_SUM;
+  a.tk.route_scale = c.route_scale;
+  a.mts = (c.T + 31) / 32;
+  a.nyb = (c.H / 8 + 255) / 256;
+  a.has_shared = c.I_shared > 0;
+  a.out_f32 = c.out_dtype == MOE_F32;
+  a.epoch = next_epoch();
+  a.logits = d.logits;
+  a.ids = d.ids;
+  a.weights = d.weights;
+  a.counts = d.counts;
+  a.offsets = d.offsets;
+  a.sorted_pair = d.sorted_pair;
+  a.pair_pos = d.pair_pos;
+  a.err = d.err;
+  a.ctrl = d.ctrl;
+  a.y = static_cast<const uint8_t*>(d.y_perm);
+  a.ysh = a.has_shared ? static_cast<const uint8_t*>(d.y_shared) : nullptr;
+  a.out = static_cast<uint8_t*>(d.out);
+  // router: one "expert" whose E weight rows are the K-major router weights; fp32 output
+  // (partial logits of one K piece per slice [T][E])
+  GemmArgs& r = a.gr;
+  r = GemmArgs{};
+  r.A = static_cast<const uint8_t*>(d.x);
+  r.lda = (size_t)c.H * 2;
+  r.B = static_cast<const uint8_t*>(d.w_router);
+  r.ldb = (size_t)c.H * 2;
+  r.b_exp = 0;
+  r.C = reinterpret_cast<uint8_t*>(d.logits);
+  r.ldc = (size_t)c.E * 4;
+  r.offsets = d.ctrl + dec::kShOff;
+  r.a_rows = nullptr;
+  r.a_div = r.a_limit = 1;
+  r.n_exp = 1;
+  r.K = c.H;
+  r.N_out = c.E;
+  r.Nb = c.E;
+  r.glu_I = 0;
+  r.n_tiles_n = (c.E + 255) / 256;
+  // routed experts: Linear-1 gathers its rows from x (row i = token sorted_pair[i] / K)
+  FfnArgs f;
+  f.dtype = MOE_BF16;
+  f.n_exp = c.E;
+  f.n_rows = c.T * c.K;
+  f.H = c.H;
+  f.I = c.I;
+  f.offsets = d.offsets;
+  f.x = d.x;
+  f.x_rows_index = d.sorted_pair;
+  f.x_rows_div = c.K;
+  f.x_rows_limit = c.T;
+  f.w13 = d.w13;
+  f.w2 = d.w2;
+  f.y = d.y_perm;
+  f.h = d.h;
+  ffn_gemm_args(f, a.g1, a.g2);
+  if (a.has_shared) {
+    // shared expert: one expert over the T rows of x; its offsets {0, T} are in the control block
+    FfnArgs fs;
+    fs.dtype = MOE_BF16;
+    fs.n_exp = 1;
+    fs.n_rows = c.T;
+    fs.H = c.H;
+    fs.I = c.I_shared;
+    fs.offsets = d.ctrl + dec::kShOff;
+    fs.x = d.x;
+    fs.w13 = d.sh_w13;
+    fs.w2 = d.sh_w2;
+    fs.y = d.y_shared;
+    fs.h = d.h_shared;
+    ffn_gemm_args(fs, a.s1, a.s2);
+  }
+  const void* kernel = a.out_f32 ? reinterpret_cast<const void*>(&k_layer_decode_bf16<true>)
+                                 : reinterpret_cast<const void*>(&k_layer_decode_bf16<false>);
+  int grid = 0;
+  hipError_t e = decode_grid(kernel, &grid);
+  if (e != hipSuccess) return e;
+  return timed_launch("layer_decode_bf16", s, [&] {
+    if (a.out_f32)
+      hipLaunchKernelGGL(k_layer_decode_bf16<true>, dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_layer_decode_bf16<false>, dim3(grid), dim3(256), 0, s, a);
+  });
+}
+
+}  // namespace moe

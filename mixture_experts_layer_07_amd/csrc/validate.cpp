@@ -85,6 +85,30 @@ int route_splits(const moe_config& c) {
   return want < nk ? want : nk;
 }
 
+bool decode_supported(const moe_config& c, std::string* why) {
+  auto no = [&](const char* msg) {
+    if (why) *why = msg;
+    return false;
+  };
+  if (c.dtype != MOE_BF16) return no("the single-launch decode layer is built for bf16 layers");
+  if ((int64_t)c.T * c.K > kSmallPermPairs) return no("the single-launch decode layer needs T*K <= 4096");
+  if (c.E % 8) return no("the single-launch decode layer needs E a multiple of 8");
+  if ((int64_t)c.T * c.H * 2 >= (int64_t(1) << 32)) return no("x above 4 GiB");
+  return true;
+}
+
+int decode_router_splits(const moe_config& c) {
+  // the router runs as 32 x 256 GEMM tiles cut into S pieces of H (an even number of 64-channel
+  // steps each): about 224 short tasks, so that the router's weights stream through many
+  // workgroups at once (it is on the critical path), while the top-K sums S partial logits per token
+  const int tiles = ((c.T + 31) / 32) * ((c.E + 255) / 256);
+  const int half_steps = c.H / 128;  // pieces of at least two 64-channel steps
+  int s = (224 + tiles - 1) / tiles;
+  if (s > half_steps) s = half_steps;
+  if (s > 64) s = 64;  // (the top-K stages at most 64 partial rows of 256 logits in LDS)
+  return s < 1 ? 1 : s;
+}
+
 WsLayout layout(const moe_config& c) {
   WsLayout L;
   const size_t T = (size_t)c.T, E = (size_t)c.E, H = (size_t)c.H;
@@ -117,6 +141,13 @@ WsLayout layout(const moe_config& c) {
   off = align256(off + (c.dtype == MOE_FP8_E4M3 || c.dtype == MOE_MXFP4 ? P * (maxI / 128) * 4 : 0));
   L.xscale = off;
   off = align256(off + (c.dtype == MOE_MXFP4 ? P * (H / 128) * 4 : 0));
+  const bool dec = decode_supported(c, nullptr);
+  L.dctrl = off;
+  off = align256(off + (dec ? (size_t)kDecodeCtrlInts * 4 : 0));
+  L.dlogits = off;
+  off = align256(off + (dec ? (size_t)decode_router_splits(c) * T * E * 4 : 0));
+  L.dhsh = off;
+  off = align256(off + (dec ? T * (size_t)c.I_shared * 2 : 0));
   L.total = off;
   return L;
 }

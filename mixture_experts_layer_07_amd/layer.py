@@ -1,6 +1,9 @@
 """One MoE layer forward on torch device buffers: the C-ABI calls in order.
 
 route -> permute -> expert FFN (routed experts, then the shared expert if any) -> combine.
+With fused=True (bf16 layers with T*K <= 4096) the whole layer is one call, moe_layer_decode: one
+kernel launch that fills the same buffers (it reads the router weights K-major, transposed once
+at construction).
 With gather=True (the default) the permute stage only builds the pair order (and, for fp8 and
 MX layers, quantises the T input rows once) and Linear-1 of the routed experts reads the token rows in
 place (moe_expert_ffn_gather); with gather=False the permute stage also writes the permuted
@@ -15,10 +18,11 @@ from .configs import LayerConfig
 
 class MoELayer:
     def __init__(self, cfg: LayerConfig, w_router, bias, experts, shared=None, device="cuda",
-                 gather=True):
+                 gather=True, fused=False):
         """experts / shared: dicts with w13, w2 (+ w13_scale, w2_scale for fp8 / mxfp4) on `device`."""
         self.cfg = cfg
-        self.gather = gather
+        self.gather = gather or fused
+        self.fused = fused
         self.c = B.make_config(cfg)
         B.moe_check_config(self.c)
         T, H, E, K, P = cfg.T, cfg.H, cfg.E, cfg.K, cfg.P
@@ -28,6 +32,9 @@ class MoELayer:
         self.quant = self.fp8 or self.mx   # experts read e4m3 codes plus scales
         dev = torch.device(device)
         self.w_router = w_router
+        # the single launch reads the router weights K-major ([E, H], as the expert weights are
+        # stored); transposed once here, as a weight-loading step
+        self.w_router_t = w_router.t().contiguous() if fused else None
         self.bias = bias
         self.experts = experts
         self.shared = shared if cfg.I_shared > 0 else None
@@ -41,12 +48,12 @@ class MoELayer:
         self.sorted_pair = torch.empty(P, **i32)
         self.pair_pos = torch.empty(P, **i32)
         self.x_perm = self.x_perm_scale = None
-        if not gather:
+        if not self.gather:
             self.x_perm = torch.empty((P, H), dtype=torch.uint8 if self.quant else act, device=dev)
             if self.quant:
                 self.x_perm_scale = self._scales(P, H, dev)
         self.xq = self.xq_scale = None
-        if self.quant and (gather or self.shared is not None):
+        if self.quant and (self.gather or self.shared is not None):
             # the e4m3 codes of the T input rows, read by the gathered Linear-1 and the shared expert
             self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
             self.xq_scale = self._scales(T, H, dev)
@@ -113,6 +120,14 @@ class MoELayer:
         B.moe_combine(self.c, self.pair_pos, self.topk_weights, self.y_perm, self.y_shared, self.out)
 
     def forward(self, x):
+        if self.fused:
+            ex, sh = self.experts, self.shared
+            B.moe_layer_decode(self.c, x, self.w_router_t, self.bias, ex["w13"], ex["w2"],
+                               None if sh is None else sh["w13"], None if sh is None else sh["w2"],
+                               self.topk_ids, self.topk_weights, self.counts, self.offsets,
+                               self.sorted_pair, self.pair_pos, self.y_perm, self.y_shared, self.out,
+                               self.ws)
+            return self.out
         self.route(x)
         self.permute(x)
         self.expert_ffn(x)

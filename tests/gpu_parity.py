@@ -65,7 +65,7 @@ def row_err(got, ref):
 class Case:
     """A layer config with its inputs on the GPU (expert weights drawn on `wdev`)."""
 
-    def __init__(self, cfg, bias=None, wdev="cpu", dev="cuda", gather=True):
+    def __init__(self, cfg, bias=None, wdev="cpu", dev="cuda", gather=True, fused=False):
         self.cfg = cfg
         self.dev = dev
         x, w_r, b = make_router_inputs(cfg)
@@ -81,7 +81,7 @@ class Case:
             self.sh = None
         clean = lambda d: None if d is None else {k: v for k, v in d.items() if v is not None}  # noqa: E731
         self.layer = MoELayer(cfg, w_r.to(dev), None if b is None else b.to(dev), clean(self.ex),
-                              clean(self.sh), dev, gather=gather)
+                              clean(self.sh), dev, gather=gather, fused=fused)
         self.xd = x.to(dev)
 
     def run(self):

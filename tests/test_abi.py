@@ -137,6 +137,25 @@ def test_entry_points_validate_before_device(lib):
     assert lib.moe_permute(pm, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, nm,
                            None) == INVALID                                  # MX without x_perm_scale
     assert lib.moe_get_device_error(None, ctypes.byref(ctypes.c_int32()), None) == INVALID
+    # the single-launch decode layer: shape support, NULL buffers and the shared-expert buffers
+    # (given iff I_shared > 0) are checked before any device call
+    dec = lambda pcfg, nb, **o: lib.moe_layer_decode(  # noqa: E731
+        pcfg, o.get("x", FAKE), FAKE, None, FAKE, FAKE, o.get("sw13", FAKE), o.get("sw2", FAKE), FAKE, FAKE,
+        FAKE, FAKE, FAKE, FAKE, FAKE, o.get("ysh", FAKE), FAKE, o.get("ws", FAKE), o.get("wsb", nb), None)
+    assert dec(pc, n, x=None) == INVALID
+    assert dec(pc, n, sw13=None) == INVALID
+    assert dec(pc, n, ysh=None) == INVALID
+    assert dec(pc, n, wsb=n - 1) == WORKSPACE
+    assert dec(pc, n, ws=None) == INVALID
+    c0 = cfg(3, T=64, H=256, I=128, E=16, K=4, n_group=4, topk_group=2, I_shared=0)
+    n0 = lib.moe_workspace_size(ctypes.byref(c0))
+    assert dec(ctypes.byref(c0), n0) == INVALID                  # shared buffers without a shared expert
+    assert dec(ctypes.byref(c0), n0, sw13=None, sw2=None, ysh=None, wsb=n0 - 1) == WORKSPACE
+    assert dec(ctypes.byref(cfg(3, T=1024, K=8)), n) == UNSUPPORTED   # T*K above 4096
+    assert "4096" in lib.moe_last_error().decode()
+    assert dec(p8, lib.moe_workspace_size(p8)) == UNSUPPORTED          # fp8 layer
+    c12 = cfg(3, T=64, H=256, I=128, E=12, K=4, n_group=4, topk_group=2, I_shared=128)
+    assert dec(ctypes.byref(c12), lib.moe_workspace_size(ctypes.byref(c12))) == UNSUPPORTED  # E % 8
     # logits-only routing reads only the routing fields: H, I and dtype are not checked
     cr = cfg(3, T=83, E=256, K=8, n_group=8, topk_group=4)
     cr.H, cr.I, cr.dtype = 0, 0, 9
