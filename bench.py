@@ -362,7 +362,10 @@ def bench_route(args, cfg):
 
 # Sources whose change invalidates a stored traffic measurement of a kernel.
 KERNEL_SOURCES = {
-    "gemm_bf16": ["kernels_gemm_bf16.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
+    "gemm_bf16": ["kernels_gemm_bf16.hip", "gemm_bf16_tile.h", "gemm_common.h", "kernels_ffn.hip", "device.h",
+                  "internal.h"],
+    "layer_decode": ["kernels_layer.hip", "gemm_bf16_tile.h", "gemm_common.h", "route_topk.h", "perm_small.h",
+                     "combine_rows.h", "kernels_ffn.hip", "device.h", "internal.h", "validate.cpp"],
     "gemm_fp8": ["kernels_gemm_fp8.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
     "gemm_mx": ["kernels_gemm_mx.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
     "gemm_f32": ["kernels_ffn.hip", "gemm_common.h", "device.h", "internal.h"],

@@ -232,19 +232,23 @@ moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const flo
                        const void* y_perm, const void* y_shared, void* out, void* stream);
 
 /* moe_layer_decode -- the whole layer (moe_route, moe_permute, moe_expert_ffn_gather for the
- * routed experts, moe_expert_ffn for the shared expert, moe_combine) in one kernel launch, for
- * decode-sized bf16 batches. The persistent-kernel design of "MoE 优化的探索：从 MiniMax-01、Comet、
- * FlashMoE 到 DeepSeek-V4" (wqh011128.github.io, 4.1-4.7) and the fused dispatch-to-combine kernel
- * of "DeepGEMM质变：从GEMM库到统一LLM计算原语平台" (itsolotime.com, 1.2), on one GPU: the
- * workgroups pull router, top-K, permutation, GEMM-tile and combine tasks in a fixed order and
- * hand results over through counters in the workspace.
- *   Supported: dtype MOE_BF16, T*K <= 4096, E a multiple of 8 (MOE_ERR_UNSUPPORTED otherwise,
- *   before any device call).
+ * routed experts, moe_expert_ffn for the shared expert, moe_combine; for MX layers also the MXFP8
+ * quantisation of x) in one kernel launch, for decode-sized batches. The persistent-kernel design
+ * of "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4" (wqh011128.github.io, 4.1-4.7)
+ * and the fused dispatch-to-combine kernel of "DeepGEMM质变：从GEMM库到统一LLM计算原语平台"
+ * (itsolotime.com, 1.2), on one GPU: the workgroups pull router, quantisation, top-K, GEMM-tile
+ * and combine tasks in a fixed order and hand results over through counters in the workspace.
+ *   Supported: dtype MOE_BF16 or MOE_MXFP4, T*K <= 4096, E a multiple of 8 (MOE_ERR_UNSUPPORTED
+ *   otherwise, before any device call).
  *   x, bias             as moe_route (bf16 x [T,H]; bias [E] fp32 or NULL)
  *   w_router_t          device [E,H] bf16: the router weights K-major (W_r transposed, the layout
  *                       of the expert weights), z[t][e] = sum_h x[t][h] w_router_t[e][h]
- *   w13, w2             routed experts as moe_expert_ffn with n_experts = E, inter = I (bf16)
- *   shared_w13, shared_w2  the shared expert (one expert, inter = I_shared), NULL iff I_shared == 0
+ *   w13, w13_scale, w2, w2_scale
+ *                       routed experts as moe_expert_ffn with n_experts = E, inter = I (scales:
+ *                       MX only, else NULL)
+ *   shared_w13, shared_w13_scale, shared_w2, shared_w2_scale
+ *                       the shared expert (one expert, inter = I_shared), NULL iff I_shared == 0
+ *                       (scales: MX only)
  *   topk_ids, topk_weights, counts, offsets, sorted_pair, pair_pos
  *                       out: as moe_route and moe_permute
  *   y_perm              device [T*K,H] bf16 out: the routed expert rows, as moe_expert_ffn_gather
@@ -260,10 +264,11 @@ moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const flo
  * time (calls in flight together on one workspace race). The call may be captured in a HIP
  * graph. */
 moe_status moe_layer_decode(const moe_config* cfg, const void* x, const void* w_router_t, const float* bias,
-                            const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
-                            int32_t* topk_ids, float* topk_weights, int32_t* counts, int32_t* offsets,
-                            int32_t* sorted_pair, int32_t* pair_pos, void* y_perm, void* y_shared, void* out,
-                            void* ws, size_t ws_bytes, void* stream);
+                            const void* w13, const void* w13_scale, const void* w2, const void* w2_scale,
+                            const void* shared_w13, const void* shared_w13_scale, const void* shared_w2,
+                            const void* shared_w2_scale, int32_t* topk_ids, float* topk_weights, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* y_perm,
+                            void* y_shared, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* moe_quantize_fp8 -- e4m3 row quantisation of bf16 rows (the shared expert's input in the
  * fp8 layer): per row per 128 columns, scale = absmax/448 (fp32), code = e4m3(v / scale),

@@ -52,7 +52,7 @@ _SIGS = {
     "moe_expert_ffn_gather": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                    _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _P, _P, _P]),
-    "moe_layer_decode": (_I, [_P] + [_P] * 17 + [ctypes.c_size_t, _P]),
+    "moe_layer_decode": (_I, [_P] + [_P] * 21 + [ctypes.c_size_t, _P]),
     "moe_quantize_fp8": (_I, [_I, _I, _P, _P, _P, _P]),
     "moe_quantize_mx": (_I, [_I, _I, _P, _P, _P, _P]),
     "moe_get_device_error": (_I, [_P, ctypes.POINTER(_I), _P]),
@@ -189,13 +189,16 @@ def moe_combine(cfg, pair_pos, topk_weights, y_perm, y_shared, out, stream=None)
                              _stream(stream)), "moe_combine")
 
 
-def moe_layer_decode(cfg, x, w_router_t, bias, w13, w2, shared_w13, shared_w2, topk_ids, topk_weights,
-                     counts, offsets, sorted_pair, pair_pos, y_perm, y_shared, out, ws, stream=None):
+def moe_layer_decode(cfg, x, w_router_t, bias, w13, w13_scale, w2, w2_scale, shared_w13, shared_w13_scale,
+                     shared_w2, shared_w2_scale, topk_ids, topk_weights, counts, offsets, sorted_pair,
+                     pair_pos, y_perm, y_shared, out, ws, stream=None):
     c, pc = _cfg(cfg)
-    _check(lib().moe_layer_decode(pc, _p(x), _p(w_router_t), _p(bias), _p(w13), _p(w2), _p(shared_w13),
-                                  _p(shared_w2), _p(topk_ids), _p(topk_weights), _p(counts), _p(offsets),
-                                  _p(sorted_pair), _p(pair_pos), _p(y_perm), _p(y_shared), _p(out), _p(ws),
-                                  ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_decode")
+    _check(lib().moe_layer_decode(pc, _p(x), _p(w_router_t), _p(bias), _p(w13), _p(w13_scale), _p(w2),
+                                  _p(w2_scale), _p(shared_w13), _p(shared_w13_scale), _p(shared_w2),
+                                  _p(shared_w2_scale), _p(topk_ids), _p(topk_weights), _p(counts),
+                                  _p(offsets), _p(sorted_pair), _p(pair_pos), _p(y_perm), _p(y_shared),
+                                  _p(out), _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_layer_decode")
 
 
 def moe_quantize_fp8(rows, cols, inp, codes, scales, stream=None):

@@ -340,10 +340,11 @@ moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const flo
 }
 
 moe_status moe_layer_decode(const moe_config* cfg, const void* x, const void* w_router_t, const float* bias,
-                            const void* w13, const void* w2, const void* shared_w13, const void* shared_w2,
-                            int32_t* topk_ids, float* topk_weights, int32_t* counts, int32_t* offsets,
-                            int32_t* sorted_pair, int32_t* pair_pos, void* y_perm, void* y_shared, void* out,
-                            void* ws, size_t ws_bytes, void* stream) {
+                            const void* w13, const void* w13_scale, const void* w2, const void* w2_scale,
+                            const void* shared_w13, const void* shared_w13_scale, const void* shared_w2,
+                            const void* shared_w2_scale, int32_t* topk_ids, float* topk_weights, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* y_perm,
+                            void* y_shared, void* out, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(checked_config(cfg));
   const moe_config& c = *cfg;
   std::string why;
@@ -354,8 +355,13 @@ moe_status moe_layer_decode(const moe_config* cfg, const void* x, const void* w_
   const bool sh = c.I_shared > 0;
   if (sh && (!shared_w13 || !shared_w2 || !y_shared))
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: I_shared > 0 needs shared_w13, shared_w2 and y_shared");
-  if (!sh && (shared_w13 || shared_w2 || y_shared))
+  if (!sh && (shared_w13 || shared_w2 || y_shared || shared_w13_scale || shared_w2_scale))
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: shared expert buffers given with I_shared == 0");
+  const bool mx = c.dtype == MOE_MXFP4;
+  if (mx && (!w13_scale || !w2_scale || (sh && (!shared_w13_scale || !shared_w2_scale))))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: MX layers need the weight scale arrays");
+  if (!mx && (w13_scale || w2_scale || shared_w13_scale || shared_w2_scale))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: weight scales are only for MX layers");
   WsLayout L;
   MOE_TRY(check_ws(c, ws, ws_bytes, &L));
   MOE_TRY(ensure_device());
@@ -365,9 +371,13 @@ moe_status moe_layer_decode(const moe_config* cfg, const void* x, const void* w_
   d.w_router = w_router_t;
   d.bias = bias;
   d.w13 = w13;
+  d.w13_scale = w13_scale;
   d.w2 = w2;
+  d.w2_scale = w2_scale;
   d.sh_w13 = shared_w13;
+  d.sh_w13_scale = shared_w13_scale;
   d.sh_w2 = shared_w2;
+  d.sh_w2_scale = shared_w2_scale;
   d.ids = topk_ids;
   d.weights = topk_weights;
   d.counts = counts;
@@ -379,9 +389,14 @@ moe_status moe_layer_decode(const moe_config* cfg, const void* x, const void* w_
   d.out = out;
   d.err = at<int32_t>(ws, L.err);
   d.ctrl = at<int32_t>(ws, L.dctrl);
+  d.flags = at<int32_t>(ws, L.dflags);
   d.logits = at<float>(ws, L.dlogits);
   d.h = at<void>(ws, L.h);
+  d.h_scale = mx ? at<void>(ws, L.hscale) : nullptr;
   d.h_shared = at<void>(ws, L.dhsh);
+  d.h_shared_scale = mx ? at<void>(ws, L.dhshs) : nullptr;
+  d.xq = mx ? at<uint8_t>(ws, L.dxq) : nullptr;
+  d.xqs = mx ? at<uint32_t>(ws, L.dxqs) : nullptr;
   MOE_HIP(launch_layer_decode(d, static_cast<hipStream_t>(stream)), "layer_decode");
   return MOE_OK;
 }

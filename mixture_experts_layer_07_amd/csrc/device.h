@@ -30,6 +30,15 @@ __device__ __forceinline__ void store_dev(T* p, T v) {
     *p = v;
 }
 
+// Store of one byte, device-scope (an agent-scope relaxed atomic store) when SC1, else plain.
+template <bool SC1>
+__device__ __forceinline__ void store_dev_u8(uint8_t* p, uint8_t v) {
+  if constexpr (SC1)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // threadIdx.x through an empty asm: values derived from it are formed where they are used, instead
 // of being hoisted out of a caller's loop and held in registers across everything else it runs
 // (the single-launch layer kernel runs many kinds of task in one loop).

@@ -27,10 +27,14 @@ namespace moe {
 //   the single-launch decode layer's regions (bf16 layers with T*K <= kSmallPermPairs, else empty):
 //   dctrl    kDecodeCtrlInts int32 control block (task counters, flags, the m-tile prefix)
 //   dlogits  [S][T][E] fp32 partial router logits (S = decode_router_splits)
-//   dhsh     [T][I_shared] bf16 SwiGLU output of the shared expert (the routed one is in h)
+//   dhsh     [T][I_shared] SwiGLU output of the shared expert (bf16, MX: e4m3 codes; the routed
+//            one is in h)
+//   dhshs    MX: its scale words [I_shared/128][T]
+//   dxq      MX: [T][H] e4m3 codes of x, then dxqs: their scale words [H/128][T]
+//   dflags   kDecodeFlagBytes: the flags many workgroups poll, in copies 4 KiB apart
 struct WsLayout {
   size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, part = 0, h = 0, hscale = 0, xscale = 0,
-         dctrl = 0, dlogits = 0, dhsh = 0, total = 0;
+         dctrl = 0, dlogits = 0, dhsh = 0, dhshs = 0, dxq = 0, dxqs = 0, dflags = 0, total = 0;
   int route_splits = 1;
   int perm_blocks = 0;
 };
@@ -43,6 +47,7 @@ constexpr int kTileMetaInts = 2048;  // tile metadata of the expert GEMMs (prefi
 // array of this many bytes; the histogram and bases take 2 * ceil(P / 256) * E * 4 of them.
 constexpr size_t kNoAllocScratchBytes = (size_t(2) << 20) + 256;
 constexpr int kDecodeCtrlInts = 2048;  // control block of the single-launch decode layer
+constexpr size_t kDecodeFlagBytes = 64 * 4096;  // its polled flags (64 copies, 4 KiB apart)
 
 // Validation; returns MOE_OK or the failure status with a reason in *why.
 moe_status check_routing(const moe_config* c, std::string* why);
@@ -144,9 +149,13 @@ struct DecodeCall {
   const void* w_router = nullptr;
   const float* bias = nullptr;
   const void* w13 = nullptr;
+  const void* w13_scale = nullptr;  // MX
   const void* w2 = nullptr;
+  const void* w2_scale = nullptr;   // MX
   const void* sh_w13 = nullptr;
+  const void* sh_w13_scale = nullptr;
   const void* sh_w2 = nullptr;
+  const void* sh_w2_scale = nullptr;
   int32_t* ids = nullptr;
   float* weights = nullptr;
   int32_t* counts = nullptr;
@@ -158,9 +167,14 @@ struct DecodeCall {
   void* out = nullptr;
   int32_t* err = nullptr;     // workspace
   int32_t* ctrl = nullptr;    // workspace
+  int32_t* flags = nullptr;   // workspace
   float* logits = nullptr;    // workspace
   void* h = nullptr;          // workspace
+  void* h_scale = nullptr;    // workspace (MX)
   void* h_shared = nullptr;   // workspace
+  void* h_shared_scale = nullptr;  // workspace (MX)
+  uint8_t* xq = nullptr;      // workspace (MX): MXFP8 codes of x
+  uint32_t* xqs = nullptr;    // workspace (MX): their scale words
 };
 hipError_t launch_layer_decode(const DecodeCall& d, hipStream_t s);
 // combine

@@ -1,5 +1,6 @@
-// Single-launch decode layer (bf16): router, top-K, permutation, the routed and shared experts'
-// Linear-1 and Linear-2, and the weighted combine in one persistent kernel.
+// Single-launch decode layer (bf16, or MXFP8 x MXFP4 experts): router, top-K, permutation, the
+// routed and shared experts' Linear-1 and Linear-2, and the weighted combine in one persistent
+// kernel.
 //
 // The persistent-kernel idea is FlashMoE's ("MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到
 // DeepSeek-V4", wqh011128.github.io, 4.1-4.7: one launch, blocks that pull ready tasks, tile-sized
@@ -12,14 +13,18 @@
 // one counter per segment, and a task waits only for tasks of earlier segments:
 //   0 router     32 x 256 tiles of the router GEMM z = x W_r (K-major W_r) over a piece of H:
 //                partial logits, fp32 (the grouped-GEMM tile code with one "expert")
-//   1 shared L1  32 x 256 tiles of the shared expert's gate/up GEMM with SwiGLU (reads x only)
-//   2 top-K      one token: waits for the router tiles of its 32-token block
-//   3 permute    one task: the one-workgroup counting sort, then the m-tile prefix of the
-//                routed experts; publishes "routing ready"
+//   1 quantise   (MX layers) 4 rows of x to MXFP8 codes and scales (one per wave)
+//   2 shared L1  32 x 256 tiles of the shared expert's gate/up GEMM with SwiGLU (reads x, or its
+//                MXFP8 codes, only)
+//   3 top-K      one token: waits for the router tiles of its 32-token block; the task that
+//                completes the last token runs the one-workgroup counting sort and the m-tile
+//                prefix of the routed experts, and announces "routing ready"
 //   4 routed L1  32 x 256 tiles over the expert-grouped pairs (rows gathered from x in place)
 //   5 shared L2  waits for the shared L1 tiles of its m-tile
 //   6 routed L2  waits for the L1 tiles of its expert m-tile
 //   7 combine    token x 2048-channel block: waits for every Linear-2 tile
+// The expert GEMM tiles are those of the separate GEMM kernels (bf16: 32 x 256 tiles through two
+// LDS stages; MX: the three-stage 32 x 256 tiles on the scaled MFMA), the router's always bf16.
 // Tasks are pulled in list order (expert-major for the GEMMs), so the Linear-1 tiles finish
 // roughly in the order the Linear-2 tiles are pulled and Linear-2 rarely waits. A workgroup moves
 // to the next segment only once every task of the current one has been pulled, and a task waits
@@ -55,22 +60,24 @@
 
 #include "combine_rows.h"
 #include "gemm_bf16_tile.h"
+#include "gemm_mx_tile.h"
 #include "perm_small.h"
+#include "quant_rows.h"
 #include "route_topk.h"
 
 namespace moe {
 
 namespace dec {
 constexpr int kSegs = 8;
-enum Seg { kRouter = 0, kSh1, kTopk, kPerm, kL1, kSh2, kL2, kComb };
+enum Seg { kRouter = 0, kQuant, kSh1, kTopk, kL1, kSh2, kL2, kComb };
 constexpr int kMaxTokBlocks = kSmallPermPairs / 32;  // 32-token router m-tiles (T <= P <= 4096)
 constexpr int kMaxMTiles = kSmallPermPairs / 32 + kMaxExperts;
 // control block (int32 words)
 constexpr int kQ = 0;                              // [kSegs] task counters
-constexpr int kReady = kQ + kSegs;                 // routing outputs and the m-tile prefix written
-constexpr int kTopkDone = kReady + 1;              // top-K tasks done
+constexpr int kTopkDone = kQ + kSegs;              // top-K tasks done
 constexpr int kL2Done = kTopkDone + 1;             // Linear-2 tiles done (routed and shared)
-constexpr int kAbort = kL2Done + 1;                // a wait ran past its limit
+constexpr int kQuantDone = kL2Done + 1;            // MX: MXFP8 quantisation tasks of x done
+constexpr int kAbort = kQuantDone + 1;             // a wait ran past its limit
 constexpr int kExit = kAbort + 1;                  // workgroups finished
 constexpr int kShOff = kExit + 1;                  // offsets {0, T} of the one-"expert" GEMMs
 constexpr int kRouterDone = 32;                    // [kMaxTokBlocks] router tiles done per m-tile
@@ -81,7 +88,15 @@ constexpr int kClear = kTp + kMaxExperts + 1;         // words cleared at the st
 constexpr int kEpoch = (kClear + 1) & ~1;             // 64-bit launch epoch
 static_assert(kShOff + 2 <= kRouterDone, "control block layout");
 static_assert(kEpoch + 2 <= kDecodeCtrlInts, "control block too small");
+static_assert(3 + kMaxTokBlocks <= 1024, "flags of one copy within its 4 KiB");
 constexpr unsigned long long kWaitLimit = 200000000ull;  // 2 s of the 100 MHz real-time counter
+// Flags that many workgroups wait on at once (routing ready, every Linear-2 tile done) are kept in
+// kFlagCopies copies kFlagStride words apart, workgroup b polling copy b % kFlagCopies, so that the
+// polls spread over the memory channels instead of queueing on one.
+constexpr int kFlagCopies = 64;
+constexpr int kFlagStride = 1024;  // (4 KiB)
+constexpr int kFlagReady = 0, kFlagAllDone = 1, kFlagQuant = 2;
+constexpr int kFlagRouter = 3;  // [kMaxTokBlocks]: every router tile of 32-token m-tile m done
 }  // namespace dec
 
 struct DecodeArgs {
@@ -100,6 +115,10 @@ struct DecodeArgs {
   int32_t* pair_pos;
   int32_t* err;           // device error word
   int32_t* ctrl;          // control block
+  int32_t* flags;         // kFlagCopies x kFlagStride words: the polled flags
+  const uint8_t* x;       // MX: the layer input [T][H] bf16, quantised by the kQuant tasks into
+  uint8_t* xq;            //     xq [T][H] e4m3 codes and
+  uint32_t* xqs;          //     xqs, the MX scale array of its T rows ([H/128][T] words)
   GemmArgs gr;            // router GEMM: x [T,H] x W_r^T [E,H] -> logits (C of piece 0)
   GemmArgs g1, g2;        // routed Linear-1 (gathered rows) and Linear-2
   GemmArgs s1, s2;        // shared expert
@@ -128,6 +147,16 @@ __device__ __forceinline__ void snapshot_l1(const int32_t* ctrl, int n, int per,
   __syncthreads();
 }
 
+// All threads call, after the results the flag announces have completed (s_waitcnt) on every wave.
+// Sets flag f in every copy. (The copies of flag f, and the flags past 64 on one copy, are cleared
+// at the start and at the end of a launch.)
+__device__ __forceinline__ void raise_flag(int32_t* flags, int f) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x < dec::kFlagCopies)
+    __hip_atomic_store(flags + threadIdx.x * dec::kFlagStride + f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Polling: every poll is a read at the memory side (agent scope), and hundreds of workgroups may
 // wait on one counter at once (for the routing, at the end for the last Linear-2 tiles), so the
 // interval between polls doubles from about 0.25 us up to about 4 us; a wait gives up after
@@ -138,10 +167,9 @@ __device__ __forceinline__ void poll_pause(int units) {
 
 // All threads call. Waits until *p >= target (thread 0 polls), then acquires. Returns false
 // (uniformly) if the wait gave up or another workgroup's did.
-__device__ __forceinline__ bool wait_geq(const DecodeArgs& a, int idx, int target, int* s_flag) {
+__device__ __forceinline__ bool wait_geq(const DecodeArgs& a, const int32_t* p, int target, int* s_flag) {
   if (threadIdx.x == 0) {
     int ok = 1;
-    int32_t* p = a.ctrl + idx;
     if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
       int units = 1;
@@ -186,9 +214,36 @@ __device__ __forceinline__ void combine_task(const DecodeArgs& a, int task, int*
   }
 }
 
+// ---------------------------------------------------------------- expert GEMM tiles
+// One whole tile of an expert GEMM of the layer: bf16 (the 32 x 256 tiles of gemm_bf16_tile.h on
+// the stages sA0..sB1) or MX (the three-stage 32 x 256 tiles of gemm_mx_tile.h, their six stages
+// carved from sB0 and sB1). Device-scope output stores. GSC (MX): the activation scale words are
+// read at the gathered source rows.
+using MxDecode = MxR3<32, 256, 1, 4>;
+static_assert(2 * MxDecode::BCH <= w4::kStageB && MxDecode::BCH + 3 * MxDecode::ACH <= w4::kStageB,
+              "MX stages within the bf16 ones");
+
+template <bool MX, bool GLU, bool GSC = false>
+__device__ __forceinline__ void expert_tile(const GemmArgs& g, const int* tp, int tile, u32x4* sA0, u32x4* sA1,
+                                            u32x4* sB0, u32x4* sB1, int* s_slot) {
+  if constexpr (MX) {
+    constexpr int AC = MxDecode::ACH, BC = MxDecode::BCH;
+    mx_r3_item<MxDecode, GLU, true, GSC>(g, tp, tile, sB1 + BC, sB1 + BC + AC, sB1 + BC + 2 * AC, sB0, sB0 + BC, sB1);
+  } else {
+    const SplitQueue sq0 = {0, 0, 1, 0, 0, 0};  // (whole tiles: no hand-over of K pieces)
+    WorkItem w;
+    w.tile = tile;
+    w.piece = -1;
+    w.slot = w.first = 0;
+    w.k0 = 0;
+    w.k1 = g.K / 64;
+    m32_item<GLU, false, false, kCpolSc1>(g, tp, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+  }
+}
+
 // ---------------------------------------------------------------- the kernel
-template <bool OF32>
-__global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
+template <bool MX, bool OF32>
+__global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
   __shared__ u32x4 sA0[m32::kStageA];
   __shared__ u32x4 sA1[m32::kStageA];
   __shared__ u32x4 sB0[w4::kStageB];
@@ -209,6 +264,10 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(s_slot[0])) {
       for (int i = tid; i < dec::kClear; i += 256) store_dev<true>(ctrl + i, (int32_t)(i == dec::kShOff + 1 ? a.T : 0));
+      for (int i = tid; i < dec::kFlagCopies * (dec::kFlagRouter + a.mts); i += 256) {
+        const int c = i / (dec::kFlagRouter + a.mts), f = i - c * (dec::kFlagRouter + a.mts);
+        store_dev<true>(a.flags + c * dec::kFlagStride + f, (int32_t)0);
+      }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0) __hip_atomic_store(epoch, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -242,12 +301,18 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
   bool alive = true;
   int n_l2 = 0;    // Linear-2 tiles (routed and shared) done and not yet counted
   bool snap = false;  // s_l1ok holds a snapshot of the Linear-1 m-tile counters
+  bool quant = !MX;   // the MXFP8 codes of x are complete
   float* f0 = reinterpret_cast<float*>(sB0);
   float* f1 = reinterpret_cast<float*>(sB1);
 
   for (int seg = 0; seg < dec::kSegs && alive; ++seg) {
+    if ((seg == dec::kSh1 || seg == dec::kL1) && !quant) {
+      alive = wait_geq(a, a.flags + (blockIdx.x % dec::kFlagCopies) * dec::kFlagStride + dec::kFlagQuant, 1, s_slot);
+      if (!alive) break;
+      quant = true;
+    }
     if ((seg == dec::kL1 || seg == dec::kL2 || seg == dec::kComb) && !routed) {
-      alive = wait_geq(a, dec::kReady, 1, s_slot);
+      alive = wait_geq(a, a.flags + (blockIdx.x % dec::kFlagCopies) * dec::kFlagStride + dec::kFlagReady, 1, s_slot);
       if (!alive) break;
       for (int i = tid; i <= a.E; i += 256) s_tp[i] = ctrl[dec::kTp + i];
       __syncthreads();
@@ -256,9 +321,9 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
     int n = 0;
     switch (seg) {
       case dec::kRouter: n = rtiles * S; break;
+      case dec::kQuant: n = MX ? (a.T + 3) / 4 : 0; break;
       case dec::kSh1: n = a.has_shared ? a.mts * a.s1.n_tiles_n : 0; break;
       case dec::kTopk: n = a.T; break;
-      case dec::kPerm: n = 1; break;
       case dec::kL1: n = s_tp[a.E] * a.g1.n_tiles_n; break;
       case dec::kSh2: n = a.has_shared ? a.mts * a.s2.n_tiles_n : 0; break;
       case dec::kL2: n = s_tp[a.E] * a.g2.n_tiles_n; break;
@@ -275,7 +340,13 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
       if (task >= n) {
         // leaving Linear-2: count this workgroup's Linear-2 tiles (and shared ones) as done
         if (seg == dec::kL2 && n_l2 > 0) {
-          handoff_add(ctrl + dec::kL2Done, n_l2);
+          const int total = s_tp[a.E] * a.g2.n_tiles_n + (a.has_shared ? a.mts * a.s2.n_tiles_n : 0);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (tid == 0)
+            s_slot[0] = __hip_atomic_fetch_add(ctrl + dec::kL2Done, n_l2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __syncthreads();
+          if (__builtin_amdgcn_readfirstlane(s_slot[0]) + n_l2 == total) raise_flag(a.flags, dec::kFlagAllDone);
           n_l2 = 0;
         }
         break;
@@ -296,17 +367,36 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
         g.C += (size_t)p * a.T * a.E * 4;
         m32_item<false, true, false, kCpolSc1>(g, s_tps, w, sq0, sA0, sA1, sB0, sB1, s_slot);
         const TileInfo ti = decode_tile(w.tile, s_tps, a.gr, 32);
-        handoff_add(ctrl + dec::kRouterDone + ti.mt, 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0)
+          s_slot[0] = __hip_atomic_fetch_add(ctrl + dec::kRouterDone + ti.mt, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(s_slot[0]) == a.gr.n_tiles_n * S - 1)
+          raise_flag(a.flags, dec::kFlagRouter + ti.mt);
+      } else if (seg == dec::kQuant) {
+        // rows 4 task .. 4 task + 3 of x to MXFP8, one per wave; the task that completes the
+        // count announces the codes
+        const int r = task * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
+        if (r < a.T) gather_row<2, true>(nullptr, 1, a.T, a.T, a.x, (size_t)a.H * 2, a.xq, a.xqs, a.H, r);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0)
+          s_slot[0] = __hip_atomic_fetch_add(ctrl + dec::kQuantDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(s_slot[0]) == n - 1) raise_flag(a.flags, dec::kFlagQuant);
       } else if (seg == dec::kSh1) {
-        w.k1 = a.s1.K / 64;
-        m32_item<true, false, false, kCpolSc1>(a.s1, s_tps, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        expert_tile<MX, true>(a.s1, s_tps, task, sA0, sA1, sB0, sB1, s_slot);
         const TileInfo ti = decode_tile(task, s_tps, a.s1, 32);
         handoff_add(ctrl + dec::kL1sDone + ti.mt, 1);
       } else if (seg == dec::kTopk) {
         // token `task`: its router m-tile's every n-tile and piece must be done; the four waves
         // stage the S partial logits in LDS (one round of loads), then wave 0 sums them in split
         // order and selects
-        if (!(alive = wait_geq(a, dec::kRouterDone + task / 32, a.gr.n_tiles_n * S, s_slot))) break;
+        if (!(alive = wait_geq(a, a.flags + (blockIdx.x % dec::kFlagCopies) * dec::kFlagStride + dec::kFlagRouter +
+                                      task / 32, 1, s_slot)))
+          break;
         {
           // loads in flight eight at a time (S * E / 4 <= 64 * 64: at most two rounds), then the
           // LDS stores
@@ -360,31 +450,36 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
           topk_select<true>(z, a.bias, a.tk, a.ids, a.weights, task, lw, reinterpret_cast<int*>(lw + 256),
                             reinterpret_cast<int*>(lw + 512), lw + 768);
         }
-        handoff_add(ctrl + dec::kTopkDone, 1);
-      } else if (seg == dec::kPerm) {
-        if (!(alive = wait_geq(a, dec::kTopkDone, a.T, s_slot))) break;
-        int* off = reinterpret_cast<int*>(f1);
-        int* sbuf = off + 512;
-        perm_small_block<true>(a.ids, a.T * a.K, a.E, a.counts, a.offsets, a.sorted_pair, a.pair_pos, a.err,
-                               reinterpret_cast<uint16_t(*)[kMaxExperts]>(f0), off, sbuf);
+        // the top-K task that completes the count runs the permutation right away
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // m-tile prefix of the routed experts (32-row tiles)
-        const int c = tid < a.E ? off[tid + 1] - off[tid] : 0;
-        int tot;
-        const int ex = block_exscan_256(c > 0 ? (c + 31) / 32 : 0, sbuf, &tot);
-        if (tid < a.E) store_dev<true>(ctrl + dec::kTp + tid, (int32_t)ex);
-        if (tid == 0) store_dev<true>(ctrl + dec::kTp + a.E, (int32_t)tot);
-        handoff_add(ctrl + dec::kReady, 1);
+        if (tid == 0)
+          s_slot[0] = __hip_atomic_fetch_add(ctrl + dec::kTopkDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(s_slot[0]) == a.T - 1) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // (every token's ids)
+          __syncthreads();
+          int* off = reinterpret_cast<int*>(f1);
+          int* sbuf = off + 512;
+          perm_small_block<true>(a.ids, a.T * a.K, a.E, a.counts, a.offsets, a.sorted_pair, a.pair_pos, a.err,
+                                 reinterpret_cast<uint16_t(*)[kMaxExperts]>(f0), off, sbuf);
+          __syncthreads();
+          // m-tile prefix of the routed experts (32-row tiles)
+          const int c = tid < a.E ? off[tid + 1] - off[tid] : 0;
+          int tot;
+          const int ex = block_exscan_256(c > 0 ? (c + 31) / 32 : 0, sbuf, &tot);
+          if (tid < a.E) store_dev<true>(ctrl + dec::kTp + tid, (int32_t)ex);
+          if (tid == 0) store_dev<true>(ctrl + dec::kTp + a.E, (int32_t)tot);
+          raise_flag(a.flags, dec::kFlagReady);
+        }
       } else if (seg == dec::kL1) {
-        w.k1 = a.g1.K / 64;
-        m32_item<true, false, false, kCpolSc1>(a.g1, s_tp, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        expert_tile<MX, true, true>(a.g1, s_tp, task, sA0, sA1, sB0, sB1, s_slot);
         const TileInfo ti = decode_tile(task, s_tp, a.g1, 32);
         handoff_add(ctrl + dec::kL1Done + s_tp[ti.e] + ti.mt, 1);
       } else if (seg == dec::kSh2) {
         const TileInfo ti = decode_tile(task, s_tps, a.s2, 32);
-        if (!(alive = wait_geq(a, dec::kL1sDone + ti.mt, a.s1.n_tiles_n, s_slot))) break;
-        w.k1 = a.s2.K / 64;
-        m32_item<false, false, false, kCpolSc1>(a.s2, s_tps, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        if (!(alive = wait_geq(a, ctrl + dec::kL1sDone + ti.mt, a.s1.n_tiles_n, s_slot))) break;
+        expert_tile<MX, false>(a.s2, s_tps, task, sA0, sA1, sB0, sB1, s_slot);
         ++n_l2;
       } else if (seg == dec::kL2) {
         const TileInfo ti = decode_tile(task, s_tp, a.g2, 32);
@@ -394,16 +489,16 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
           snap = true;
         }
         if (!s_l1ok[m]) {
-          if (!(alive = wait_geq(a, dec::kL1Done + m, a.g1.n_tiles_n, s_slot))) break;
+          if (!(alive = wait_geq(a, ctrl + dec::kL1Done + m, a.g1.n_tiles_n, s_slot))) break;
           snapshot_l1(ctrl, s_tp[a.E], a.g1.n_tiles_n, s_l1ok);
         }
-        w.k1 = a.g2.K / 64;
-        m32_item<false, false, false, kCpolSc1>(a.g2, s_tp, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+        expert_tile<MX, false>(a.g2, s_tp, task, sA0, sA1, sB0, sB1, s_slot);
         ++n_l2;
       } else {
         if (!l2_all) {
-          const int total = s_tp[a.E] * a.g2.n_tiles_n + (a.has_shared ? a.mts * a.s2.n_tiles_n : 0);
-          if (!(alive = wait_geq(a, dec::kL2Done, total, s_slot))) break;
+          if (!(alive = wait_geq(a, a.flags + (blockIdx.x % dec::kFlagCopies) * dec::kFlagStride + dec::kFlagAllDone,
+                                 1, s_slot)))
+            break;
           l2_all = true;
         }
         combine_task<OF32>(a, task, reinterpret_cast<int*>(sA0), reinterpret_cast<float*>(sA0) + kMaxExperts);
@@ -419,6 +514,10 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode_bf16(DecodeArgs a) {
   if (__builtin_amdgcn_readfirstlane(s_slot[0]) == (int)gridDim.x - 1) {
     for (int i = tid; i < dec::kClear; i += 256)
       if (i != dec::kShOff && i != dec::kShOff + 1) ctrl[i] = 0;
+    for (int i = tid; i < dec::kFlagCopies * (dec::kFlagRouter + a.mts); i += 256) {
+      const int c = i / (dec::kFlagRouter + a.mts), f = i - c * (dec::kFlagRouter + a.mts);
+      a.flags[c * dec::kFlagStride + f] = 0;
+    }
   }
 }
 
@@ -495,6 +594,7 @@ hipError_t launch_layer_decode(const DecodeCall& d, hipStream_t s) {
   a.pair_pos = d.pair_pos;
   a.err = d.err;
   a.ctrl = d.ctrl;
+  a.flags = d.flags;
   a.y = static_cast<const uint8_t*>(d.y_perm);
   a.ysh = a.has_shared ? static_cast<const uint8_t*>(d.y_shared) : nullptr;
   a.out = static_cast<uint8_t*>(d.out);
@@ -518,49 +618,75 @@ hipError_t launch_layer_decode(const DecodeCall& d, hipStream_t s) {
   r.Nb = c.E;
   r.glu_I = 0;
   r.n_tiles_n = (c.E + 255) / 256;
-  // routed experts: Linear-1 gathers its rows from x (row i = token sorted_pair[i] / K)
+  const bool mx = c.dtype == MOE_MXFP4;
+  a.x = static_cast<const uint8_t*>(d.x);
+  a.xq = d.xq;
+  a.xqs = d.xqs;
+  // routed experts: Linear-1 gathers its rows from x (row i = token sorted_pair[i] / K); MX: from
+  // the MXFP8 codes xq, with the scale words of the source rows
   FfnArgs f;
-  f.dtype = MOE_BF16;
+  f.dtype = c.dtype;
   f.n_exp = c.E;
   f.n_rows = c.T * c.K;
   f.H = c.H;
   f.I = c.I;
   f.offsets = d.offsets;
-  f.x = d.x;
+  f.x = mx ? static_cast<const void*>(d.xq) : d.x;
+  f.x_scale = mx ? d.xqs : nullptr;
   f.x_rows_index = d.sorted_pair;
   f.x_rows_div = c.K;
   f.x_rows_limit = c.T;
   f.w13 = d.w13;
+  f.w13_scale = d.w13_scale;
   f.w2 = d.w2;
+  f.w2_scale = d.w2_scale;
   f.y = d.y_perm;
   f.h = d.h;
+  f.h_scale = d.h_scale;
   ffn_gemm_args(f, a.g1, a.g2);
+  if (mx) {  // (scale words read at the gathered source rows, see expert_tile)
+    a.g1.a_scale = static_cast<const float*>(static_cast<const void*>(d.xqs));
+    a.g1.a_scale_ld = c.T;
+  }
   if (a.has_shared) {
     // shared expert: one expert over the T rows of x; its offsets {0, T} are in the control block
     FfnArgs fs;
-    fs.dtype = MOE_BF16;
+    fs.dtype = c.dtype;
     fs.n_exp = 1;
     fs.n_rows = c.T;
     fs.H = c.H;
     fs.I = c.I_shared;
     fs.offsets = d.ctrl + dec::kShOff;
-    fs.x = d.x;
+    fs.x = mx ? static_cast<const void*>(d.xq) : d.x;
+    fs.x_scale = mx ? d.xqs : nullptr;
     fs.w13 = d.sh_w13;
+    fs.w13_scale = d.sh_w13_scale;
     fs.w2 = d.sh_w2;
+    fs.w2_scale = d.sh_w2_scale;
     fs.y = d.y_shared;
     fs.h = d.h_shared;
+    fs.h_scale = d.h_shared_scale;
     ffn_gemm_args(fs, a.s1, a.s2);
   }
-  const void* kernel = a.out_f32 ? reinterpret_cast<const void*>(&k_layer_decode_bf16<true>)
-                                 : reinterpret_cast<const void*>(&k_layer_decode_bf16<false>);
+  const void* kernel = mx ? (a.out_f32 ? reinterpret_cast<const void*>(&k_layer_decode<true, true>)
+                                       : reinterpret_cast<const void*>(&k_layer_decode<true, false>))
+                          : (a.out_f32 ? reinterpret_cast<const void*>(&k_layer_decode<false, true>)
+                                       : reinterpret_cast<const void*>(&k_layer_decode<false, false>));
   int grid = 0;
   hipError_t e = decode_grid(kernel, &grid);
   if (e != hipSuccess) return e;
-  return timed_launch("layer_decode_bf16", s, [&] {
-    if (a.out_f32)
-      hipLaunchKernelGGL(k_layer_decode_bf16<true>, dim3(grid), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(k_layer_decode_bf16<false>, dim3(grid), dim3(256), 0, s, a);
+  return timed_launch(mx ? "layer_decode_mx" : "layer_decode_bf16", s, [&] {
+    if (mx) {
+      if (a.out_f32)
+        hipLaunchKernelGGL((k_layer_decode<true, true>), dim3(grid), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_layer_decode<true, false>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+      if (a.out_f32)
+        hipLaunchKernelGGL((k_layer_decode<false, true>), dim3(grid), dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_layer_decode<false, false>), dim3(grid), dim3(256), 0, s, a);
+    }
   });
 }
 

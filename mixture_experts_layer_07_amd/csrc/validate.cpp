@@ -90,7 +90,8 @@ bool decode_supported(const moe_config& c, std::string* why) {
     if (why) *why = msg;
     return false;
   };
-  if (c.dtype != MOE_BF16) return no("the single-launch decode layer is built for bf16 layers");
+  if (c.dtype != MOE_BF16 && c.dtype != MOE_MXFP4)
+    return no("the single-launch decode layer is built for bf16 and MXFP4 layers");
   if ((int64_t)c.T * c.K > kSmallPermPairs) return no("the single-launch decode layer needs T*K <= 4096");
   if (c.E % 8) return no("the single-launch decode layer needs E a multiple of 8");
   if ((int64_t)c.T * c.H * 2 >= (int64_t(1) << 32)) return no("x above 4 GiB");
@@ -146,8 +147,17 @@ WsLayout layout(const moe_config& c) {
   off = align256(off + (dec ? (size_t)kDecodeCtrlInts * 4 : 0));
   L.dlogits = off;
   off = align256(off + (dec ? (size_t)decode_router_splits(c) * T * E * 4 : 0));
+  const bool dmx = dec && c.dtype == MOE_MXFP4;
   L.dhsh = off;
-  off = align256(off + (dec ? T * (size_t)c.I_shared * 2 : 0));
+  off = align256(off + (dec ? T * (size_t)c.I_shared * (dmx ? 1 : 2) : 0));
+  L.dhshs = off;
+  off = align256(off + (dmx ? T * (size_t)(c.I_shared / 128) * 4 : 0));
+  L.dxq = off;
+  off = align256(off + (dmx ? T * H : 0));
+  L.dxqs = off;
+  off = align256(off + (dmx ? T * (H / 128) * 4 : 0));
+  L.dflags = off;
+  off = align256(off + (dec ? kDecodeFlagBytes : 0));
   L.total = off;
   return L;
 }

@@ -1,7 +1,7 @@
 """One MoE layer forward on torch device buffers: the C-ABI calls in order.
 
 route -> permute -> expert FFN (routed experts, then the shared expert if any) -> combine.
-With fused=True (bf16 layers with T*K <= 4096) the whole layer is one call, moe_layer_decode: one
+With fused=True (bf16 and MX layers with T*K <= 4096) the whole layer is one call, moe_layer_decode: one
 kernel launch that fills the same buffers (it reads the router weights K-major, transposed once
 at construction).
 With gather=True (the default) the permute stage only builds the pair order (and, for fp8 and
@@ -53,7 +53,7 @@ class MoELayer:
             if self.quant:
                 self.x_perm_scale = self._scales(P, H, dev)
         self.xq = self.xq_scale = None
-        if self.quant and (self.gather or self.shared is not None):
+        if self.quant and not fused and (self.gather or self.shared is not None):
             # the e4m3 codes of the T input rows, read by the gathered Linear-1 and the shared expert
             self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
             self.xq_scale = self._scales(T, H, dev)
@@ -122,11 +122,12 @@ class MoELayer:
     def forward(self, x):
         if self.fused:
             ex, sh = self.experts, self.shared
-            B.moe_layer_decode(self.c, x, self.w_router_t, self.bias, ex["w13"], ex["w2"],
-                               None if sh is None else sh["w13"], None if sh is None else sh["w2"],
-                               self.topk_ids, self.topk_weights, self.counts, self.offsets,
-                               self.sorted_pair, self.pair_pos, self.y_perm, self.y_shared, self.out,
-                               self.ws)
+            shg = (lambda k: None) if sh is None else sh.get  # noqa: E731
+            B.moe_layer_decode(self.c, x, self.w_router_t, self.bias, ex["w13"], ex.get("w13_scale"),
+                               ex["w2"], ex.get("w2_scale"), shg("w13"), shg("w13_scale"), shg("w2"),
+                               shg("w2_scale"), self.topk_ids, self.topk_weights, self.counts,
+                               self.offsets, self.sorted_pair, self.pair_pos, self.y_perm,
+                               self.y_shared, self.out, self.ws)
             return self.out
         self.route(x)
         self.permute(x)

@@ -191,8 +191,9 @@ def check_permute(case, ids_g, rows=None):
     sel = np.arange(c.P) if rows is None else np.asarray(rows)
     src_tok = sp[sel] // c.K
     if L.gather:
-        # no permuted copy: Linear-1 reads x (fp8 / MX: the codes of the T rows) in place
-        if c.dtype in QUANT:
+        # no permuted copy: Linear-1 reads x (fp8 / MX: the codes of the T rows) in place. (The
+        # single launch keeps the codes in its workspace: the expert rows check them there.)
+        if c.dtype in QUANT and not L.fused:
             toks = np.unique(src_tok)
             codes, scales = quantize(c.dtype, case.x[torch.from_numpy(toks)].float().numpy())
             ti = torch.from_numpy(toks).to(L.xq.device)

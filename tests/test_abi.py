@@ -140,8 +140,9 @@ def test_entry_points_validate_before_device(lib):
     # the single-launch decode layer: shape support, NULL buffers and the shared-expert buffers
     # (given iff I_shared > 0) are checked before any device call
     dec = lambda pcfg, nb, **o: lib.moe_layer_decode(  # noqa: E731
-        pcfg, o.get("x", FAKE), FAKE, None, FAKE, FAKE, o.get("sw13", FAKE), o.get("sw2", FAKE), FAKE, FAKE,
-        FAKE, FAKE, FAKE, FAKE, FAKE, o.get("ysh", FAKE), FAKE, o.get("ws", FAKE), o.get("wsb", nb), None)
+        pcfg, o.get("x", FAKE), FAKE, None, FAKE, o.get("s13"), FAKE, o.get("s2"), o.get("sw13", FAKE),
+        o.get("ss13"), o.get("sw2", FAKE), o.get("ss2"), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        o.get("ysh", FAKE), FAKE, o.get("ws", FAKE), o.get("wsb", nb), None)
     assert dec(pc, n, x=None) == INVALID
     assert dec(pc, n, sw13=None) == INVALID
     assert dec(pc, n, ysh=None) == INVALID
@@ -154,6 +155,12 @@ def test_entry_points_validate_before_device(lib):
     assert dec(ctypes.byref(cfg(3, T=1024, K=8)), n) == UNSUPPORTED   # T*K above 4096
     assert "4096" in lib.moe_last_error().decode()
     assert dec(p8, lib.moe_workspace_size(p8)) == UNSUPPORTED          # fp8 layer
+    assert dec(pc, n, s13=FAKE) == INVALID                              # scales of a bf16 layer
+    cmx = cfg(7, T=64, H=256, I=256, E=16, K=4, n_group=4, topk_group=2, I_shared=256)
+    nmx = lib.moe_workspace_size(ctypes.byref(cmx))
+    assert dec(ctypes.byref(cmx), nmx) == INVALID                       # MX without weight scales
+    assert dec(ctypes.byref(cmx), nmx, s13=FAKE, s2=FAKE) == INVALID     # MX without shared scales
+    assert dec(ctypes.byref(cmx), nmx - 1, s13=FAKE, s2=FAKE, ss13=FAKE, ss2=FAKE) == WORKSPACE
     c12 = cfg(3, T=64, H=256, I=128, E=12, K=4, n_group=4, topk_group=2, I_shared=128)
     assert dec(ctypes.byref(c12), lib.moe_workspace_size(ctypes.byref(c12))) == UNSUPPORTED  # E % 8
     # logits-only routing reads only the routing fields: H, I and dtype are not checked
