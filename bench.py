@@ -6,7 +6,7 @@ layer (T=8192, H=7168, I=2048, E=256, K=8, grouped sigmoid routing, one shared e
 largest layer of the set that one GPU holds. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 25] [--config 3] [--no-cpu-baseline]
-                  [--single-launch]   (decode-sized bf16 layers: the whole layer in one kernel launch)
+                  [--single-launch]   (decode-sized bf16 / MXFP4 layers: the whole layer in one kernel launch)
 """
 import argparse
 import json
@@ -38,8 +38,8 @@ def parse():
                    help="time the path that writes the permuted activations x_perm instead of "
                         "gathering the token rows in Linear-1")
     p.add_argument("--single-launch", action="store_true",
-                   help="time the whole layer as one kernel launch (moe_layer_decode; bf16 layers "
-                        "with T*K <= 4096)")
+                   help="time the whole layer as one kernel launch (moe_layer_decode; bf16 and "
+                        "MXFP4 layers with T*K <= 4096)")
     p.add_argument("--cpu-tokens", type=int, default=0, help="tokens in the oracle sample (0 = auto)")
     p.add_argument("--copy-calibration-gib", type=float, default=0.0,
                    help="after the measurement, run one plain copy-like pass over this many GiB "
@@ -117,11 +117,13 @@ def kernel_work(cfg, active, gather=True):
 def single_launch_work(cfg, active):
     """Work of the single-launch layer: the whole layer's flops and the bytes of every operand the
     separate launches read and write (each once), less the router-weight transpose (the single
-    launch reads the router weights K-major as given) and the tile lists (built in LDS)."""
+    launch reads the router weights K-major as given), the tile lists (built in LDS) and, for MX
+    layers, the scale words in grouped row order (Linear-1 reads them at the source rows)."""
     w = kernel_work(cfg, active, True)
-    fl = sum(v[0] for k, v in w.items() if not k.endswith(("router_transpose", "build_tiles")))
-    by = sum(v[1] for k, v in w.items() if not k.endswith(("router_transpose", "build_tiles")))
-    return {"layer/layer_decode_bf16": (fl, by)}
+    skip = ("router_transpose", "build_tiles", "gather_scales_mx")
+    fl = sum(v[0] for k, v in w.items() if not k.endswith(skip))
+    by = sum(v[1] for k, v in w.items() if not k.endswith(skip))
+    return {"layer/layer_decode_" + ("mx" if cfg.dtype == "mxfp4" else "bf16"): (fl, by)}
 
 
 def variant_free(name):
@@ -157,8 +159,9 @@ def main():
     ex = make_expert_weights(cfg, dev)
     sh = make_expert_weights(cfg, dev, shared=True) if cfg.I_shared else None
     clean = lambda d: None if d is None else {k: v for k, v in d.items() if v is not None}  # noqa: E731
-    if args.single_launch and not (cfg.dtype == "bf16" and cfg.P <= SMALL_PERM_PAIRS and cfg.E % 8 == 0):
-        print(f"bench.py: --single-launch takes bf16 layers with T*K <= {SMALL_PERM_PAIRS} "
+    if args.single_launch and not (cfg.dtype in ("bf16", "mxfp4") and cfg.P <= SMALL_PERM_PAIRS
+                                   and cfg.E % 8 == 0):
+        print(f"bench.py: --single-launch takes bf16 and MXFP4 layers with T*K <= {SMALL_PERM_PAIRS} "
               f"({cfg.name} is {cfg.dtype}, T*K = {cfg.P})", file=sys.stderr)
         sys.exit(2)
     layer = MoELayer(cfg, w_r.to(dev), None if bias is None else bias.to(dev), clean(ex), clean(sh), dev,
@@ -362,13 +365,15 @@ def bench_route(args, cfg):
 
 # Sources whose change invalidates a stored traffic measurement of a kernel.
 KERNEL_SOURCES = {
-    "gemm_bf16": ["kernels_gemm_bf16.hip", "gemm_bf16_tile.h", "gemm_common.h", "kernels_ffn.hip", "device.h",
-                  "internal.h"],
-    "layer_decode": ["kernels_layer.hip", "gemm_bf16_tile.h", "gemm_common.h", "route_topk.h", "perm_small.h",
-                     "combine_rows.h", "kernels_ffn.hip", "device.h", "internal.h", "validate.cpp"],
-    "gemm_fp8": ["kernels_gemm_fp8.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
-    "gemm_mx": ["kernels_gemm_mx.hip", "gemm_common.h", "kernels_ffn.hip", "device.h", "internal.h"],
-    "gemm_f32": ["kernels_ffn.hip", "gemm_common.h", "device.h", "internal.h"],
+    "gemm_bf16": ["kernels_gemm_bf16.hip", "gemm_bf16_tile.h", "gemm_common.h", "tile_plan.h", "kernels_ffn.hip",
+                  "device.h", "internal.h"],
+    "layer_decode": ["kernels_layer.hip", "gemm_bf16_tile.h", "gemm_mx_tile.h", "gemm_common.h", "tile_plan.h",
+                     "route_topk.h", "perm_small.h", "quant_rows.h", "combine_rows.h", "kernels_ffn.hip", "device.h",
+                     "internal.h", "validate.cpp"],
+    "gemm_fp8": ["kernels_gemm_fp8.hip", "gemm_common.h", "tile_plan.h", "kernels_ffn.hip", "device.h", "internal.h"],
+    "gemm_mx": ["kernels_gemm_mx.hip", "gemm_mx_tile.h", "gemm_common.h", "tile_plan.h", "kernels_ffn.hip",
+                "device.h", "internal.h"],
+    "gemm_f32": ["kernels_ffn.hip", "gemm_common.h", "tile_plan.h", "device.h", "internal.h"],
 }
 
 

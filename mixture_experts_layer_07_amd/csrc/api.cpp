@@ -390,6 +390,7 @@ moe_status moe_layer_decode(const moe_config* cfg, const void* x, const void* w_
   d.err = at<int32_t>(ws, L.err);
   d.ctrl = at<int32_t>(ws, L.dctrl);
   d.flags = at<int32_t>(ws, L.dflags);
+  d.cnt = at<int32_t>(ws, L.dcnt);
   d.logits = at<float>(ws, L.dlogits);
   d.h = at<void>(ws, L.h);
   d.h_scale = mx ? at<void>(ws, L.hscale) : nullptr;

@@ -145,4 +145,57 @@ __device__ __forceinline__ void combine_block(int t, int yb, const int32_t* __re
   }
 }
 
+// One chunk (8 channels, chunk index ch) of token t's combined row from bf16 expert rows, with
+// combine_block's arithmetic: fp32 fma of the live pairs in k order from zero (KC > 0: every row
+// chunk loaded first, a dropped pair read at row 0 and left out by a select), then the shared
+// row added, one rounding to the output type. pair_pos and w are read from global memory (the
+// same words for every chunk of the token). Any subset of threads may call.
+template <bool OF32, int KC>
+__device__ __forceinline__ void combine_chunk(int t, int ch, const int32_t* __restrict__ pair_pos,
+                                              const float* __restrict__ w, const uint8_t* __restrict__ y,
+                                              const uint8_t* __restrict__ ysh, uint8_t* __restrict__ out, int H,
+                                              int K) {
+  const size_t yrow = (size_t)H * 2;
+  uint8_t* o = out + (size_t)t * H * (OF32 ? 4 : 2);
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  if constexpr (KC > 0) {
+    int r[KC];
+    float wk[KC], v[KC][8], vs[8];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      r[k] = pair_pos[(size_t)t * KC + k];
+      wk[k] = w[(size_t)t * KC + k];
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) load_row_chunk<8, false>(y + (size_t)(r[k] < 0 ? 0 : r[k]) * yrow, ch, v[k]);
+    if (ysh) load_row_chunk<8, false>(ysh + (size_t)t * yrow, ch, vs);
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = r[k] >= 0 ? fmaf(wk[k], v[k][j], acc[j]) : acc[j];
+    if (ysh) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += vs[j];
+    }
+  } else {
+    float v[8];
+    for (int k = 0; k < K; ++k) {
+      const int r = pair_pos[(size_t)t * K + k];
+      if (r < 0) continue;
+      const float wk = w[(size_t)t * K + k];
+      load_row_chunk<8, false>(y + (size_t)r * yrow, ch, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wk, v[j], acc[j]);
+    }
+    if (ysh) {
+      load_row_chunk<8, false>(ysh + (size_t)t * yrow, ch, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += v[j];
+    }
+  }
+  store_out_chunk<8, OF32>(o, ch, acc);
+}
+
 }  // namespace moe

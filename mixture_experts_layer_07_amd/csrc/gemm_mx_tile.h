@@ -220,7 +220,7 @@ __device__ __forceinline__ void mx8_sched() {
 template <class P, bool GLU, bool SC1 = false, bool GSC = false>
 __device__ __forceinline__ void mx_r3_item(const GemmArgs& g, const int* tp, int t, u32x4* sA0, u32x4* sA1,
                                            u32x4* sA2, u32x4* sB0, u32x4* sB1, u32x4* sB2) {
-  constexpr int BM = P::BM, BN = P::BN, NWN = P::NWN, NT = P::NT, NW = P::NW;
+  constexpr int BM = P::BM, BN = P::BN, NWN = P::NWN, NW = P::NW;
   constexpr int WM = P::WM, WN = P::WN, MB = P::MB, NB = P::NB;
   constexpr int AJ = P::AJ, BJ = P::BJ;
   static_assert(!GLU || (NB % 2 == 0 && BN == 256), "GLU: gate / up pairs per wave, 128 h columns per tile");

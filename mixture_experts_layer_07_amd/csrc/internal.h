@@ -24,7 +24,8 @@ namespace moe {
 //   hscale   [max_rows][max_I/128] fp32 (fp8 layer) / [max_I/128][rows] E8M0 words (MX layer)
 //   xscale   [H/128][T*K] E8M0 words (MX layer): the activation scales of a gathered Linear-1 in
 //            grouped row order
-//   the single-launch decode layer's regions (bf16 layers with T*K <= kSmallPermPairs, else empty):
+//   the single-launch decode layer's regions (bf16 and MX layers with T*K <= kSmallPermPairs, else
+//   empty):
 //   dctrl    kDecodeCtrlInts int32 control block (task counters, flags, the m-tile prefix)
 //   dlogits  [S][T][E] fp32 partial router logits (S = decode_router_splits)
 //   dhsh     [T][I_shared] SwiGLU output of the shared expert (bf16, MX: e4m3 codes; the routed
@@ -32,9 +33,10 @@ namespace moe {
 //   dhshs    MX: its scale words [I_shared/128][T]
 //   dxq      MX: [T][H] e4m3 codes of x, then dxqs: their scale words [H/128][T]
 //   dflags   kDecodeFlagBytes: the flags many workgroups poll, in copies 4 KiB apart
+//   dcnt     [T][ceil(H/256)] int32 arrival counters of the combine in the Linear-2 epilogue
 struct WsLayout {
   size_t err = 0, logits = 0, wrt = 0, hist = 0, base = 0, tiles = 0, part = 0, h = 0, hscale = 0, xscale = 0,
-         dctrl = 0, dlogits = 0, dhsh = 0, dhshs = 0, dxq = 0, dxqs = 0, dflags = 0, total = 0;
+         dctrl = 0, dlogits = 0, dhsh = 0, dhshs = 0, dxq = 0, dxqs = 0, dflags = 0, dcnt = 0, total = 0;
   int route_splits = 1;
   int perm_blocks = 0;
 };
@@ -168,6 +170,7 @@ struct DecodeCall {
   int32_t* err = nullptr;     // workspace
   int32_t* ctrl = nullptr;    // workspace
   int32_t* flags = nullptr;   // workspace
+  int32_t* cnt = nullptr;     // workspace
   float* logits = nullptr;    // workspace
   void* h = nullptr;          // workspace
   void* h_scale = nullptr;    // workspace (MX)

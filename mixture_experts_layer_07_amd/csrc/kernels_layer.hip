@@ -11,18 +11,20 @@
 //
 // Work is a fixed sequence of segments; every workgroup walks them in order, pulling tasks from
 // one counter per segment, and a task waits only for tasks of earlier segments:
-//   0 router     32 x 256 tiles of the router GEMM z = x W_r (K-major W_r) over a piece of H:
+//   0 zero       4096 words of the combine's arrival counters set to zero
+//   1 router     32 x 256 tiles of the router GEMM z = x W_r (K-major W_r) over a piece of H:
 //                partial logits, fp32 (the grouped-GEMM tile code with one "expert")
-//   1 quantise   (MX layers) 4 rows of x to MXFP8 codes and scales (one per wave)
-//   2 shared L1  32 x 256 tiles of the shared expert's gate/up GEMM with SwiGLU (reads x, or its
+//   2 quantise   (MX layers) 4 rows of x to MXFP8 codes and scales (one per wave)
+//   3 shared L1  32 x 256 tiles of the shared expert's gate/up GEMM with SwiGLU (reads x, or its
 //                MXFP8 codes, only)
-//   3 top-K      one token: waits for the router tiles of its 32-token block; the task that
+//   4 top-K      one token: waits for the router tiles of its 32-token block; the task that
 //                completes the last token runs the one-workgroup counting sort and the m-tile
 //                prefix of the routed experts, and announces "routing ready"
-//   4 routed L1  32 x 256 tiles over the expert-grouped pairs (rows gathered from x in place)
-//   5 shared L2  waits for the shared L1 tiles of its m-tile
-//   6 routed L2  waits for the L1 tiles of its expert m-tile
-//   7 combine    token x 2048-channel block: waits for every Linear-2 tile
+//   5 routed L1  32 x 256 tiles over the expert-grouped pairs (rows gathered from x in place)
+//   6 shared L2  waits for the shared L1 tiles of its m-tile
+//   7 routed L2  waits for the L1 tiles of its expert m-tile
+// The weighted combine has no segment of its own: it runs in the Linear-2 epilogue (see
+// arrive_combine below).
 // The expert GEMM tiles are those of the separate GEMM kernels (bf16: 32 x 256 tiles through two
 // LDS stages; MX: the three-stage 32 x 256 tiles on the scaled MFMA), the router's always bf16.
 // Tasks are pulled in list order (expert-major for the GEMMs), so the Linear-1 tiles finish
@@ -41,8 +43,7 @@
 // at agent scope (its L1 and L2 invalidated, so no stale line of an earlier call is read) before
 // reading. A release fence would do the producer's part as well, but it writes back the whole L2
 // of the XCD and costs a workgroup about as long as streaming a few hundred KB, once per tile.
-// Linear-2 completions are counted once per workgroup, as it leaves that segment (only the
-// combine waits for them, and for all of them). A workgroup entering Linear-2 reads every
+// A workgroup entering Linear-2 reads every
 // Linear-1 m-tile counter once; a Linear-2 tile whose m-tile was then complete does not poll.
 // Every result is computed by one workgroup in a fixed order, so the layer is deterministic.
 //
@@ -69,14 +70,15 @@ namespace moe {
 
 namespace dec {
 constexpr int kSegs = 8;
-enum Seg { kRouter = 0, kQuant, kSh1, kTopk, kL1, kSh2, kL2, kComb };
+enum Seg { kZero = 0, kRouter, kQuant, kSh1, kTopk, kL1, kSh2, kL2 };
+constexpr int kZeroWords = 4096;  // arrival counters zeroed per task
 constexpr int kMaxTokBlocks = kSmallPermPairs / 32;  // 32-token router m-tiles (T <= P <= 4096)
 constexpr int kMaxMTiles = kSmallPermPairs / 32 + kMaxExperts;
 // control block (int32 words)
 constexpr int kQ = 0;                              // [kSegs] task counters
 constexpr int kTopkDone = kQ + kSegs;              // top-K tasks done
-constexpr int kL2Done = kTopkDone + 1;             // Linear-2 tiles done (routed and shared)
-constexpr int kQuantDone = kL2Done + 1;            // MX: MXFP8 quantisation tasks of x done
+constexpr int kZeroDone = kTopkDone + 1;           // zeroing tasks of the arrival counters done
+constexpr int kQuantDone = kZeroDone + 1;          // MX: MXFP8 quantisation tasks of x done
 constexpr int kAbort = kQuantDone + 1;             // a wait ran past its limit
 constexpr int kExit = kAbort + 1;                  // workgroups finished
 constexpr int kShOff = kExit + 1;                  // offsets {0, T} of the one-"expert" GEMMs
@@ -88,23 +90,24 @@ constexpr int kClear = kTp + kMaxExperts + 1;         // words cleared at the st
 constexpr int kEpoch = (kClear + 1) & ~1;             // 64-bit launch epoch
 static_assert(kShOff + 2 <= kRouterDone, "control block layout");
 static_assert(kEpoch + 2 <= kDecodeCtrlInts, "control block too small");
-static_assert(3 + kMaxTokBlocks <= 1024, "flags of one copy within its 4 KiB");
 constexpr unsigned long long kWaitLimit = 200000000ull;  // 2 s of the 100 MHz real-time counter
-// Flags that many workgroups wait on at once (routing ready, every Linear-2 tile done) are kept in
+// Flags that many workgroups wait on at once (routing ready, the MXFP8 codes of x) are kept in
 // kFlagCopies copies kFlagStride words apart, workgroup b polling copy b % kFlagCopies, so that the
 // polls spread over the memory channels instead of queueing on one.
 constexpr int kFlagCopies = 64;
 constexpr int kFlagStride = 1024;  // (4 KiB)
-constexpr int kFlagReady = 0, kFlagAllDone = 1, kFlagQuant = 2;
-constexpr int kFlagRouter = 3;  // [kMaxTokBlocks]: every router tile of 32-token m-tile m done
+constexpr int kFlagReady = 0, kFlagQuant = 1;
+constexpr int kFlagRouter = 2;  // [kMaxTokBlocks]: every router tile of 32-token m-tile m done
+static_assert(kFlagRouter + kMaxTokBlocks <= 1024, "flags of one copy within its 4 KiB");
 }  // namespace dec
 
 struct DecodeArgs {
   TopkParams tk;          // tk.splits = router K pieces S
   const float* bias;      // [E] or nullptr
   int T, H, E, K;
-  int mts, nyb;           // 32-token m-tiles, combine blocks per token
+  int mts, nb2;           // 32-token m-tiles, 256-column blocks of a Linear-2 output row
   int has_shared, out_f32;
+  int need;               // rows a token's output block sums: K (+ 1 with a shared expert)
   unsigned long long epoch;
   float* logits;          // [S][T][E] partial logits
   int32_t* ids;
@@ -116,6 +119,7 @@ struct DecodeArgs {
   int32_t* err;           // device error word
   int32_t* ctrl;          // control block
   int32_t* flags;         // kFlagCopies x kFlagStride words: the polled flags
+  int32_t* cnt;           // [T][nb2] arrival counters of the combine
   const uint8_t* x;       // MX: the layer input [T][H] bf16, quantised by the kQuant tasks into
   uint8_t* xq;            //     xq [T][H] e4m3 codes and
   uint32_t* xqs;          //     xqs, the MX scale array of its T rows ([H/128][T] words)
@@ -203,14 +207,44 @@ __device__ __forceinline__ bool wait_geq(const DecodeArgs& a, const int32_t* p, 
 // K piece p of S over KT steps: an even number of steps, at least two (S <= KT / 2).
 __device__ __forceinline__ int piece_k(int p, int S, int KT) { return (int)((long long)p * (KT / 2) / S) * 2; }
 
-// ---------------------------------------------------------------- combine task
+// ---------------------------------------------------------------- combine in the Linear-2 epilogue
+// The weighted combine fused into Linear-2 ("MoE 优化的探索", 3.6.2 and 3.7.3: the reduce
+// happens as the second GEMM's tiles finish, with an arrival count per token rather than a pass
+// of its own). All threads call, after a Linear-2 tile (routed: its rows are expert-grouped pairs;
+// shared: its rows are tokens) has stored its y rows with device-scope stores. Each row counts one
+// arrival on its token's counter for the tile's 256-column block; the arrival that completes the
+// count (K routed rows, plus the shared row) acquires and combines that block of the token's
+// output row (combine_chunk: fp32 in k order, the shared row last, one rounding), so every output
+// value is still summed by one workgroup in a fixed order and the result matches the separate
+// combine bit for bit. s_list: 33 ints of LDS.
 template <bool OF32>
-__device__ __forceinline__ void combine_task(const DecodeArgs& a, int task, int* spp, float* sw) {
-  const int t = task / a.nyb, yb = task - t * a.nyb;
-  switch (a.K) {
-    case 8: combine_block<8, false, OF32, 8, 1>(t, yb, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K, spp, sw); break;
-    case 2: combine_block<8, false, OF32, 2, 1>(t, yb, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K, spp, sw); break;
-    default: combine_block<8, false, OF32, 0, 1>(t, yb, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K, spp, sw);
+__device__ __forceinline__ void arrive_combine(const DecodeArgs& a, const TileInfo& ti, bool routed_rows, int* s_list) {
+  const int tid = opaque_tid();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (tid == 0) s_list[32] = 0;
+  __syncthreads();
+  if (tid < ti.mvalid) {  // (32-row tiles: wave 0)
+    const int gr = ti.row0 + tid;
+    const int t = routed_rows ? a.sorted_pair[gr] / a.K : gr;
+    const int old = __hip_atomic_fetch_add(a.cnt + (size_t)t * a.nb2 + ti.nt, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    if (old == a.need - 1) s_list[atomicAdd(s_list + 32, 1)] = t;
+  }
+  __syncthreads();
+  const int n = __builtin_amdgcn_readfirstlane(s_list[32]);
+  if (n == 0) return;
+  if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // (the other rows' y, by wave 0)
+  __syncthreads();
+  const int ch = ti.nt * 32 + (tid & 31);  // 8-channel chunk of this thread; eight tokens at a time
+  if (ch < a.H / 8) {
+    for (int j = tid >> 5; j < n; j += 8) {
+      const int t = s_list[j];
+      switch (a.K) {
+        case 8: combine_chunk<OF32, 8>(t, ch, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K); break;
+        case 2: combine_chunk<OF32, 2>(t, ch, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K); break;
+        default: combine_chunk<OF32, 0>(t, ch, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K);
+      }
+    }
   }
 }
 
@@ -252,6 +286,7 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
   __shared__ int s_tps[2];
   __shared__ int s_slot[4];
   __shared__ int s_l1ok[dec::kMaxMTiles];
+  __shared__ int s_list[33];
   const int tid = threadIdx.x;
   int32_t* ctrl = a.ctrl;
   unsigned long long* epoch = reinterpret_cast<unsigned long long*>(ctrl + dec::kEpoch);
@@ -297,9 +332,8 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
   const int S = a.tk.splits;
   const int rtiles = a.mts * a.gr.n_tiles_n;  // router tiles per K piece
   bool routed = false;  // s_tp holds the routed m-tile prefix
-  bool l2_all = false;  // every Linear-2 tile is done (the combine may run)
+  bool zeroed = false;  // the arrival counters are known to be zero
   bool alive = true;
-  int n_l2 = 0;    // Linear-2 tiles (routed and shared) done and not yet counted
   bool snap = false;  // s_l1ok holds a snapshot of the Linear-1 m-tile counters
   bool quant = !MX;   // the MXFP8 codes of x are complete
   float* f0 = reinterpret_cast<float*>(sB0);
@@ -311,7 +345,12 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
       if (!alive) break;
       quant = true;
     }
-    if ((seg == dec::kL1 || seg == dec::kL2 || seg == dec::kComb) && !routed) {
+    if ((seg == dec::kSh2 || seg == dec::kL2) && !zeroed) {
+      alive = wait_geq(a, ctrl + dec::kZeroDone, (a.T * a.nb2 + dec::kZeroWords - 1) / dec::kZeroWords, s_slot);
+      if (!alive) break;
+      zeroed = true;
+    }
+    if ((seg == dec::kL1 || seg == dec::kL2) && !routed) {
       alive = wait_geq(a, a.flags + (blockIdx.x % dec::kFlagCopies) * dec::kFlagStride + dec::kFlagReady, 1, s_slot);
       if (!alive) break;
       for (int i = tid; i <= a.E; i += 256) s_tp[i] = ctrl[dec::kTp + i];
@@ -320,14 +359,14 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
     }
     int n = 0;
     switch (seg) {
+      case dec::kZero: n = (a.T * a.nb2 + dec::kZeroWords - 1) / dec::kZeroWords; break;
       case dec::kRouter: n = rtiles * S; break;
       case dec::kQuant: n = MX ? (a.T + 3) / 4 : 0; break;
       case dec::kSh1: n = a.has_shared ? a.mts * a.s1.n_tiles_n : 0; break;
       case dec::kTopk: n = a.T; break;
       case dec::kL1: n = s_tp[a.E] * a.g1.n_tiles_n; break;
       case dec::kSh2: n = a.has_shared ? a.mts * a.s2.n_tiles_n : 0; break;
-      case dec::kL2: n = s_tp[a.E] * a.g2.n_tiles_n; break;
-      default: n = a.T * a.nyb; break;
+      default: n = s_tp[a.E] * a.g2.n_tiles_n; break;  // routed L2
     }
     for (;;) {
       int task = n;
@@ -337,26 +376,17 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
         task = __builtin_amdgcn_readfirstlane(s_slot[0]);
         __syncthreads();
       }
-      if (task >= n) {
-        // leaving Linear-2: count this workgroup's Linear-2 tiles (and shared ones) as done
-        if (seg == dec::kL2 && n_l2 > 0) {
-          const int total = s_tp[a.E] * a.g2.n_tiles_n + (a.has_shared ? a.mts * a.s2.n_tiles_n : 0);
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          if (tid == 0)
-            s_slot[0] = __hip_atomic_fetch_add(ctrl + dec::kL2Done, n_l2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __syncthreads();
-          if (__builtin_amdgcn_readfirstlane(s_slot[0]) + n_l2 == total) raise_flag(a.flags, dec::kFlagAllDone);
-          n_l2 = 0;
-        }
-        break;
-      }
+      if (task >= n) break;
       WorkItem w;
       w.tile = task;
       w.piece = -1;
       w.slot = w.first = 0;
       w.k0 = 0;
-      if (seg == dec::kRouter) {
+      if (seg == dec::kZero) {
+        const int w0 = task * dec::kZeroWords, w1 = min(w0 + dec::kZeroWords, a.T * a.nb2);
+        for (int i = w0 + tid; i < w1; i += 256) store_dev<true>(a.cnt + i, (int32_t)0);
+        handoff_add(ctrl + dec::kZeroDone, 1);
+      } else if (seg == dec::kRouter) {
         // piece p of H for router tile `tile`: its partial logits go to slice p
         const int p = task / rtiles;
         w.tile = task - p * rtiles;
@@ -480,7 +510,7 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
         const TileInfo ti = decode_tile(task, s_tps, a.s2, 32);
         if (!(alive = wait_geq(a, ctrl + dec::kL1sDone + ti.mt, a.s1.n_tiles_n, s_slot))) break;
         expert_tile<MX, false>(a.s2, s_tps, task, sA0, sA1, sB0, sB1, s_slot);
-        ++n_l2;
+        arrive_combine<OF32>(a, ti, false, s_list);
       } else if (seg == dec::kL2) {
         const TileInfo ti = decode_tile(task, s_tp, a.g2, 32);
         const int m = s_tp[ti.e] + ti.mt;
@@ -493,15 +523,7 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
           snapshot_l1(ctrl, s_tp[a.E], a.g1.n_tiles_n, s_l1ok);
         }
         expert_tile<MX, false>(a.g2, s_tp, task, sA0, sA1, sB0, sB1, s_slot);
-        ++n_l2;
-      } else {
-        if (!l2_all) {
-          if (!(alive = wait_geq(a, a.flags + (blockIdx.x % dec::kFlagCopies) * dec::kFlagStride + dec::kFlagAllDone,
-                                 1, s_slot)))
-            break;
-          l2_all = true;
-        }
-        combine_task<OF32>(a, task, reinterpret_cast<int*>(sA0), reinterpret_cast<float*>(sA0) + kMaxExperts);
+        arrive_combine<OF32>(a, ti, true, s_list);
       }
     }
   }
@@ -581,8 +603,9 @@ hipError_t launch_layer_decode(const DecodeCall& d, hipStream_t s) {
   a.tk.group_top2 = c.group_score == MOE_GROUP_TOP2_SUM;
   a.tk.route_scale = c.route_scale;
   a.mts = (c.T + 31) / 32;
-  a.nyb = (c.H / 8 + 255) / 256;
+  a.nb2 = (c.H + 255) / 256;
   a.has_shared = c.I_shared > 0;
+  a.need = c.K + (a.has_shared ? 1 : 0);
   a.out_f32 = c.out_dtype == MOE_F32;
   a.epoch = next_epoch();
   a.logits = d.logits;
@@ -595,6 +618,7 @@ hipError_t launch_layer_decode(const DecodeCall& d, hipStream_t s) {
   a.err = d.err;
   a.ctrl = d.ctrl;
   a.flags = d.flags;
+  a.cnt = d.cnt;
   a.y = static_cast<const uint8_t*>(d.y_perm);
   a.ysh = a.has_shared ? static_cast<const uint8_t*>(d.y_shared) : nullptr;
   a.out = static_cast<uint8_t*>(d.out);

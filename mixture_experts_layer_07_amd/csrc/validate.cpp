@@ -158,6 +158,8 @@ WsLayout layout(const moe_config& c) {
   off = align256(off + (dmx ? T * (H / 128) * 4 : 0));
   L.dflags = off;
   off = align256(off + (dec ? kDecodeFlagBytes : 0));
+  L.dcnt = off;
+  off = align256(off + (dec ? T * (size_t)((c.H + 255) / 256) * 4 : 0));
   L.total = off;
   return L;
 }
