@@ -162,9 +162,10 @@ __device__ __forceinline__ void raise_flag(int32_t* flags, int f) {
 }
 
 // Polling: every poll is a read at the memory side (agent scope), and hundreds of workgroups may
-// wait on one counter at once (for the routing, at the end for the last Linear-2 tiles), so the
-// interval between polls doubles from about 0.25 us up to about 4 us; a wait gives up after
-// kWaitLimit of the 100 MHz real-time counter.
+// wait on one counter at once (for the routing, most of the grid), so the interval between polls
+// doubles from about 0.2 us up to about 3.4 us. (Capping it at 0.4 us for the waits of the
+// routing phase made the layer slower: the extra polls delay the latency-bound router tiles.)
+// A wait gives up after kWaitLimit of the 100 MHz real-time counter.
 __device__ __forceinline__ void poll_pause(int units) {
   for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(8);  // (about 512 cycles each)
 }
@@ -216,21 +217,28 @@ __device__ __forceinline__ int piece_k(int p, int S, int KT) { return (int)((lon
 // count (K routed rows, plus the shared row) acquires and combines that block of the token's
 // output row (combine_chunk: fp32 in k order, the shared row last, one rounding), so every output
 // value is still summed by one workgroup in a fixed order and the result matches the separate
-// combine bit for bit. s_list: 33 ints of LDS.
+// combine bit for bit. The workgroup's next task of the segment is pulled from queue q in the
+// same round trip as the arrivals (returned in `next`). s_list: 34 ints of LDS.
 template <bool OF32>
-__device__ __forceinline__ void arrive_combine(const DecodeArgs& a, const TileInfo& ti, bool routed_rows, int* s_list) {
+__device__ __forceinline__ void arrive_combine(const DecodeArgs& a, const TileInfo& ti, bool routed_rows, int* q,
+                                               int* s_list, int& next) {
   const int tid = opaque_tid();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (tid == 0) s_list[32] = 0;
   __syncthreads();
-  if (tid < ti.mvalid) {  // (32-row tiles: wave 0)
-    const int gr = ti.row0 + tid;
-    const int t = routed_rows ? a.sorted_pair[gr] / a.K : gr;
-    const int old = __hip_atomic_fetch_add(a.cnt + (size_t)t * a.nb2 + ti.nt, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    if (old == a.need - 1) s_list[atomicAdd(s_list + 32, 1)] = t;
+  if (tid < 64) {  // (32-row tiles: the rows' arrivals in lanes 0..31, the pull in lane 32)
+    int t = 0, old = 0, nq = 0;
+    if (tid < ti.mvalid) {
+      const int gr = ti.row0 + tid;
+      t = routed_rows ? a.sorted_pair[gr] / a.K : gr;
+      old = __hip_atomic_fetch_add(a.cnt + (size_t)t * a.nb2 + ti.nt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 32) nq = atomicAdd(q, 1);
+    if (tid < ti.mvalid && old == a.need - 1) s_list[atomicAdd(s_list + 32, 1)] = t;
+    if (tid == 32) s_list[33] = nq;
   }
   __syncthreads();
+  next = __builtin_amdgcn_readfirstlane(s_list[33]);
   const int n = __builtin_amdgcn_readfirstlane(s_list[32]);
   if (n == 0) return;
   if (tid < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // (the other rows' y, by wave 0)
@@ -246,6 +254,57 @@ __device__ __forceinline__ void arrive_combine(const DecodeArgs& a, const TileIn
       }
     }
   }
+}
+
+// ---------------------------------------------------------------- router tiles
+// One router task: tile ti (32 tokens x 256 experts) of z = x W_r over the 64-channel steps
+// [k0, k1) of H (an even count). A piece is a few steps long, so rather than a pipeline it takes
+// two steps at a time with every load in flight at once: both operands go straight into the two
+// LDS stages (x rows and K-major W_r rows, clamped into their arrays), one wait, then the MFMAs
+// (32x32x16 bf16, four waves of 32 x 64). The fp32 partial logits leave with device-scope stores
+// (rows past T and columns past E are not stored). All threads of the workgroup call.
+__device__ __forceinline__ void router_piece(const GemmArgs& g, const TileInfo& ti, int k0, int k1, int T, int E,
+                                             u32x4* sA0, u32x4* sA1, u32x4* sB0, u32x4* sB1) {
+  const int tid = opaque_tid(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the chunk of one A row and of eight weight rows that this lane moves per step (byte offsets)
+  const int ra = wave * 8 + (lane >> 3);
+  const int xr = min(ti.row0 + ra, T - 1);
+  const uint32_t oa = (uint32_t)xr * (uint32_t)g.lda + (uint32_t)dma_chunk(ra, lane) * 16u;
+  uint32_t ob[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rb = (j * 4 + wave) * 8 + (lane >> 3);
+    const int er = min(ti.nt * 256 + rb, E - 1);
+    ob[j] = (uint32_t)er * (uint32_t)g.ldb + (uint32_t)dma_chunk(rb, lane) * 16u;
+  }
+  f32x16 acc[1][2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[0][nb][i] = 0.f;
+  for (int k = k0; k < k1; k += 2) {
+    if (k > k0) __syncthreads();  // (every wave's fragment reads of the last round are done)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      u32x4* sa = st ? sA1 : sA0;
+      u32x4* sb = st ? sB1 : sB0;
+      const uint32_t koff = (uint32_t)(k + st) * 128u;
+      dma_to_lds<16>(g.A + (oa + koff), sa + wave * 64);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dma_to_lds<16>(g.B + (ob[j] + koff), sb + (j * 4 + wave) * 64);
+    }
+    dma_wait_and_barrier();
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 fa[1], fb[2];
+        w4::frags<1, 2>(st ? sA1 : sA0, st ? sB1 : sB0, ks, 0, wave * 64, lane, fa, fb);
+        w4::mfmas<1, 2>(acc, fa, fb);
+      }
+  }
+  w4::epilogue<1, 2, false, true, kCpolSc1>(g, ti, acc, 0, wave * 64, lane);
 }
 
 // ---------------------------------------------------------------- expert GEMM tiles
@@ -286,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
   __shared__ int s_tps[2];
   __shared__ int s_slot[4];
   __shared__ int s_l1ok[dec::kMaxMTiles];
-  __shared__ int s_list[33];
+  __shared__ int s_list[34];
   const int tid = threadIdx.x;
   int32_t* ctrl = a.ctrl;
   unsigned long long* epoch = reinterpret_cast<unsigned long long*>(ctrl + dec::kEpoch);
@@ -328,7 +387,6 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
   __syncthreads();
   if (blockIdx.x != 0 && !__builtin_amdgcn_readfirstlane(s_slot[1])) return;
 
-  const SplitQueue sq0 = {0, 0, 1, 0, 0, 0};  // (whole work items: no hand-over of K pieces)
   const int S = a.tk.splits;
   const int rtiles = a.mts * a.gr.n_tiles_n;  // router tiles per K piece
   bool routed = false;  // s_tp holds the routed m-tile prefix
@@ -368,35 +426,31 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
       case dec::kSh2: n = a.has_shared ? a.mts * a.s2.n_tiles_n : 0; break;
       default: n = s_tp[a.E] * a.g2.n_tiles_n; break;  // routed L2
     }
+    int pre = -1;  // a task of this segment already pulled (by the Linear-2 epilogue)
     for (;;) {
       int task = n;
-      if (n > 0) {
+      if (pre >= 0) {
+        task = pre;
+        pre = -1;
+      } else if (n > 0) {
         if (tid == 0) s_slot[0] = atomicAdd(&ctrl[dec::kQ + seg], 1);
         __syncthreads();
         task = __builtin_amdgcn_readfirstlane(s_slot[0]);
         __syncthreads();
       }
       if (task >= n) break;
-      WorkItem w;
-      w.tile = task;
-      w.piece = -1;
-      w.slot = w.first = 0;
-      w.k0 = 0;
       if (seg == dec::kZero) {
         const int w0 = task * dec::kZeroWords, w1 = min(w0 + dec::kZeroWords, a.T * a.nb2);
         for (int i = w0 + tid; i < w1; i += 256) store_dev<true>(a.cnt + i, (int32_t)0);
         handoff_add(ctrl + dec::kZeroDone, 1);
       } else if (seg == dec::kRouter) {
-        // piece p of H for router tile `tile`: its partial logits go to slice p
+        // piece p of H for router tile task - p * rtiles: its partial logits go to slice p
         const int p = task / rtiles;
-        w.tile = task - p * rtiles;
         const int KT = a.gr.K / 64;
-        w.k0 = piece_k(p, S, KT);
-        w.k1 = piece_k(p + 1, S, KT);
         GemmArgs g = a.gr;
         g.C += (size_t)p * a.T * a.E * 4;
-        m32_item<false, true, false, kCpolSc1>(g, s_tps, w, sq0, sA0, sA1, sB0, sB1, s_slot);
-        const TileInfo ti = decode_tile(w.tile, s_tps, a.gr, 32);
+        const TileInfo ti = decode_tile(task - p * rtiles, s_tps, a.gr, 32);
+        router_piece(g, ti, piece_k(p, S, KT), piece_k(p + 1, S, KT), a.T, a.E, sA0, sA1, sB0, sB1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0)
@@ -421,64 +475,38 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
         const TileInfo ti = decode_tile(task, s_tps, a.s1, 32);
         handoff_add(ctrl + dec::kL1sDone + ti.mt, 1);
       } else if (seg == dec::kTopk) {
-        // token `task`: its router m-tile's every n-tile and piece must be done; the four waves
-        // stage the S partial logits in LDS (one round of loads), then wave 0 sums them in split
-        // order and selects
+        // token `task`: the bias goes to LDS while the router tiles of the token's 32-token block
+        // finish; then thread e sums expert e's S partial logits in split order straight from
+        // memory (loads 32 at a time), and wave 0 selects
+        float* zs = f0;        // [256] the token's logits
+        float* bs = f0 + 256;  // [256] the bias
+        if (a.bias && tid < a.E) bs[tid] = a.bias[tid];
         if (!(alive = wait_geq(a, a.flags + (blockIdx.x % dec::kFlagCopies) * dec::kFlagStride + dec::kFlagRouter +
                                       task / 32, 1, s_slot)))
           break;
         {
-          // loads in flight eight at a time (S * E / 4 <= 64 * 64: at most two rounds), then the
-          // LDS stores
-          const int E4 = a.E / 4, n4 = S * E4;
-          for (int i0 = 0; i0 < n4; i0 += 8 * 256) {
-            f32x4 v[8];
+          const int e = tid < a.E ? tid : a.E - 1;  // (clamped: every load in bounds)
+          const float* src = a.logits + (size_t)task * a.E + e;
+          const size_t stride = (size_t)a.T * a.E;
+          float z = 0.f;
+          for (int s0 = 0; s0 < S; s0 += 32) {
+            float v[32];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int i = i0 + tid + 256 * u;
-              if (i < n4) {
-                const int sp = i / E4, c = i - sp * E4;
-                v[u] = reinterpret_cast<const f32x4*>(a.logits + ((size_t)sp * a.T + task) * a.E)[c];
-              }
-            }
+            for (int u = 0; u < 32; ++u) v[u] = src[(size_t)(s0 + u < S ? s0 + u : S - 1) * stride];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int i = i0 + tid + 256 * u;
-              if (i < n4) {
-                const int sp = i / E4, c = i - sp * E4;
-                reinterpret_cast<f32x4*>(sp < 32 ? f0 + sp * 256 : f1 + (sp - 32) * 256)[c] = v[u];
-              }
-            }
+            for (int u = 0; u < 32; ++u)
+              if (s0 + u < S) z += v[u];
           }
+          zs[tid] = tid < a.E ? z : -INFINITY;
         }
         __syncthreads();
         if (tid < 64) {
-          // the partial logits summed in split order, eight rows read ahead at a time
           float z[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) z[j] = 0.f;
-          for (int s0 = 0; s0 < S; s0 += 8) {
-            float r[8][4];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int sp = s0 + u < S ? s0 + u : S - 1;
-              const float* row = sp < 32 ? f0 + sp * 256 : f1 + (sp - 32) * 256;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) r[u][j] = row[tid + 64 * j];
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-              if (s0 + u < S) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) z[j] += r[u][j];
-              }
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (tid + 64 * j >= a.E) z[j] = -INFINITY;
+          for (int j = 0; j < 4; ++j) z[j] = zs[tid + 64 * j];
           float* lw = reinterpret_cast<float*>(sA0);  // (4 KB: the selection's scratch)
-          topk_select<true>(z, a.bias, a.tk, a.ids, a.weights, task, lw, reinterpret_cast<int*>(lw + 256),
-                            reinterpret_cast<int*>(lw + 512), lw + 768);
+          topk_select<true>(z, a.bias ? bs : nullptr, a.tk, a.ids, a.weights, task, lw,
+                            reinterpret_cast<int*>(lw + 256), reinterpret_cast<int*>(lw + 512), lw + 768);
         }
         // the top-K task that completes the count runs the permutation right away
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -510,7 +538,7 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
         const TileInfo ti = decode_tile(task, s_tps, a.s2, 32);
         if (!(alive = wait_geq(a, ctrl + dec::kL1sDone + ti.mt, a.s1.n_tiles_n, s_slot))) break;
         expert_tile<MX, false>(a.s2, s_tps, task, sA0, sA1, sB0, sB1, s_slot);
-        arrive_combine<OF32>(a, ti, false, s_list);
+        arrive_combine<OF32>(a, ti, false, ctrl + dec::kQ + seg, s_list, pre);
       } else if (seg == dec::kL2) {
         const TileInfo ti = decode_tile(task, s_tp, a.g2, 32);
         const int m = s_tp[ti.e] + ti.mt;
@@ -523,7 +551,7 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
           snapshot_l1(ctrl, s_tp[a.E], a.g1.n_tiles_n, s_l1ok);
         }
         expert_tile<MX, false>(a.g2, s_tp, task, sA0, sA1, sB0, sB1, s_slot);
-        arrive_combine<OF32>(a, ti, true, s_list);
+        arrive_combine<OF32>(a, ti, true, ctrl + dec::kQ + seg, s_list, pre);
       }
     }
   }
