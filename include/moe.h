@@ -236,8 +236,10 @@ moe_status moe_combine(const moe_config* cfg, const int32_t* pair_pos, const flo
  * quantisation of x) in one kernel launch, for decode-sized batches. The persistent-kernel design
  * of "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4" (wqh011128.github.io, 4.1-4.7)
  * and the fused dispatch-to-combine kernel of "DeepGEMM质变：从GEMM库到统一LLM计算原语平台"
- * (itsolotime.com, 1.2), on one GPU: the workgroups pull router, quantisation, top-K, GEMM-tile
- * and combine tasks in a fixed order and hand results over through counters in the workspace.
+ * (itsolotime.com, 1.2), on one GPU: the workgroups pull router, quantisation, top-K and GEMM-tile
+ * tasks in a fixed order and hand results over through counters in the workspace; the weighted
+ * combine runs in the Linear-2 epilogue (a per-token arrival count per 256-column block; the
+ * arrival that completes a block sums it in k order, bit-identical to moe_combine).
  *   Supported: dtype MOE_BF16 or MOE_MXFP4, T*K <= 4096, E a multiple of 8 (MOE_ERR_UNSUPPORTED
  *   otherwise, before any device call).
  *   x, bias             as moe_route (bf16 x [T,H]; bias [E] fp32 or NULL)

@@ -13,7 +13,7 @@
 // one counter per segment, and a task waits only for tasks of earlier segments:
 //   0 zero       4096 words of the combine's arrival counters set to zero
 //   1 router     32 x 256 tiles of the router GEMM z = x W_r (K-major W_r) over a piece of H:
-//                partial logits, fp32 (the grouped-GEMM tile code with one "expert")
+//                partial logits, fp32 (router_piece below)
 //   2 quantise   (MX layers) 4 rows of x to MXFP8 codes and scales (one per wave)
 //   3 shared L1  32 x 256 tiles of the shared expert's gate/up GEMM with SwiGLU (reads x, or its
 //                MXFP8 codes, only)
@@ -43,11 +43,12 @@
 // at agent scope (its L1 and L2 invalidated, so no stale line of an earlier call is read) before
 // reading. A release fence would do the producer's part as well, but it writes back the whole L2
 // of the XCD and costs a workgroup about as long as streaming a few hundred KB, once per tile.
-// A workgroup entering Linear-2 reads every
-// Linear-1 m-tile counter once; a Linear-2 tile whose m-tile was then complete does not poll.
+// A workgroup entering Linear-2 reads every Linear-1 m-tile counter once; a Linear-2 tile whose
+// m-tile was then complete does not poll.
 // Every result is computed by one workgroup in a fixed order, so the layer is deterministic.
 //
-// The control block (counters, flags, the routed m-tile prefix) sits in the workspace. Every
+// The control block (counters, flags, the routed m-tile prefix) sits in the workspace (the
+// combine's arrival counters beside it are zeroed by segment 0 of every launch). Every
 // launch carries a 64-bit epoch, unique per host call. If the block does not hold the launch's
 // epoch yet, workgroup 0 clears the counters and then publishes the epoch, and the other
 // workgroups wait for it before touching a counter; the last workgroup to finish clears the
