@@ -5,8 +5,9 @@ Every stage's output (ids and weights, counts / offsets / sorted_pair / pair_pos
 shared expert rows, the layer output) against the CPU oracle with the bars of the multi-launch
 path, at small shapes spanning several tiles, token blocks and ragged tails, at the largest pair
 count the kernel takes, and at the decode workload's full size on sampled rows and tokens; plus
-equality with the multi-launch path, determinism, back-to-back calls on one workspace with new
-inputs, HIP-graph replays, and a clear device error word after every case.
+equality with the multi-launch path, the fused combine bit for bit against moe_combine on the
+launch's own expert rows, determinism, back-to-back calls on one workspace with new inputs,
+HIP-graph replays, and a clear device error word after every case.
 """
 import numpy as np
 import pytest
@@ -136,6 +137,24 @@ def test_decode_layer_graph_replays_match_eager(name):
     graph.replay()
     torch.cuda.synchronize()
     assert torch.equal(L.out, want2), "replay on new inputs"
+    assert B.moe_get_device_error(L.ws) == 0
+
+
+@pytest.mark.parametrize("name", ["decode-grouped-shared", "decode-softmax-noshared", "decode-bf16out",
+                                  "decode-ragged", "mx-decode-shared", "mx-decode-noshared", "full-4", "full-8"])
+def test_decode_layer_combine_equals_moe_combine(name):
+    """The combine in the Linear-2 epilogue (per-token arrival counts, the last arrival of a
+    256-column block sums it) against moe_combine run afterwards on the launch's own pair_pos,
+    topk_weights, y rows and y_shared: the same bits, at small shapes (with and without a shared
+    expert, K = 2, 4, 8, fp32 and bf16 outputs, a half last column block) and at full size."""
+    print(f"decode layer combine case {name}", flush=True)
+    case = Case(CONFIGS[int(name[5:])], wdev="cuda", fused=True) if name.startswith("full-") else _case(name)
+    L = case.layer
+    case.run()
+    out2 = torch.empty_like(L.out)
+    B.moe_combine(L.c, L.pair_pos, L.topk_weights, L.y_perm, L.y_shared, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(L.out, out2)
     assert B.moe_get_device_error(L.ws) == 0
 
 
