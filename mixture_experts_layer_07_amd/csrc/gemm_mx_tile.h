@@ -26,9 +26,7 @@
 // 从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", 5.1): each wave holds exactly one 32-column
 // block of h per row, so the block maximum is a reduction over its 32 lanes; the scale code is
 // the maximum's binary exponent minus 8 (clamped at 0), the codes e4m3(h * 2^(127 - code)).
-// Pipeline as in the fp8 kernels: two LDS stages, one barrier per K step; A arrives by
-// direct-to-LDS loads one step ahead, the weights through registers two steps ahead, the scale
-// words in registers one step ahead.#pragma once
+#pragma once
 
 #include "gemm_common.h"
 

@@ -7,6 +7,8 @@
 namespace moe {
 
 // BM x BN tiles, NWM x NWN waves of WM x WN; one K step is 256 channels. Requires K % 256 == 0.
+// Two LDS stages, one barrier per K step: A arrives by direct-to-LDS loads one step ahead, the
+// weights through registers two steps ahead, the scale words in registers one step ahead.
 template <int BM, int BN, int NWM, int NWN, bool GLU, int MINB>
 __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
   constexpr int NT = NWM * NWN * 64, NW = NWM * NWN;
