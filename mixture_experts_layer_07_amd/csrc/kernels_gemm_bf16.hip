@@ -18,7 +18,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   __shared__ u32x4 sB1[w4::kStageB];
   __shared__ int tp[kMaxExperts + 1];
   __shared__ int s_slot[1];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS offsets in SGPRs
   for (int i = tid; i <= g.n_exp; i += 256) tp[i] = g.tp[i];
   __syncthreads();
@@ -29,6 +29,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   constexpr int kCpol = 0;                     // (plain output stores)
 
   for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {
+    // lane-derived offsets are formed per tile: derived once above the loop, they were held across
+    // it and spilled (≈ 90 registers, reloaded in every tile's set-up and epilogue)
+    const int lane = opaque_tid() & 63;
     TileInfo ti = decode_tile(w.tile, tp, g, BM);
     // the same for every lane: keep it in scalar registers
     ti.e = __builtin_amdgcn_readfirstlane(ti.e);
