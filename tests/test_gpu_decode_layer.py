@@ -50,6 +50,8 @@ SMALL = {
                                      I_shared=0), None),
     "mx-decode-one-token": (MX.scaled(T=1, H=256, I=256, E=16, K=4, n_group=4, topk_group=2, bias="normal",
                                       I_shared=256), None),
+    # MX at the largest pair count (16 router token blocks, 128 quantisation tasks)
+    "mx-decode-max-pairs": (MX.scaled(T=512, H=256, I=256, E=64, K=8, bias="normal", I_shared=256), "zipf"),
 }
 
 
