@@ -306,12 +306,12 @@ constexpr int kWaitLgkm0Vm8 = wait_lgkm0_vm(8), kWaitLgkm0Vm0 = wait_lgkm0_vm(0)
     if (SPLIT && w.piece >= 0) {                                                                 \
       /* K piece: publish it; the last piece to arrive sums all of them in piece order */        \
       w4::store_partial(g.part + (size_t)w.slot * kPartStride, acc, tid);                        \
-      store = split_arrive(&g.split_cnt[w.first], sq.S, s_slot);                                 \
+      store = split_arrive(&g.split_cnt[w.first], w.S, s_slot);                                  \
       if (store) {                                                                               \
         _Pragma("unroll") for (int mb = 0; mb < (MB_); ++mb)                                     \
           _Pragma("unroll") for (int nb = 0; nb < (NB_); ++nb)                                   \
             _Pragma("unroll") for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;                 \
-        for (int pc = 0; pc < sq.S; ++pc)                                                        \
+        for (int pc = 0; pc < w.S; ++pc)                                                         \
           w4::add_partial(g.part + (size_t)(w.first + pc) * kPartStride, acc, tid);              \
       }                                                                                          \
     }                                                                                            \
@@ -334,8 +334,8 @@ constexpr int kSink = 256;
 // m-tile prefix sums in LDS; sA0 .. sB1: the caller's LDS stages (__shared__ arrays of
 // m32::kStageA and w4::kStageB entries); s_slot: one LDS int. All threads of the workgroup call.
 template <bool GLU, bool OUTF32, bool SPLIT, int CPOL = 0>
-__device__ __forceinline__ void m32_item(const GemmArgs& g, const int* tp, const WorkItem& w, const SplitQueue& sq,
-                                         u32x4* sA0, u32x4* sA1, u32x4* sB0, u32x4* sB1, int* s_slot) {
+__device__ __forceinline__ void m32_item(const GemmArgs& g, const int* tp, const WorkItem& w, u32x4* sA0, u32x4* sA1,
+                                         u32x4* sB0, u32x4* sB1, int* s_slot) {
   constexpr int BM = 32, BN = 256;
   constexpr size_t kPartStride = 32 * 256;  // floats per partial tile
   constexpr int kCpol = CPOL;               // (the epilogue's store cache policy)

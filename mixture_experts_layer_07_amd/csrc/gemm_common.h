@@ -55,8 +55,8 @@ struct TileQueue {
   int beg, end;
 };
 
-__device__ __forceinline__ TileQueue tile_queue(int total) {
-  const int q = blockIdx.x % kQueues;
+// Tile range q of a launch of `total` tiles: equal tile counts.
+__device__ __forceinline__ TileQueue tile_queue(int q, int total) {
   const int per = (total + kQueues - 1) / kQueues;
   TileQueue r;
   r.beg = q * per < total ? q * per : total;
@@ -64,37 +64,122 @@ __device__ __forceinline__ TileQueue tile_queue(int total) {
   return r;
 }
 
-// Next tile of this workgroup's range, or -1. All threads must call (two barriers).
-__device__ __forceinline__ int next_tile(const GemmArgs& g, const TileQueue& tq, int* s_slot) {
-  if (threadIdx.x == 0) s_slot[0] = tq.beg + atomicAdd(&g.queue[blockIdx.x % kQueues], 1);
+// Workgroup b draws from range b % 8 first, so every range is served by exactly gridDim.x / 8
+// workgroups (the grid is a multiple of 8) and drains whatever the placement; workgroups are
+// dispatched round-robin over the 8 XCDs, so those are normally one XCD's, under one L2. Ranges of
+// equal tile counts do not hold equal work (the ragged m-tiles of skewed experts are cheaper than
+// full ones), so once its range is drained a workgroup goes on drawing from the range with the
+// most items left, until every range is drained; without that the XCDs with lighter ranges idle
+// while the others finish.
+
+// The range with the most items left, or -1 once every range is drained: wave 0 reads all the
+// counters at once, one per lane. Only a range with more items than its own workgroups take in
+// one round is drawn from (in a launch with fewer tiles than workgroups every item has its own
+// workgroup already, and a draw from elsewhere only adds round trips); with none, no counter is
+// read. s_slot[1 + l]: the item count of range l (range_items). All threads must call (two
+// barriers, none if no range qualifies).
+__device__ __forceinline__ int fullest_range(const GemmArgs& g, int* s_slot) {
+  const int C = gridDim.x / kQueues;
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < kQueues; ++r) any |= s_slot[1 + r] > C;
+  if (!any) return -1;
+  const int l = opaque_tid();  // (formed here: values derived from it are not held across the loop)
+  if (l < 64) {
+    int left = 0;
+    if (l < kQueues && s_slot[1 + l] > C)
+      left = s_slot[1 + l] - __hip_atomic_load(&g.queue[l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int key = (left > 0 ? left : 0) * kQueues + l;  // (the most items left, then the highest range)
+#pragma unroll
+    for (int o = 1; o < kQueues; o <<= 1) key = max(key, __shfl_xor(key, o, 64));
+    if (l == 0) s_slot[0] = key >= kQueues ? key % kQueues : -1;
+  }
   __syncthreads();
-  const int t = __builtin_amdgcn_readfirstlane(s_slot[0]);  // uniform: scalar registers
+  const int q = __builtin_amdgcn_readfirstlane(s_slot[0]);
   __syncthreads();
-  return t < tq.end ? t : -1;
+  return q;
 }
 
-// Tile queue whose last round is split along K: the plan (split_plan) and the item decode
-// (plan_item) are pure integer arithmetic in tile_plan.h; here they are fed the workgroup's range
-// and drawn from the range's counter.
-// The range is chosen by the workgroup id (b % 8), so every range is served by exactly
-// gridDim.x / 8 workgroups (the grid is a multiple of 8) and drains whatever the placement.
-// Workgroups are dispatched round-robin over the 8 XCDs, so the workgroups of a range, and the
-// pieces of a split tile, normally share one XCD and its L2; the handoff of the pieces
-// (split_arrive) does not rely on that.
-// max_slots: partial tiles the kernel's workspace region holds (pieces of one launch).
-__device__ __forceinline__ SplitQueue split_queue(int total, int KT, int min_steps, int max_slots) {
-  return split_plan(blockIdx.x % kQueues, total, KT, min_steps, max_slots, gridDim.x / kQueues,
-                    kMaxSplitItems, MOE_MAX_K_PIECES);
+// Item counts of the ranges of a launch of `total` tiles into s_slot[1 .. kQueues] (an LDS array
+// of 1 + kQueues ints; s_slot[0] is the draw slot), for whole tiles (tile_queue) or, with KT > 0,
+// for the split plans (split_plan). Formed once the workgroup's own range is drained (formed
+// before the first draw, it measurably slowed launches made of split pieces only). All threads
+// call (one barrier).
+__device__ __forceinline__ void range_items(int total, int KT, int min_steps, int max_slots, int* s_slot) {
+  const int l = threadIdx.x;
+  if (l < kQueues) {
+    if (KT > 0) {
+      s_slot[1 + l] = split_plan(l, total, KT, min_steps, max_slots, gridDim.x / kQueues, kMaxSplitItems,
+                                 MOE_MAX_K_PIECES).items;
+    } else {
+      const TileQueue r = tile_queue(l, total);
+      s_slot[1 + l] = r.end - r.beg;
+    }
+  }
+  __syncthreads();
 }
 
-// Next work item of this workgroup's range, or item.tile = -1. All threads must call (two barriers).
-__device__ __forceinline__ WorkItem next_item(const GemmArgs& g, const SplitQueue& sq, int KT, int* s_slot) {
-  if (threadIdx.x == 0) s_slot[0] = atomicAdd(&g.queue[sq.q], 1);
-  __syncthreads();
-  // the same for every lane; readfirstlane tells the compiler so (scalar registers, uniform branches)
-  const int it = __builtin_amdgcn_readfirstlane(s_slot[0]);
-  __syncthreads();
-  return plan_item(sq, it, KT);
+// Next tile of this workgroup: from its own range tq (tile_queue(b % 8, total)) while `own` is
+// set (cleared once that range is drained), then (STEAL) from the fullest range. Returns -1 once
+// every range is drained. All threads must call (two barriers per draw).
+template <bool STEAL = true>
+__device__ __forceinline__ int next_tile(const GemmArgs& g, const TileQueue& tq, int total, int* s_slot, bool& own) {
+  if (own) {
+    if (threadIdx.x == 0) s_slot[0] = tq.beg + atomicAdd(&g.queue[blockIdx.x % kQueues], 1);
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(s_slot[0]);  // uniform: scalar registers
+    __syncthreads();
+    if (t < tq.end) return t;
+    own = false;
+    if (STEAL) range_items(total, 0, 0, 0, s_slot);
+  }
+  if (!STEAL) return -1;
+  for (int q; (q = fullest_range(g, s_slot)) >= 0;) {
+    const TileQueue r = tile_queue(q, total);
+    if (threadIdx.x == 0) s_slot[0] = r.beg + atomicAdd(&g.queue[q], 1);
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(s_slot[0]);
+    __syncthreads();
+    if (t < r.end) return t;
+  }
+  return -1;
+}
+
+// The same for tile queues whose last round is split along K: the plan of a range (split_plan)
+// and the item decode (plan_item) are pure integer arithmetic in tile_plan.h; here they are fed
+// the range drawn from and its counter. The pieces of a split tile may run on different XCDs (a
+// drawn range, or a dispatch that is not round-robin): their handoff (split_arrive) does not
+// rely on one L2. sq: the plan of the workgroup's own range (own_plan); own as for next_tile.
+// max_slots: partial tiles the kernel's workspace region holds (pieces of one launch). Returns
+// item.tile = -1 once every range is drained. All threads must call (two barriers per draw).
+__device__ __forceinline__ SplitQueue own_plan(int total, int KT, int min_steps, int max_slots) {
+  return split_plan(blockIdx.x % kQueues, total, KT, min_steps, max_slots, gridDim.x / kQueues, kMaxSplitItems,
+                    MOE_MAX_K_PIECES);
+}
+__device__ __forceinline__ WorkItem next_item(const GemmArgs& g, const SplitQueue& sq, int total, int KT, int min_steps,
+                                              int max_slots, int* s_slot, bool& own) {
+  if (own) {
+    if (threadIdx.x == 0) s_slot[0] = atomicAdd(&g.queue[sq.q], 1);
+    __syncthreads();
+    // the same for every lane; readfirstlane tells the compiler so (scalar registers, uniform branches)
+    const int it = __builtin_amdgcn_readfirstlane(s_slot[0]);
+    __syncthreads();
+    const WorkItem w = plan_item(sq, it, KT);
+    if (w.tile >= 0) return w;
+    own = false;
+    range_items(total, KT, min_steps, max_slots, s_slot);
+  }
+  for (int q; (q = fullest_range(g, s_slot)) >= 0;) {
+    const SplitQueue r =
+        split_plan(q, total, KT, min_steps, max_slots, gridDim.x / kQueues, kMaxSplitItems, MOE_MAX_K_PIECES);
+    if (threadIdx.x == 0) s_slot[0] = atomicAdd(&g.queue[q], 1);
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(s_slot[0]);
+    __syncthreads();
+    const WorkItem w = plan_item(r, it, KT);
+    if (w.tile >= 0) return w;
+  }
+  return plan_item(sq, sq.items, KT);  // (every range drained: the "drained" item, tile -1)
 }
 
 // Arrival of a K piece whose partial tile every thread of the workgroup has stored: returns true

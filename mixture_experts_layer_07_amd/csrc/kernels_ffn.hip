@@ -9,8 +9,10 @@
 //
 // Scheduling: a tiny kernel turns offsets into m-tile prefix sums tp[e] (ceil(rows_e / BM)),
 // then a persistent grid walks the tile list (expert, n-tile, m-tile) in that order; logically
-// neighbouring tiles run on the same XCD (xcd_local_id), so the m-tiles that share a weight
-// block share that XCD's L2. Experts with no rows cost nothing.
+// neighbouring tiles run on the same XCD (the MFMA kernels: one range of the list per XCD, a
+// drained range's workgroups drawing from the fullest one, gemm_common.h; the fp32 kernel:
+// xcd_local_id), so the m-tiles that share a weight block share that XCD's L2. Experts with no
+// rows cost nothing.
 #include "gemm_common.h"
 
 namespace moe {

@@ -17,18 +17,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bf16_w4(GemmArgs g) {
   __shared__ u32x4 sB0[w4::kStageB];
   __shared__ u32x4 sB1[w4::kStageB];
   __shared__ int tp[kMaxExperts + 1];
-  __shared__ int s_slot[1];
+  __shared__ int s_slot[1 + kQueues];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS offsets in SGPRs
   for (int i = tid; i <= g.n_exp; i += 256) tp[i] = g.tp[i];
   __syncthreads();
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 64;  // K is a multiple of 128: KT is even
-  const SplitQueue sq = split_queue(total, KT, 16, 256);  // (256 partial tiles of 256 x 256)
   constexpr size_t kPartStride = kPartFloats;  // floats per partial tile
   constexpr int kCpol = 0;                     // (plain output stores)
 
-  for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {
+  // (256 partial tiles of 256 x 256)
+  const SplitQueue sq = own_plan(total, KT, 16, 256);
+  bool own = true;
+  for (WorkItem w = next_item(g, sq, total, KT, 16, 256, s_slot, own); w.tile >= 0;
+       w = next_item(g, sq, total, KT, 16, 256, s_slot, own)) {
     // lane-derived offsets are formed per tile: derived once above the loop, they were held across
     // it and spilled (≈ 90 registers, reloaded in every tile's set-up and epilogue)
     const int lane = opaque_tid() & 63;
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_m32(GemmArgs g) {
   __shared__ u32x4 sB0[w4::kStageB];
   __shared__ u32x4 sB1[w4::kStageB];
   __shared__ int tp[kMaxExperts + 1];
-  __shared__ int s_slot[1];
+  __shared__ int s_slot[1 + kQueues];
   const int tid = threadIdx.x;
   for (int i = tid; i <= g.n_exp; i += 256) tp[i] = g.tp[i];
   __syncthreads();
@@ -93,9 +96,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16_m32(GemmArgs g) {
   const int KT = g.K / 64;  // even
   // a launch with fewer tiles than workgroups (a decode-sized shared expert) cuts its tiles along
   // K; a 32 x 256 partial tile is 32 KiB, so the last piece's sum stays cheap
-  const SplitQueue sq = split_queue(total, KT, 16, 512);  // (512 partial tiles of 32 x 256)
-  for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot))
-    m32_item<GLU, OUTF32, true>(g, tp, w, sq, sA0, sA1, sB0, sB1, s_slot);
+  // (512 partial tiles of 32 x 256)
+  const SplitQueue sq = own_plan(total, KT, 16, 512);
+  bool own = true;
+  for (WorkItem w = next_item(g, sq, total, KT, 16, 512, s_slot, own); w.tile >= 0;
+       w = next_item(g, sq, total, KT, 16, 512, s_slot, own))
+    m32_item<GLU, OUTF32, true>(g, tp, w, sA0, sA1, sB0, sB1, s_slot);
 }
 
 template <class K>

@@ -90,10 +90,10 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 128;
   const int lrow = lane & 31, lk = lane >> 5;
-  __shared__ int s_slot[1];
-  const TileQueue tq = tile_queue(total);
-
-  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot)) {
+  __shared__ int s_slot[1 + kQueues];
+  const TileQueue tq = tile_queue(blockIdx.x % kQueues, total);
+  bool own = true;
+  for (int t = next_tile(g, tq, total, s_slot, own); t >= 0; t = next_tile(g, tq, total, s_slot, own)) {
     TileInfo ti = decode_tile(t, tp, g, BM);
     ti.e = __builtin_amdgcn_readfirstlane(ti.e);
     ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);

@@ -30,18 +30,21 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
   const int total = tp[g.n_exp] * g.n_tiles_n;
   const int KT = g.K / 256;
   const int lrow = lane & 31, h = lane >> 5;
-  __shared__ int s_slot[1];
+  __shared__ int s_slot[1 + kQueues];
   // 32-row tiles: a launch with fewer tiles than workgroups (a decode-sized shared expert) cuts
   // its tiles along K into pieces of >= 7 steps (1792 channels; shorter loops are not repaid),
   // summed in piece order by the last piece to arrive
   constexpr bool kSplit = BM == 32;
-  const SplitQueue sq = split_queue(total, KT, kSplit ? 7 : (1 << 20), 512);  // (512 partial tiles of 32 x 256)
+  const int min_steps = kSplit ? 7 : (1 << 20);  // (512 partial tiles of 32 x 256)
   const uint32_t* a_sc = reinterpret_cast<const uint32_t*>(g.a_scale);
   const uint32_t* b_sc = reinterpret_cast<const uint32_t*>(g.b_scale);
   const size_t a_sld = (size_t)g.a_scale_ld;  // rows of the activation scale array
   const size_t b_sld = (size_t)g.b_scale_ld;  // rows of one expert's weight scale array
 
-  for (WorkItem w = next_item(g, sq, KT, s_slot); w.tile >= 0; w = next_item(g, sq, KT, s_slot)) {
+  const SplitQueue sq = own_plan(total, KT, min_steps, 512);
+  bool own = true;
+  for (WorkItem w = next_item(g, sq, total, KT, min_steps, 512, s_slot, own); w.tile >= 0;
+       w = next_item(g, sq, total, KT, min_steps, 512, s_slot, own)) {
     TileInfo ti = decode_tile(w.tile, tp, g, BM);
     const int k0 = __builtin_amdgcn_readfirstlane(w.k0), k1 = __builtin_amdgcn_readfirstlane(w.k1);
     ti.e = __builtin_amdgcn_readfirstlane(ti.e);
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
       // K piece: publish it; the last piece to arrive sums all of them in piece order
       constexpr size_t kPart = (size_t)MB * NB * 16 * NT;
       store_partial_acc<MB, NB, NT>(g.part + (size_t)w.slot * kPart, acc, tid);
-      store = split_arrive(&g.split_cnt[w.first], sq.S, s_slot);
+      store = split_arrive(&g.split_cnt[w.first], w.S, s_slot);
       if (store) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_mx(GemmArgs g) {
           for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-        for (int pc = 0; pc < sq.S; ++pc) add_partial_acc<MB, NB, NT>(g.part + (size_t)(w.first + pc) * kPart, acc, tid);
+        for (int pc = 0; pc < w.S; ++pc) add_partial_acc<MB, NB, NT>(g.part + (size_t)(w.first + pc) * kPart, acc, tid);
       }
     }
     if (!store) continue;
@@ -223,12 +226,18 @@ __global__ __launch_bounds__(P::NT, MINB) void k_gemm_mx_r3(GemmArgs g) {
   __shared__ u32x4 sB1[P::BCH];
   __shared__ u32x4 sB2[P::BCH];
   __shared__ int tp[kMaxExperts + 1];
-  __shared__ int s_slot[1];
+  __shared__ int s_slot[1 + kQueues];
   const int tid = threadIdx.x;
   for (int i = tid; i <= g.n_exp; i += P::NT) tp[i] = g.tp[i];
   __syncthreads();
-  const TileQueue tq = tile_queue(tp[g.n_exp] * g.n_tiles_n);
-  for (int t = next_tile(g, tq, s_slot); t >= 0; t = next_tile(g, tq, s_slot))
+  const int total = tp[g.n_exp] * g.n_tiles_n;
+  const TileQueue tq = tile_queue(blockIdx.x % kQueues, total);
+  bool own = true;
+  // The decode-sized 32-row tiles stream their weight blocks at the HBM rate and differ little in
+  // cost: a tile drawn from another XCD's range fetches its weights once more, which costs more
+  // than the idle tail it saves (decode-zipf-mxfp4: 846 against 814 us per layer with it).
+  constexpr bool kSteal = P::BM > 32;
+  for (int t = next_tile<kSteal>(g, tq, total, s_slot, own); t >= 0; t = next_tile<kSteal>(g, tq, total, s_slot, own))
     mx_r3_item<P, GLU>(g, tp, t, sA0, sA1, sA2, sB0, sB1, sB2);
 }
 

@@ -324,14 +324,14 @@ __device__ __forceinline__ void expert_tile(const GemmArgs& g, const int* tp, in
     constexpr int AC = MxDecode::ACH, BC = MxDecode::BCH;
     mx_r3_item<MxDecode, GLU, true, GSC>(g, tp, tile, sB1 + BC, sB1 + BC + AC, sB1 + BC + 2 * AC, sB0, sB0 + BC, sB1);
   } else {
-    const SplitQueue sq0 = {0, 0, 1, 0, 0, 0};  // (whole tiles: no hand-over of K pieces)
-    WorkItem w;
+    WorkItem w;  // (a whole tile: no hand-over of K pieces)
     w.tile = tile;
     w.piece = -1;
     w.slot = w.first = 0;
+    w.S = 1;
     w.k0 = 0;
     w.k1 = g.K / 64;
-    m32_item<GLU, false, false, kCpolSc1>(g, tp, w, sq0, sA0, sA1, sB0, sB1, s_slot);
+    m32_item<GLU, false, false, kCpolSc1>(g, tp, w, sA0, sA1, sB0, sB1, s_slot);
   }
 }
 

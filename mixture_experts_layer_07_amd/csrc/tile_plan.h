@@ -35,6 +35,7 @@ struct WorkItem {
   int k0, k1; // K steps [k0, k1)
   int slot;   // partial-tile slot of this piece
   int first;  // slot of piece 0 of the same tile (its arrival counter index as well)
+  int S;      // pieces of the tile (1: whole)
 };
 
 // Plan of range q of a launch with `total` tiles, C workgroups per range, KT K steps per tile.
@@ -76,6 +77,7 @@ __host__ __device__ inline WorkItem plan_item(const SplitQueue& sq, int it, int 
     w.tile = -1;
     w.piece = -1;
     w.k0 = w.k1 = w.slot = w.first = 0;
+    w.S = 1;
     return w;
   }
   if (it < sq.nfull) {
@@ -84,6 +86,7 @@ __host__ __device__ inline WorkItem plan_item(const SplitQueue& sq, int it, int 
     w.k0 = 0;
     w.k1 = KT;
     w.slot = w.first = 0;
+    w.S = 1;
     return w;
   }
   const int j = it - sq.nfull;
@@ -94,6 +97,7 @@ __host__ __device__ inline WorkItem plan_item(const SplitQueue& sq, int it, int 
   w.k0 = w.piece * chunk;
   w.k1 = w.piece == sq.S - 1 ? KT : w.k0 + chunk;
   w.first = sq.slot0 + tt * sq.S;
+  w.S = sq.S;
   w.slot = w.first + w.piece;
   return w;
 }

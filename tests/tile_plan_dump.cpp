@@ -16,7 +16,7 @@ int main() {
       // every workgroup of the range draws until the range is drained: draw past the end too
       for (int it = 0; it < sq.items + C; ++it) {
         const moe::WorkItem w = moe::plan_item(sq, it, KT);
-        std::printf("%d %d %d %d %d %d %d %d %d\n", q, it, w.tile, w.piece, w.k0, w.k1, w.slot, w.first, sq.S);
+        std::printf("%d %d %d %d %d %d %d %d %d\n", q, it, w.tile, w.piece, w.k0, w.k1, w.slot, w.first, w.S);
       }
     }
   }
