@@ -235,7 +235,7 @@ __global__ __launch_bounds__(P::NT, MINB) void k_gemm_mx_r3(GemmArgs g) {
   bool own = true;
   // The decode-sized 32-row tiles stream their weight blocks at the HBM rate and differ little in
   // cost: a tile drawn from another XCD's range fetches its weights once more, which costs more
-  // than the idle tail it saves (decode-zipf-mxfp4: 846 against 814 us per layer with it).
+  // than the idle tail it saves (decode-zipf-mxfp4: 836 against 815 us per layer with it).
   constexpr bool kSteal = P::BM > 32;
   for (int t = next_tile<kSteal>(g, tq, total, s_slot, own); t >= 0; t = next_tile<kSteal>(g, tq, total, s_slot, own))
     mx_r3_item<P, GLU>(g, tp, t, sA0, sA1, sA2, sB0, sB1, sB2);
