@@ -27,9 +27,10 @@
 // arrive_combine below).
 // The expert GEMM tiles are those of the separate GEMM kernels (bf16: 32 x 256 tiles through two
 // LDS stages; MX: the three-stage 32 x 256 tiles on the scaled MFMA), the router's always bf16.
-// Tasks are pulled in list order (expert-major for the GEMMs), so the Linear-1 tiles finish
-// roughly in the order the Linear-2 tiles are pulled and Linear-2 rarely waits. A workgroup moves
-// to the next segment only once every task of the current one has been pulled, and a task waits
+// Tasks are pulled in list order (expert-major for the GEMMs; the bf16 GEMM segments from one
+// tile range per XCD, see seg_range below), so the Linear-1 tiles finish roughly in the order the
+// Linear-2 tiles are pulled and Linear-2 rarely waits. A workgroup moves to the next segment only
+// once every task of the current one has been pulled, and a task waits
 // only on tasks of earlier segments, which some running workgroup has pulled; so the layer
 // completes with any number of resident workgroups (by induction over the segments). Each wait is
 // bounded all the same: past the limit the workgroup sets the device error word (code 2) and a
@@ -87,7 +88,8 @@ constexpr int kRouterDone = 32;                    // [kMaxTokBlocks] router til
 constexpr int kL1Done = kRouterDone + kMaxTokBlocks;  // [kMaxMTiles] routed L1 tiles per m-tile
 constexpr int kL1sDone = kL1Done + kMaxMTiles;        // [kSmallPermPairs / 32] shared L1 per m-tile
 constexpr int kTp = kL1sDone + kSmallPermPairs / 32;  // [kMaxExperts + 1] routed m-tile prefix
-constexpr int kClear = kTp + kMaxExperts + 1;         // words cleared at the start
+constexpr int kRQ = kTp + kMaxExperts + 1;            // [4][kQueues] range counters of the GEMM segments
+constexpr int kClear = kRQ + 4 * kQueues;             // words cleared at the start
 constexpr int kEpoch = (kClear + 1) & ~1;             // 64-bit launch epoch
 static_assert(kShOff + 2 <= kRouterDone, "control block layout");
 static_assert(kEpoch + 2 <= kDecodeCtrlInts, "control block too small");
@@ -209,6 +211,62 @@ __device__ __forceinline__ bool wait_geq(const DecodeArgs& a, const int32_t* p, 
 // K piece p of S over KT steps: an even number of steps, at least two (S <= KT / 2).
 __device__ __forceinline__ int piece_k(int p, int S, int KT) { return (int)((long long)p * (KT / 2) / S) * 2; }
 
+// ---------------------------------------------------------------- tile ranges of the GEMM segments
+// The tasks of a GEMM segment (shared / routed Linear-1 and Linear-2, in expert-major tile order)
+// are cut into kQueues ranges of equal counts, one counter each; workgroup b draws from range
+// b % kQueues first (under the round-robin dispatch, the workgroups of one XCD), so the m-tiles
+// that share a weight block run under one L2, as in the separate GEMM kernels. Once its range is
+// drained a workgroup draws from the range with the most tasks left, until every range is drained:
+// a workgroup still leaves a segment only once all of its tasks are pulled.
+__device__ __forceinline__ int seg_range(int n, int q, int& len) {
+  const int per = (n + kQueues - 1) / kQueues;
+  const int beg = min(n, q * per);
+  len = min(n, beg + per) - beg;
+  return beg;
+}
+
+// The range with the most tasks left, or -1 once every range is drained: wave 0 reads the kQueues
+// counters cnt[] at once. All threads call (two barriers).
+__device__ __forceinline__ int fullest_seg_range(const int32_t* cnt, int n, int* s_slot) {
+  const int l = opaque_tid();
+  if (l < 64) {
+    int left = 0;
+    if (l < kQueues) {
+      int len;
+      seg_range(n, l, len);
+      left = len - __hip_atomic_load(cnt + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    int key = (left > 0 ? left : 0) * kQueues + l;
+#pragma unroll
+    for (int o = 1; o < kQueues; o <<= 1) key = max(key, __shfl_xor(key, o, 64));
+    if (l == 0) s_slot[0] = key >= kQueues ? key % kQueues : -1;
+  }
+  __syncthreads();
+  const int q = __builtin_amdgcn_readfirstlane(s_slot[0]);
+  __syncthreads();
+  return q;
+}
+
+// Next task of a GEMM segment of n tasks with range counters cnt[]: from range q while `live`
+// (q may still have tasks; q starts as the workgroup's own range), else from the fullest range
+// (q updated). Returns n once every range is drained. All threads call.
+__device__ __forceinline__ int draw_ranged(int32_t* cnt, int n, int& q, bool& live, int* s_slot) {
+  for (;;) {
+    if (live) {
+      int len;
+      const int beg = seg_range(n, q, len);
+      if (threadIdx.x == 0) s_slot[0] = atomicAdd(cnt + q, 1);
+      __syncthreads();
+      const int i = __builtin_amdgcn_readfirstlane(s_slot[0]);
+      __syncthreads();
+      if (i < len) return beg + i;
+      live = false;
+    }
+    if ((q = fullest_seg_range(cnt, n, s_slot)) < 0) return n;
+    live = true;
+  }
+}
+
 // ---------------------------------------------------------------- combine in the Linear-2 epilogue
 // The weighted combine fused into Linear-2 ("MoE 优化的探索", 3.6.2 and 3.7.3: the reduce
 // happens as the second GEMM's tiles finish, with an arrival count per token rather than a pass
@@ -218,8 +276,9 @@ __device__ __forceinline__ int piece_k(int p, int S, int KT) { return (int)((lon
 // count (K routed rows, plus the shared row) acquires and combines that block of the token's
 // output row (combine_chunk: fp32 in k order, the shared row last, one rounding), so every output
 // value is still summed by one workgroup in a fixed order and the result matches the separate
-// combine bit for bit. The workgroup's next task of the segment is pulled from queue q in the
-// same round trip as the arrivals (returned in `next`). s_list: 34 ints of LDS.
+// combine bit for bit. The workgroup's next task of the segment is pulled from counter q (the
+// range the tile came from) in the same round trip as the arrivals; `next` receives the counter's
+// old value. s_list: 34 ints of LDS.
 template <bool OF32>
 __device__ __forceinline__ void arrive_combine(const DecodeArgs& a, const TileInfo& ti, bool routed_rows, int* q,
                                                int* s_list, int& next) {
@@ -254,6 +313,25 @@ __device__ __forceinline__ void arrive_combine(const DecodeArgs& a, const TileIn
         default: combine_chunk<OF32, 0>(t, ch, a.pair_pos, a.weights, a.y, a.ysh, a.out, a.H, a.K);
       }
     }
+  }
+}
+
+// A Linear-2 tile's arrivals (arrive_combine) together with the pull of the workgroup's next task
+// of the segment: from the segment's counter q (gi < 0), or from range rq of the range counters
+// rcnt (mapped to its task; a drained range clears `live`, so the next draw looks for the
+// fullest). next: the task (n or more, or -1, when there is none to take).
+template <bool OF32>
+__device__ __forceinline__ void pull_next(const DecodeArgs& a, const TileInfo& ti, bool routed_rows, int gi, int* q,
+                                          int32_t* rcnt, int n, int rq, bool& live, int* s_list, int& next) {
+  arrive_combine<OF32>(a, ti, routed_rows, gi < 0 ? q : rcnt + rq, s_list, next);
+  if (gi < 0) return;
+  int len;
+  const int beg = seg_range(n, rq, len);
+  if (next < len) {
+    next += beg;
+  } else {
+    next = -1;
+    live = false;
   }
 }
 
@@ -427,12 +505,23 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
       case dec::kSh2: n = a.has_shared ? a.mts * a.s2.n_tiles_n : 0; break;
       default: n = s_tp[a.E] * a.g2.n_tiles_n; break;  // routed L2
     }
+    // bf16 GEMM segments draw from tile ranges (seg_range); gi: their index in the range counters.
+    // The MX tiles (a quarter of the weight bytes) keep one counter per segment: with ranges the
+    // decode-zipf-mxfp4 launch took 874 against 852 us, as tiles drawn from another XCD's range
+    // fetch their weight blocks once more (the separate 32-row MX kernel likewise).
+    const int gi = MX ? -1
+                      : seg == dec::kSh1 ? 0 : seg == dec::kL1 ? 1 : seg == dec::kSh2 ? 2 : seg == dec::kL2 ? 3 : -1;
+    int32_t* rcnt = ctrl + dec::kRQ + (gi < 0 ? 0 : gi) * kQueues;
+    int rq = blockIdx.x % kQueues;  // the range drawn from
+    bool live = true;               // range rq may still have tasks
     int pre = -1;  // a task of this segment already pulled (by the Linear-2 epilogue)
     for (;;) {
       int task = n;
       if (pre >= 0) {
         task = pre;
         pre = -1;
+      } else if (n > 0 && gi >= 0) {
+        task = draw_ranged(rcnt, n, rq, live, s_slot);
       } else if (n > 0) {
         if (tid == 0) s_slot[0] = atomicAdd(&ctrl[dec::kQ + seg], 1);
         __syncthreads();
@@ -539,7 +628,7 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
         const TileInfo ti = decode_tile(task, s_tps, a.s2, 32);
         if (!(alive = wait_geq(a, ctrl + dec::kL1sDone + ti.mt, a.s1.n_tiles_n, s_slot))) break;
         expert_tile<MX, false>(a.s2, s_tps, task, sA0, sA1, sB0, sB1, s_slot);
-        arrive_combine<OF32>(a, ti, false, ctrl + dec::kQ + seg, s_list, pre);
+        pull_next<OF32>(a, ti, false, gi, ctrl + dec::kQ + seg, rcnt, n, rq, live, s_list, pre);
       } else if (seg == dec::kL2) {
         const TileInfo ti = decode_tile(task, s_tp, a.g2, 32);
         const int m = s_tp[ti.e] + ti.mt;
@@ -552,7 +641,7 @@ __global__ __launch_bounds__(256, 2) void k_layer_decode(DecodeArgs a) {
           snapshot_l1(ctrl, s_tp[a.E], a.g1.n_tiles_n, s_l1ok);
         }
         expert_tile<MX, false>(a.g2, s_tp, task, sA0, sA1, sB0, sB1, s_slot);
-        arrive_combine<OF32>(a, ti, true, ctrl + dec::kQ + seg, s_list, pre);
+        pull_next<OF32>(a, ti, true, gi, ctrl + dec::kQ + seg, rcnt, n, rq, live, s_list, pre);
       }
     }
   }
