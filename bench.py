@@ -253,7 +253,9 @@ def main():
                    "I_shared": cfg.I_shared, "output": cfg.out, "global_batch": cfg.T, "seq_len": cfg.T,
                    "parallelism": "single-gpu",
                    "linear1_input": "x_perm copy" if args.x_perm else "token rows gathered in place",
-                   "launches": "one (moe_layer_decode)" if args.single_launch else "one per stage"},
+                   "launches": "one (moe_layer_decode)" if args.single_launch else "one per stage",
+                   "shared_expert": ("none" if not cfg.I_shared else "in the launch" if args.single_launch
+                                     else "own stream, overlapped" if layer.side is not None else "serial")},
         "tokens_per_s": round(tokens_s, 1),
         "mfma_peak_frac": round(tflops / PEAK[dtype], 4),
         "active_experts": active,

@@ -65,7 +65,7 @@ def test_decode_layer_small_parity(name):
     print(f"decode layer case {name}", flush=True)
     case = _case(name)
     rep = full_check(case)
-    assert B.moe_get_device_error(case.layer.ws) == 0
+    assert case.layer.device_error() == 0
     print(name, rep)
 
 
@@ -107,7 +107,7 @@ def test_decode_layer_deterministic_and_back_to_back():
     assert torch.equal(got, fresh.layer.out)
     c = case.run().clone()
     assert torch.equal(a, c)
-    assert B.moe_get_device_error(L.ws) == 0
+    assert L.device_error() == 0
 
 
 @pytest.mark.parametrize("name", ["decode-ragged", "mx-decode-shared"])
@@ -139,7 +139,7 @@ def test_decode_layer_graph_replays_match_eager(name):
     graph.replay()
     torch.cuda.synchronize()
     assert torch.equal(L.out, want2), "replay on new inputs"
-    assert B.moe_get_device_error(L.ws) == 0
+    assert L.device_error() == 0
 
 
 @pytest.mark.parametrize("name", ["decode-grouped-shared", "decode-softmax-noshared", "decode-bf16out",
@@ -157,7 +157,7 @@ def test_decode_layer_combine_equals_moe_combine(name):
     B.moe_combine(L.c, L.pair_pos, L.topk_weights, L.y_perm, L.y_shared, out2)
     torch.cuda.synchronize()
     assert torch.equal(L.out, out2)
-    assert B.moe_get_device_error(L.ws) == 0
+    assert L.device_error() == 0
 
 
 @pytest.mark.parametrize("cid", [4, 8], ids=["decode-zipf-bf16", "decode-zipf-mxfp4"])
@@ -178,5 +178,5 @@ def test_decode_layer_full_size_parity(cid):
     check_shared(case, toks, rep)
     check_combine(case, pp, w_g, toks, rep)
     check_end_to_end(case, ids_g, w_g, toks, rep)
-    assert B.moe_get_device_error(case.layer.ws) == 0
+    assert case.layer.device_error() == 0
     print(cfg.name, "single launch", rep)
