@@ -164,12 +164,22 @@ def test_decode_layer_combine_equals_moe_combine(name):
 def test_decode_layer_full_size_parity(cid):
     """The decode workloads at their real size (T = 128, H = 7168, I = I_shared = 2048, E = 256,
     K = 8; bf16 and MX) in the launch configuration the benchmark times: exact routing and
-    permutation, sampled rows."""
+    permutation, sampled rows against the oracle, every row written from a workspace of garbage."""
     cfg = CONFIGS[cid]
     print("decode layer full size", flush=True)
     case = Case(cfg, wdev="cuda", fused=True)
     rng = np.random.default_rng(cid)
+    # every row written, and a workspace of garbage needs no initialisation: the workspace starts
+    # as 0xFF bytes (the control block included; the error word zeroed again), the outputs as NaN
+    L = case.layer
+    L.ws.fill_(0xFF)
+    L.ws[:256].zero_()
+    for t in (L.y_perm, L.y_shared, L.out):
+        t.fill_(float("nan"))
     case.run()
+    assert not torch.isnan(L.y_perm).any(), "an expert output row was not written"
+    assert not torch.isnan(L.y_shared).any(), "a shared-expert row was not written"
+    assert not torch.isnan(L.out).any(), "an output row was not written"
     rep = {}
     ids_g, w_g = check_route(case, rep)
     counts, offsets, sp, pp = check_permute(case, ids_g)

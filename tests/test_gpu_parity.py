@@ -265,12 +265,27 @@ FULL = [1, 2, 3, 4, 5, 7, 8]
 @pytest.mark.parametrize("cid,gather", [(c, True) for c in FULL] + [(3, False), (5, False), (7, False)],
                          ids=[f"{c}-gather" for c in FULL] + ["3-x_perm", "5-x_perm", "7-x_perm"])
 def test_full_size_parity(cid, gather):
-    """Real workload sizes: exact routing / permutation; sampled expert rows and tokens. The
-    gathered path is the one the benchmark times."""
+    """Real workload sizes: exact routing / permutation; sampled expert rows and tokens against
+    the oracle, and every row written (NaN-filled buffers). The gathered path is the one the
+    benchmark times."""
     cfg = CONFIGS[cid]
     case = Case(cfg, wdev="cuda", gather=gather)
     rng = np.random.default_rng(cid)
+    # completeness at full size, on every row: each buffer the layer must write starts out as NaN
+    # (the workspaces as 0xFF bytes, a NaN in every element type they hold, the error word zeroed
+    # again), so a tile that no workgroup computed, or that was read before it was written, leaves
+    # a NaN in the output
+    L = case.layer
+    for ws in {id(L.ws): L.ws, id(L.ws_shared): L.ws_shared}.values():
+        ws.fill_(0xFF)
+        ws[:256].zero_()
+    for t in (L.x_perm, L.y_perm, L.y_shared, L.out):
+        if t is not None and t.is_floating_point():
+            t.fill_(float("nan"))
     case.run()
+    assert not torch.isnan(L.y_perm).any(), "an expert output row was not written"
+    assert L.y_shared is None or not torch.isnan(L.y_shared).any(), "a shared-expert row was not written"
+    assert not torch.isnan(L.out).any(), "an output row was not written"
     from gpu_parity import (check_combine, check_end_to_end, check_permute, check_route,
                             check_shared)
     rep = {}
