@@ -5,6 +5,11 @@
 // 4.4, whose body reposts DeepGEMM material). One K step is 128 channels, i.e. one scale block:
 // per 32 x 32 block two MFMAs give the partial sum over those channels, promoted into the fp32
 // accumulator as acc += partial * (row scale * weight block scale).
+// The MFMAs take the weights as their first operand and the token rows as their second, so a
+// 32 x 32 block's lane l holds 16 weight columns of token l % 32: the promotion's scale is one
+// value per lane (the token's row scale times the column block's weight scale), one multiply per
+// block instead of one per value, and the partial sums of consecutive blocks alternate between
+// two register sets so that a block's MFMAs run while the previous block is promoted.
 // Linear-1 output: h = SiLU(g) * u re-quantised per row per 128 columns ("SwiGLU / FP8 Cast",
 // "MoE 优化的探索：从 MiniMax-01、Comet、FlashMoE 到 DeepSeek-V4", 5.1): the tile holds exactly
 // one such block (128 h columns), scale = absmax / 448, code = e4m3(h / scale).
@@ -19,6 +24,8 @@ __device__ __forceinline__ i32x8 frag32(const u32x4* row, int c0, int c1) {
   return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
 }
 
+// One K step of a wave's MB x NB blocks (block (mb, nb): tokens mb, weight columns nb; in the
+// accumulators lane l holds token l % 32 and weight columns 8 g + 4 (l / 32) + j, value 4 g + j).
 template <int MB, int NB, int WM, int WN>
 __device__ __forceinline__ void mma_step_fp8(const u32x4* sta, const u32x4* stb, const float* lsa,
                                              const float (&sb)[NB], f32x16 (&acc)[MB][NB], int wm, int wn,
@@ -32,28 +39,31 @@ __device__ __forceinline__ void mma_step_fp8(const u32x4* sta, const u32x4* stb,
     b0[nb] = frag32(lb + nb * 256, (2 * lk) ^ lsw, (2 * lk + 1) ^ lsw);
     b1[nb] = frag32(lb + nb * 256, (4 + 2 * lk) ^ lsw, (5 + 2 * lk) ^ lsw);
   }
+  constexpr int NC = MB * NB;
+  f32x16 pp[2];
+  float sa = 0.f;
+  i32x8 a0, a1;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const i32x8 a0 = frag32(la + mb * 256, (2 * lk) ^ lsw, (2 * lk + 1) ^ lsw);
-    const i32x8 a1 = frag32(la + mb * 256, (4 + 2 * lk) ^ lsw, (5 + 2 * lk) ^ lsw);
-    float sa[16];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const float4 v = *reinterpret_cast<const float4*>(lsa + wm * WM + mb * 32 + g4 * 8 + lk * 4);
-      sa[g4 * 4 + 0] = v.x;
-      sa[g4 * 4 + 1] = v.y;
-      sa[g4 * 4 + 2] = v.z;
-      sa[g4 * 4 + 3] = v.w;
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+  for (int c = 0; c <= NC; ++c) {
+    if (c < NC) {
+      const int mb = c / NB, nb = c % NB;
+      if (nb == 0) {
+        a0 = frag32(la + mb * 256, (2 * lk) ^ lsw, (2 * lk + 1) ^ lsw);
+        a1 = frag32(la + mb * 256, (4 + 2 * lk) ^ lsw, (5 + 2 * lk) ^ lsw);
+      }
       f32x16 p;
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = 0.f;
-      p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0[nb], p, 0, 0, 0, 127, 0, 127);
-      p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1[nb], p, 0, 0, 0, 127, 0, 127);
+      p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b0[nb], a0, p, 0, 0, 0, 127, 0, 127);
+      pp[c & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b1[nb], a1, p, 0, 0, 0, 127, 0, 127);
+    }
+    if (c > 0) {
+      const int mb = (c - 1) / NB, nb = (c - 1) % NB;
+      if (nb == 0) sa = lsa[wm * WM + mb * 32 + lrow];
+      const float sc = sa * sb[nb];
+      const f32x16& q = pp[(c - 1) & 1];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = fmaf(p[i], sa[i] * sb[nb], acc[mb][nb][i]);
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = fmaf(q[i], sc, acc[mb][nb][i]);
     }
   }
 }
@@ -208,70 +218,69 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (GLU) {
-      // per-row absmax over the tile's 128 h columns: lanes (32 columns) -> waves (through LDS).
-      // A 4x4 transpose inside each quad of lanes first gives every lane four adjacent columns of
-      // one row (row rb + 8 gi + 4 lk + (lane & 3), columns 4 ((lane & 31) / 4) + k of the wave's
-      // 32), so a row's maximum is the lane's own maximum reduced over the eight quads of its
-      // half-wave, and its four codes leave as one 4-byte store.
+      // per-row absmax over the tile's 128 h columns: a lane holds 16 h columns of token
+      // lane % 32 (columns 8 g + 4 (lane / 32) + j of the wave's 32), the other 16 sit in lane
+      // ^ 32; waves combine through LDS. A lane's four adjacent columns leave as one 4-byte store.
       static_assert(NB == 2, "one gate/up block pair per wave: a wave holds 32 of the 128 h columns");
       uint32_t* red = reinterpret_cast<uint32_t*>(sA0);  // [BM][NWN] maxima (bits); every wave is past the last read
-      const int qd = lane & 3, cq = lrow >> 2;
-      float hv[MB][4][4];
+      float hv[MB][16];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        uint32_t m = 0;
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) hv[mb][gi][j] = silu_fast(acc[mb][0][4 * gi + j]) * acc[mb][1][4 * gi + j];
-          quad_transpose4(hv[mb][gi], lane);
-          uint32_t m = max(max(__float_as_uint(hv[mb][gi][0]) & 0x7FFFFFFFu, __float_as_uint(hv[mb][gi][1]) & 0x7FFFFFFFu),
-                           max(__float_as_uint(hv[mb][gi][2]) & 0x7FFFFFFFu, __float_as_uint(hv[mb][gi][3]) & 0x7FFFFFFFu));
-          m = max_over_quads(m);
-          const int r = wm * WM + mb * 32 + gi * 8 + lk * 4 + qd;
-          if (cq == 0) red[r * NWN + wn] = m;
+        for (int i = 0; i < 16; ++i) {
+          hv[mb][i] = silu_fast(acc[mb][0][i]) * acc[mb][1][i];
+          m = max(m, __float_as_uint(hv[mb][i]) & 0x7FFFFFFFu);
         }
+        m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+        if (lk == 0) red[(wm * WM + mb * 32 + lrow) * NWN + wn] = m;
+      }
       __syncthreads();
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = wm * WM + mb * 32 + lrow;
+        uint32_t mb_ = 0;
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const int r = wm * WM + mb * 32 + gi * 8 + lk * 4 + qd;
-          uint32_t mb_ = 0;
+        for (int w = 0; w < NWN; ++w) mb_ = max(mb_, red[r * NWN + w]);
+        const float m = __uint_as_float(mb_);
+        const float scale = m / 448.0f;
 #pragma unroll
-          for (int w = 0; w < NWN; ++w) mb_ = max(mb_, red[r * NWN + w]);
-          const float m = __uint_as_float(mb_);
-          const float scale = m / 448.0f;
+        for (int g4 = 0; g4 < 4; ++g4) {
           // codes: e4m3(h / scale), RNE, saturating (the hardware's packed conversion after a clamp);
           // an all-zero row block has scale 0 and codes 0
           float q[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(hv[mb][gi][k] / scale, -448.f, 448.f);
+          for (int k = 0; k < 4; ++k) q[k] = __builtin_amdgcn_fmed3f(hv[mb][4 * g4 + k] / scale, -448.f, 448.f);
           int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
           w = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w, true);
           if (!(m > 0.f)) w = 0;
-          if (r < ti.mvalid) {
-            *reinterpret_cast<uint32_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc + ti.nt * 128 + wn * 32 + 4 * cq) = (uint32_t)w;
-            if (wn == 0 && cq == 0) g.c_scale[(size_t)(ti.row0 + r) * g.c_scale_ld + ti.nt] = scale;
-          }
+          if (r < ti.mvalid)
+            *reinterpret_cast<uint32_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc + ti.nt * 128 + wn * 32 + 8 * g4 + 4 * lk) =
+                (uint32_t)w;
         }
+        if (wn == 0 && lk == 0 && r < ti.mvalid) g.c_scale[(size_t)(ti.row0 + r) * g.c_scale_ld + ti.nt] = scale;
+      }
       __syncthreads();  // red[] aliases the first stage of the next tile
     } else {
+      // bf16 y: a lane holds token lane % 32 and four adjacent columns per group g (8 bytes)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = wm * WM + mb * 32 + lrow;
+        if (r < ti.mvalid) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = ti.nt * BN + wn * WN + nb * 32 + lrow;
-          if (col < g.N_out) {  // (N_out is even: both lanes of a column pair pass or fail together)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-              // bf16 column pairs, the odd lane writing the second row (rowpair_to_colpair)
-              const uint32_t w = rowpair_to_colpair(bf16x2(acc[mb][nb][i], acc[mb][nb][i + 1]), colpair_sel(lrow));
-              const int r = wm * WM + mb * 32 + (i >> 2) * 8 + lk * 4 + (i & 3) + (lrow & 1);
-              if (r < ti.mvalid)
-                *reinterpret_cast<uint32_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc + (col & ~1) * 2) = w;
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int col = ti.nt * BN + wn * WN + nb * 32 + 8 * g4 + 4 * lk;
+              if (col < g.N_out) {  // (N_out is a multiple of 4: a group passes or fails whole)
+                uint2 v;
+                v.x = bf16x2(acc[mb][nb][4 * g4 + 0], acc[mb][nb][4 * g4 + 1]);
+                v.y = bf16x2(acc[mb][nb][4 * g4 + 2], acc[mb][nb][4 * g4 + 3]);
+                *reinterpret_cast<uint2*>(g.C + (size_t)(ti.row0 + r) * g.ldc + (size_t)col * 2) = v;
+              }
             }
-          }
         }
+      }
     }
   }
 }
