@@ -77,8 +77,12 @@ def kernel_work(cfg, active, gather=True):
     kind = {"f32": "gemm_f32", "bf16": "gemm_bf16", "fp8": "gemm_fp8", "mxfp4": "gemm_mx"}[cfg.dtype]
 
     def ffn(st, rows, nexp, inter, a_rows):
+        if fp8:  # Linear-1's row scales rewritten K-major in grouped row order (+ the row list)
+            add(st + "group_scales_fp8", 0.0, a_rows * H * sc + rows * H * sc + (rows * 4 if a_rows != rows else 0))
+        # (fp8: Linear-1 reads its rows' scales in grouped order, one per row)
+        a_sc = rows * H * sc if fp8 else a_rows * H * sc
         add(st + kind + "_gateup_swiglu", 4.0 * rows * H * inter,
-            a_rows * H * (ab + sc) + nexp * 2 * inter * H * (wb + wsc) + rows * inter * (ab + sc))
+            a_rows * H * ab + a_sc + nexp * 2 * inter * H * (wb + wsc) + rows * inter * (ab + sc))
         add(st + kind + "_down", 2.0 * rows * H * inter,
             rows * inter * (ab + sc) + nexp * H * inter * (wb + wsc) + rows * H * yb)
 

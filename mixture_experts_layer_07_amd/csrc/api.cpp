@@ -299,7 +299,7 @@ static moe_status expert_ffn(const char* where, const moe_config* cfg, int32_t n
   a.y = y_rows;
   a.h = at<void>(ws, L.h);
   a.h_scale = quant ? at<void>(ws, L.hscale) : nullptr;
-  a.x_scale_grouped = c.dtype == MOE_MXFP4 ? at<void>(ws, L.xscale) : nullptr;
+  a.x_scale_grouped = quant ? at<void>(ws, L.xscale) : nullptr;
   a.tiles = at<int32_t>(ws, L.tiles);
   a.part = at<float>(ws, L.part);
   MOE_HIP(launch_expert_ffn(a, static_cast<hipStream_t>(stream)), "expert_ffn");

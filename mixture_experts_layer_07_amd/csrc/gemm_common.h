@@ -279,10 +279,6 @@ __device__ __forceinline__ int a_row(const GemmArgs& g, const TileInfo& ti, int 
   const unsigned v = (unsigned)g.a_rows[ti.row0 + r] / (unsigned)g.a_div;
   return v < (unsigned)g.a_limit ? (int)v : g.a_limit - 1;
 }
-// The fp8 row scales [rows][a_scale_ld] follow the same rows.
-__device__ __forceinline__ const float* a_scale_base(const GemmArgs& g, const TileInfo& ti) {
-  return g.a_rows ? g.a_scale : g.a_scale + (size_t)ti.row0 * g.a_scale_ld;
-}
 
 // Weight row held in row r of the B tile. GLU (Linear-1): 32-row blocks alternate gate / up,
 // so a wave's neighbouring n-blocks hold gate column j and up column j in the same lanes.

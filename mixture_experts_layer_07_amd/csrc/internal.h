@@ -21,9 +21,9 @@ namespace moe {
 //   base     [perm_blocks][E] int32 per-block starting rank inside each expert
 //   tiles    [2][257] int32 m-tile prefix sums of the grouped GEMMs
 //   h        [max_rows][max_I] SwiGLU output (fp32 / bf16 / e4m3 codes)
-//   hscale   [max_rows][max_I/128] fp32 (fp8 layer) / [max_I/128][rows] E8M0 words (MX layer)
-//   xscale   [H/128][T*K] E8M0 words (MX layer): the activation scales of a gathered Linear-1 in
-//            grouped row order
+//   hscale   [max_I/128][rows] fp32 (fp8 layer) / E8M0 words (MX layer): h's scales, K-major
+//   xscale   [H/128][rows] fp32 (fp8 layer) / E8M0 words (MX layer, gathered Linear-1 only): the
+//            activation scales of Linear-1's rows, K-major in grouped row order
 //   the single-launch decode layer's regions (bf16 and MX layers with T*K <= kSmallPermPairs, else
 //   empty):
 //   dctrl    kDecodeCtrlInts int32 control block (task counters, flags, the m-tile prefix)

@@ -48,6 +48,24 @@ __global__ __launch_bounds__(256) void k_gather_scale_words(const int32_t* __res
   for (int g = blockIdx.y; g < groups; g += gridDim.y) out[(size_t)g * n_rows + i] = in[(size_t)g * limit + tok];
 }
 
+// fp8 activation scales of Linear-1 K-major in grouped row order: out[g][i] = in[row(i)][g] with
+// row(i) = the token of row i for a gathered Linear-1 (clamped into x, as the row itself), else i.
+// The GEMM's K step then reads its tile rows' scales as consecutive words; row-major, every row's
+// scale of a step sat in its own cache line.
+__global__ __launch_bounds__(256) void k_group_scales_fp8(const int32_t* __restrict__ rows_index, int div,
+                                                          int limit, const float* __restrict__ in,
+                                                          float* __restrict__ out, int n_rows, int groups) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_rows) return;
+  unsigned row = (unsigned)i;
+  if (rows_index) {
+    row = (unsigned)rows_index[i] / (unsigned)div;
+    row = row < (unsigned)limit ? row : (unsigned)(limit - 1);
+  }
+  const float* src = in + (size_t)row * groups;
+  for (int g = blockIdx.y; g < groups; g += gridDim.y) out[(size_t)g * n_rows + i] = src[g];
+}
+
 // ============================================================================ fp32 (VALU)
 // 64 x 64 output tiles, 16-channel K steps through LDS, 4 x 4 outputs per thread, fp32 FMA in
 // channel order. GLU tiles compute the gate and up tiles together.
@@ -201,11 +219,15 @@ void ffn_gemm_args(const FfnArgs& a, GemmArgs& g1, GemmArgs& g2) {
   g2.a_scale = static_cast<const float*>(a.h_scale);
   g2.b_scale = static_cast<const float*>(a.w2_scale);
   if (fp8) {
-    g1.a_scale_ld = H / 128;
+    // activation scales K-major, [K/128][rows] in grouped row order: Linear-1's from the
+    // caller's row-major x_scale (k_group_scales_fp8 into x_scale_grouped), h's as the Linear-1
+    // epilogue writes them
+    g1.a_scale = static_cast<const float*>(a.x_scale_grouped);
+    g1.a_scale_ld = a.n_rows;
     g1.b_scale_ld = H / 128;
     g1.b_scale_exp = (size_t)(2 * I / 128) * (H / 128);
-    g1.c_scale_ld = I / 128;
-    g2.a_scale_ld = I / 128;
+    g1.c_scale_ld = a.n_rows;
+    g2.a_scale_ld = a.n_rows;
     g2.b_scale_ld = I / 128;
     g2.b_scale_exp = (size_t)(H / 128) * (I / 128);
   }
@@ -266,6 +288,15 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
            hipLaunchKernelGGL(k_gather_scale_words, grid, dim3(256), 0, s, a.x_rows_index, a.x_rows_div,
                               a.x_rows_limit, static_cast<const uint32_t*>(a.x_scale),
                               static_cast<uint32_t*>(a.x_scale_grouped), a.n_rows, groups);
+         })) != hipSuccess)
+      return e;
+  }
+  if (fp8) {
+    const int groups = H / 128;
+    if ((e = timed_launch("group_scales_fp8", s, [&] {
+           hipLaunchKernelGGL(k_group_scales_fp8, dim3((a.n_rows + 255) / 256, groups < 8 ? groups : 8), dim3(256), 0, s,
+                              a.x_rows_index, a.x_rows_div, a.x_rows_limit, static_cast<const float*>(a.x_scale),
+                              static_cast<float*>(a.x_scale_grouped), a.n_rows, groups);
          })) != hipSuccess)
       return e;
   }

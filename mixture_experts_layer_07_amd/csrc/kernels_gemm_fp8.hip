@@ -127,13 +127,14 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
     }
     // the LDS entry a direct-to-LDS load of this lane fills for weight chunk j: + j * NT
     const int bw_off = wave * 64 + lane;
-    // row scales: wave w < SAW loads rows 64w + lane (clamped) for the K step
-    const uint8_t* sab = reinterpret_cast<const uint8_t*>(a_scale_base(g, ti));
+    // row scales: wave w < SAW loads rows 64w + lane (clamped) for the K step; they are K-major,
+    // [K/128][a_scale_ld] in grouped row order, so a step's rows are consecutive words
+    const uint8_t* sab = reinterpret_cast<const uint8_t*>(g.a_scale);
+    const size_t sstep = (size_t)g.a_scale_ld * 4;
     uint32_t soff = 0;
     {
       const int r = wave * 64 + lane;
-      const int rr = a_row(g, ti, r < ti.mvalid ? r : ti.mvalid - 1);
-      soff = (uint32_t)rr * (uint32_t)g.a_scale_ld * 4u;
+      soff = (uint32_t)(ti.row0 + (r < ti.mvalid ? r : ti.mvalid - 1)) * 4u;
     }
     // formed once per tile: the empty asm keeps the compiler from recomputing them (with the
     // row lookups of a gathered A) inside the K loop
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
 #define MOE_FP8_AISSUE(kt, sta, ssa)                                                                \
   do {                                                                                              \
     MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt) * 128u, sta, wave);                                \
-    if (wave < SAW) dma_to_lds<4>(sab + (soff + (uint32_t)(kt) * 4u), (ssa) + wave * 64);           \
+    if (wave < SAW) dma_to_lds<4>(sab + (size_t)(kt) * sstep + soff, (ssa) + wave * 64);            \
   } while (0)
 // weights of step kt (clamped into the loop) into registers R
 #define MOE_FP8_BLOAD(R, kt)                                                                        \
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
             *reinterpret_cast<uint32_t*>(g.C + (size_t)(ti.row0 + r) * g.ldc + ti.nt * 128 + wn * 32 + 8 * g4 + 4 * lk) =
                 (uint32_t)w;
         }
-        if (wn == 0 && lk == 0 && r < ti.mvalid) g.c_scale[(size_t)(ti.row0 + r) * g.c_scale_ld + ti.nt] = scale;
+        if (wn == 0 && lk == 0 && r < ti.mvalid) g.c_scale[(size_t)ti.nt * g.c_scale_ld + ti.row0 + r] = scale;
       }
       __syncthreads();  // red[] aliases the first stage of the next tile
     } else {
