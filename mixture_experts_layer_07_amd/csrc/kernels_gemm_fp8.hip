@@ -131,16 +131,16 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
     // [K/128][a_scale_ld] in grouped row order, so a step's rows are consecutive words
     const uint8_t* sab = reinterpret_cast<const uint8_t*>(g.a_scale);
     const size_t sstep = (size_t)g.a_scale_ld * 4;
-    uint32_t soff = 0;
+    uint32_t srow = 0;  // (the grouped row; its byte offset is formed in 64 bits: rows may reach 2^31)
     {
       const int r = wave * 64 + lane;
-      soff = (uint32_t)(ti.row0 + (r < ti.mvalid ? r : ti.mvalid - 1)) * 4u;
+      srow = (uint32_t)(ti.row0 + (r < ti.mvalid ? r : ti.mvalid - 1));
     }
     // formed once per tile: the empty asm keeps the compiler from recomputing them (with the
     // row lookups of a gathered A) inside the K loop
 #pragma unroll
     for (int j = 0; j < AJ; ++j) asm volatile("" : "+v"(da.off[j]));
-    asm volatile("" : "+v"(soff));
+    asm volatile("" : "+v"(srow));
     // weight block scales of this wave's column blocks: wave-uniform, read with scalar loads one
     // step ahead
     const float* psb[NB];
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(NWM * NWN * 64, MINB) void k_gemm_fp8(GemmArgs g) {
 #define MOE_FP8_AISSUE(kt, sta, ssa)                                                                \
   do {                                                                                              \
     MOE_DMA_ISSUE(AJ, NW, Ab, da, (uint32_t)(kt) * 128u, sta, wave);                                \
-    if (wave < SAW) dma_to_lds<4>(sab + (size_t)(kt) * sstep + soff, (ssa) + wave * 64);            \
+    if (wave < SAW) dma_to_lds<4>(sab + (size_t)(kt) * sstep + (size_t)srow * 4, (ssa) + wave * 64); \
   } while (0)
 // weights of step kt (clamped into the loop) into registers R
 #define MOE_FP8_BLOAD(R, kt)                                                                        \
